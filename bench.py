@@ -1,0 +1,368 @@
+"""Benchmark of the Key-only GLA token mixer (libgtrscan) on one MI355X.
+
+One step = one full mixer call (every phase of the chunkwise scan, epilogue
+and grid-order store) on the 16.4K-token workload: B=1, 128x128 grid
+(16384 tokens), H=12, dk=dv=64, fp16 I/O, chunk 64.  Inputs are seeded
+synthetic arrays already resident in HBM; consecutive steps rotate over
+enough buffer sets (>= 512 MB in total) that the 256 MB Infinity Cache cannot
+serve one step from the previous one.
+
+Prints one JSON line (see the keys below); progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gated_token_recurrence_amd as g  # noqa: E402
+from gated_token_recurrence_amd import _lib, workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # dense bf16/fp16 MFMA
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------- HIP events --
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            if self.lib.hipEventCreate(ctypes.byref(arr, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+        return arr
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, arr):
+        for e in arr:
+            self.lib.hipEventDestroy(e)
+
+
+# ----------------------------------------------------------------- inputs --
+TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def device_sets(w: W.Workload, n_sets: int, dev):
+    x = W.make_inputs(w)
+    base = {}
+    for key in ("q", "k", "v", "z"):
+        a = x[key]
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
+            else torch.from_numpy(a)
+        base[key] = t
+    base["log_g"] = torch.from_numpy(x["log_g"])
+    base["rms_w"] = torch.from_numpy(x["rms_w"])
+    sets = []
+    for _ in range(n_sets):
+        s = {key: val.to(dev) for key, val in base.items()}
+        s["out"] = torch.empty_like(s["v"])
+        sets.append(s)
+    torch.cuda.synchronize(dev)
+    return x, sets
+
+
+def call(lib, w, s, direction, chunk, path, stream, events=None, n_events=0, nl=None):
+    args = (s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(), s["log_g"].data_ptr(),
+            s["z"].data_ptr(), s["rms_w"].data_ptr(), s["out"].data_ptr(), w.B, w.H, w.grid_h,
+            w.grid_w, w.dk, w.dv, direction, chunk, W.DTYPE_CODE[w.dtype], path)
+    if events is None:
+        st = lib.gtr_gla_fwd_path(*args, stream)
+    else:
+        st = lib.gtr_gla_fwd_events(*args, events, n_events, nl, stream)
+    _lib.check(st)
+
+
+def time_workload(w, dev, hip, stream_ptr, steps, warmup, path, chunk, direction=0,
+                  per_kernel=True, graph=True):
+    """Returns a dict of timings for one workload (rotating buffer sets)."""
+    lib = _lib.load()
+    per_set = w.compulsory_bytes()
+    n_sets = W.rotation_sets(per_set)
+    x, sets = device_sets(w, n_sets, dev)
+    res = {"n_sets": n_sets, "set_mb": per_set / 1e6}
+    for i in range(warmup):
+        call(lib, w, sets[i % n_sets], direction, chunk, path, stream_ptr)
+    torch.cuda.synchronize(dev)
+
+    # Whole-call timing: events at the ends of the region, rotating sets.
+    ev = hip.events(2)
+    hip.record(ev[0], stream_ptr)
+    for i in range(steps):
+        call(lib, w, sets[i % n_sets], direction, chunk, path, stream_ptr)
+    hip.record(ev[1], stream_ptr)
+    total_ms = hip.elapsed_ms(ev[0], ev[1])
+    torch.cuda.synchronize(dev)
+    res["us_per_call"] = total_ms * 1e3 / steps
+    hip.destroy(ev)
+
+    # Hot: the same set every time (cache-resident inputs), labelled as such.
+    ev = hip.events(2)
+    hip.record(ev[0], stream_ptr)
+    for i in range(steps):
+        call(lib, w, sets[0], direction, chunk, path, stream_ptr)
+    hip.record(ev[1], stream_ptr)
+    res["us_per_call_hot"] = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+    torch.cuda.synchronize(dev)
+    hip.destroy(ev)
+
+    if per_kernel:
+        # Per-launch timing: events between the launches of every call.
+        nl = ctypes.c_int(0)
+        probe = hip.events(8)
+        call(lib, w, sets[0], direction, chunk, path, stream_ptr, probe, 8, ctypes.byref(nl))
+        torch.cuda.synchronize(dev)
+        hip.destroy(probe)
+        n_ev = nl.value + 1
+        evs = [hip.events(n_ev) for _ in range(steps)]
+        for i in range(steps):
+            call(lib, w, sets[i % n_sets], direction, chunk, path, stream_ptr, evs[i], n_ev,
+                 None)
+        torch.cuda.synchronize(dev)
+        per = [[hip.elapsed_ms(e[j], e[j + 1]) * 1e3 for j in range(n_ev - 1)] for e in evs]
+        for e in evs:
+            hip.destroy(e)
+        res["launch_us_mean"] = [statistics.fmean(p[j] for p in per) for j in range(n_ev - 1)]
+        res["launch_us_median"] = [statistics.median(p[j] for p in per) for j in range(n_ev - 1)]
+        calls = [sum(p) for p in per]
+        res["us_per_call_evented_median"] = statistics.median(calls)
+        res["us_per_call_evented_p10"] = float(np.percentile(calls, 10))
+        res["us_per_call_evented_p90"] = float(np.percentile(calls, 90))
+
+    if graph:
+        # hipGraph replay of one call per buffer set (the pages' own kernel
+        # benchmark used graph launch).
+        s = torch.cuda.Stream(device=dev)
+        sp = s.cuda_stream
+        with torch.cuda.stream(s):
+            for i in range(n_sets):
+                call(lib, w, sets[i], direction, chunk, path, sp)
+        torch.cuda.synchronize(dev)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=s):
+            for i in range(n_sets):
+                call(lib, w, sets[i], direction, chunk, path, sp)
+        torch.cuda.synchronize(dev)
+        reps = max(1, steps // n_sets)
+        for _ in range(2):
+            gr.replay()
+        torch.cuda.synchronize(dev)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            gr.replay()
+        t1.record()
+        torch.cuda.synchronize(dev)
+        res["us_per_call_graph"] = t0.elapsed_time(t1) * 1e3 / (reps * n_sets)
+        del gr
+    del sets
+    torch.cuda.empty_cache()
+    return x, res
+
+
+# ----------------------------------------------------------- CPU baseline --
+def cpu_baseline(w: W.Workload, x: dict, target_s: float = 12.0):
+    """The fp64 oracle (test infrastructure, untuned) on a bounded sample of heads."""
+    import oracle
+    oracle.build(force=False)
+    f = {key: W.io_to_f64(x[key], w.dtype) for key in ("q", "k", "v", "z")}
+    lg = x["log_g"].astype(np.float64)
+    rw = x["rms_w"].astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0, bh=[0])
+    t1 = time.perf_counter() - t0
+    n = int(min(w.B * w.H, max(1, target_s / max(t1, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0, bh=list(range(n)))
+    dt = time.perf_counter() - t0
+    tokens = n * w.L / w.H  # grid tokens with all heads counted once
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{n} of {w.B * w.H} (batch, head) sequences of {w.name} "
+                      f"({n * w.L} token-heads, LR scan), {dt:.1f} s",
+            "us_per_call_equiv": dt / n * w.B * w.H * 1e6}
+
+
+# --------------------------------------------------------------- roofline --
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "gated_token_recurrence_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(path_name, workload):
+    p = os.path.join(ROOT, "profiles", f"traffic_{path_name}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("sources_hash") != kernel_sources_hash():
+        return None  # the kernels changed since the counters were taken
+    return rec
+
+
+PATH_NAMES = {g.PATH_AUTO: "auto", g.PATH_MFMA: "mfma", g.PATH_FAST: "fast",
+              g.PATH_SERIAL: "serial"}
+LAUNCH_NAMES = {
+    "mfma": ["segment_summary", "state_scan", "chunk_output"],
+    "serial": ["chunk_summary", "state_scan", "chunk_output"],
+    "fast": ["fast_single_launch"],
+}
+
+
+def resolve_path(w, requested):
+    if requested != g.PATH_AUTO:
+        return requested
+    if w.dtype == "f32":
+        return g.PATH_SERIAL
+    return g.PATH_MFMA if _mfma_available(w) else g.PATH_SERIAL
+
+
+def _mfma_available(w):
+    return w.dk == 64 and w.dv in (64, 128)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mixer_2048")
+    ap.add_argument("--path", type=int, default=g.PATH_AUTO)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    w = W.WORKLOADS[args.workload]
+    chunk = args.chunk or w.chunk
+    path = resolve_path(w, args.path)
+    pname = PATH_NAMES[path]
+    log(f"workload {w.name}: B={w.B} grid {w.grid_h}x{w.grid_w} H={w.H} dk={w.dk} dv={w.dv} "
+        f"{w.dtype} chunk {chunk} path {pname}")
+    x, res = time_workload(w, dev, hip, sp, args.steps, args.warmup, path, chunk)
+    log(f"  {res['us_per_call']:.2f} us/call (rotating {res['n_sets']} sets), "
+        f"hot {res['us_per_call_hot']:.2f}, graph {res.get('us_per_call_graph', 0):.2f}, "
+        f"launches {['%.2f' % t for t in res['launch_us_mean']]}")
+
+    comp = w.compulsory_bytes()
+    us = res["us_per_call"]
+    value = w.tokens / (us * 1e-6)
+    names = LAUNCH_NAMES[pname]
+    dom = int(np.argmax(res["launch_us_mean"]))
+    dom_us = res["launch_us_mean"][dom]
+    achieved = comp / (dom_us * 1e-6) / 1e9
+    tr = traffic_record(pname, w.name)
+    traffic = None
+    if tr is not None and tr.get("kernel") == names[dom]:
+        traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": names[dom], "kernel_us": round(dom_us, 3),
+                "algorithmic_bytes": comp,
+                "whole_call_frac": round(comp / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "mfma_frac_algorithmic": round(w.algorithmic_flops(chunk) / (us * 1e-6) / 1e12
+                                               / MFMA_BF16_PEAK_TFLOPS, 5)}
+    extra = {}
+    if not args.no_extra:
+        for name in ("mixer_640", "mixer_640_wide"):
+            we = W.WORKLOADS[name]
+            pe = resolve_path(we, g.PATH_AUTO if args.path == g.PATH_AUTO else args.path)
+            try:
+                _, r = time_workload(we, dev, hip, sp, args.steps, args.warmup, pe, we.chunk,
+                                     per_kernel=False)
+            except Exception as exc:  # report, do not hide
+                extra[name] = {"error": str(exc)}
+                continue
+            extra[name] = {"us_per_call": round(r["us_per_call"], 3),
+                           "us_per_call_graph": round(r["us_per_call_graph"], 3),
+                           "us_per_call_hot": round(r["us_per_call_hot"], 3),
+                           "tokens_per_s": round(we.tokens / (r["us_per_call"] * 1e-6)),
+                           "hbm_frac": round(we.compulsory_bytes() / (r["us_per_call"] * 1e-6)
+                                             / 1e9 / HBM_PEAK_GBS, 4),
+                           "path": PATH_NAMES[pe]}
+            log(f"  {name}: {r['us_per_call']:.2f} us/call, graph {r['us_per_call_graph']:.2f}")
+    cpu = None
+    if not args.no_cpu:
+        log("  timing the fp64 oracle on the host (bounded sample)")
+        cpu = cpu_baseline(w, x)
+        log(f"  oracle: {cpu['value']:.3e} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "GLA-scan tokens/s + µs/call at 1.6K & 16.4K tokens; % of HBM/MFMA roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if pname == "serial" else "bf16x2-f32acc",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B}, grid {w.grid_h}x{w.grid_w} ({w.L} tokens), "
+                               f"H={w.H}, dk={w.dk}, dv={w.dv}, {w.dtype} I/O, chunk {chunk}, "
+                               f"direction LR",
+                   "path": pname, "global_batch": w.B, "seq_len": w.L, "parallelism": "none"},
+        "us_per_call": round(us, 3),
+        "us_per_call_hot": round(res["us_per_call_hot"], 3),
+        "us_per_call_graph": round(res["us_per_call_graph"], 3),
+        "us_per_call_p10_p50_p90": [round(res["us_per_call_evented_p10"], 3),
+                                    round(res["us_per_call_evented_median"], 3),
+                                    round(res["us_per_call_evented_p90"], 3)],
+        "launch_us_mean": {n: round(t, 3) for n, t in zip(names, res["launch_us_mean"])},
+        "rotating_sets": res["n_sets"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra_1p6k": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

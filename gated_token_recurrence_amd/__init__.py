@@ -1,0 +1,109 @@
+"""Key-only gated-linear-attention token mixer of GTR on MI355X (gfx950).
+
+Python binding of libgtrscan (``include/gtrscan.h``).  torch supplies device
+memory and the current stream; the mixer itself runs in the library's HIP
+kernels.  ``gla_fwd`` is one block's mixer call, ``gla_stack_fwd`` a stack of
+blocks with the direction cycle and the residual feed.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (GtrError, PATH_AUTO, PATH_FAST, PATH_MFMA, PATH_SERIAL)  # noqa: F401
+
+__all__ = ["gla_fwd", "gla_stack_fwd", "GtrError", "DIRECTIONS", "dtype_code", "version"]
+
+DIRECTIONS = {"LR": 0, "RL": 1, "TB": 2, "BT": 3}
+_DT = {torch.float32: _lib.GTR_F32, torch.float16: _lib.GTR_F16, torch.bfloat16: _lib.GTR_BF16}
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise TypeError(f"unsupported I/O dtype {dt}")
+    return _DT[dt]
+
+
+def version() -> int:
+    return _lib.load().gtr_version()
+
+
+def _dir(direction) -> int:
+    return DIRECTIONS[direction] if isinstance(direction, str) else int(direction)
+
+
+def _check_tensors(named, device):
+    for name, t in named:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def gla_fwd(q, k, v, log_g, z, rms_w, direction=0, chunk: int = 0, path: int = PATH_AUTO,
+            out=None):
+    """One mixer call.  q, k, log_g: [B, gh, gw, H, dk]; v, z: [B, gh, gw, H, dv];
+    rms_w: [dv] float32; log_g float32; q, k, v, z one I/O dtype.  Returns out."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    B, gh, gw, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or log_g.shape != q.shape:
+        raise ValueError("k and log_g must have q's shape")
+    if v.shape != (B, gh, gw, H, dv) or z.shape != v.shape or rms_w.shape != (dv,):
+        raise ValueError("v, z must be [B, gh, gw, H, dv] and rms_w [dv]")
+    if not (q.dtype == k.dtype == v.dtype == z.dtype):
+        raise TypeError("q, k, v, z must share one dtype")
+    if log_g.dtype != torch.float32 or rms_w.dtype != torch.float32:
+        raise TypeError("log_g and rms_w must be float32")
+    if out is None:
+        out = torch.empty_like(v)
+    _check_tensors((("q", q), ("k", k), ("v", v), ("log_g", log_g), ("z", z),
+                    ("rms_w", rms_w), ("out", out)), dev)
+    if out.shape != v.shape or out.dtype != v.dtype:
+        raise ValueError("out must match v")
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        st = lib.gtr_gla_fwd_path(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_g.data_ptr(),
+                                  z.data_ptr(), rms_w.data_ptr(), out.data_ptr(), B, H, gh, gw,
+                                  dk, dv, _dir(direction), int(chunk), dtype_code(q.dtype),
+                                  int(path), _stream_ptr(dev))
+    _lib.check(st)
+    return out
+
+
+def gla_stack_fwd(q, k, v, log_g, z, rms_w, first_direction=0, chunk: int = 0, out=None):
+    """Stack of blocks: every tensor has a leading [n_blocks] dimension; rms_w is
+    [n_blocks, dv].  Returns out [n_blocks, B, gh, gw, H, dv] (every block's output)."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    nb, B, gh, gw, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or log_g.shape != q.shape:
+        raise ValueError("k and log_g must have q's shape")
+    if v.shape != (nb, B, gh, gw, H, dv) or z.shape != v.shape or rms_w.shape != (nb, dv):
+        raise ValueError("v, z must be [n, B, gh, gw, H, dv] and rms_w [n, dv]")
+    if not (q.dtype == k.dtype == v.dtype == z.dtype):
+        raise TypeError("q, k, v, z must share one dtype")
+    if log_g.dtype != torch.float32 or rms_w.dtype != torch.float32:
+        raise TypeError("log_g and rms_w must be float32")
+    if out is None:
+        out = torch.empty_like(v)
+    _check_tensors((("q", q), ("k", k), ("v", v), ("log_g", log_g), ("z", z),
+                    ("rms_w", rms_w), ("out", out)), dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        st = lib.gtr_gla_stack_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_g.data_ptr(),
+                                   z.data_ptr(), rms_w.data_ptr(), out.data_ptr(), nb, B, H, gh,
+                                   gw, dk, dv, _dir(first_direction), int(chunk),
+                                   dtype_code(q.dtype), _stream_ptr(dev))
+    _lib.check(st)
+    return out

@@ -1,0 +1,337 @@
+// api.cpp -- libgtrscan's C ABI: argument checks, path choice, workspace, launches.
+//
+// The operation and the layouts are documented in include/gtrscan.h.  Every
+// check runs on the host before anything is enqueued; device data (NaN, Inf,
+// positive log-gates) is not inspected.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "gtr_internal.hpp"
+#include "gtrscan.h"
+
+using namespace gtr;
+
+namespace {
+
+thread_local std::string g_err;
+
+gtr_status fail(gtr_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+gtr_status hip_fail(hipError_t e, const char *what) {
+    return fail(GTR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- workspace --
+// Grow-only device buffer per (device, stream).  Growing synchronises the
+// stream first, because queued kernels may still use the old buffer.
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+gtr_status workspace(hipStream_t stream, size_t bytes, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            e = hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+        }
+        size_t want = bytes + bytes / 4;  // headroom against repeated small growth
+        e = hipMalloc(&w.ptr, want);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return hip_fail(e, "hipMalloc(workspace)");
+        }
+        w.bytes = want;
+    }
+    *out = w.ptr;
+    return GTR_OK;
+}
+
+// --------------------------------------------------------------- validation --
+bool head_width_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+gtr_status check(const void *q, const void *k, const void *v, const float *log_g,
+                 const void *z, const float *rms_w, const void *out, int B, int H, int gh,
+                 int gw, int dk, int dv, int direction, int chunk, int dtype, int path) {
+    if (!q || !k || !v || !log_g || !z || !rms_w || !out)
+        return fail(GTR_ERR_ARG, "null tensor pointer");
+    if (B <= 0 || H <= 0 || gh <= 0 || gw <= 0)
+        return fail(GTR_ERR_ARG, "B, H, grid_h, grid_w must be positive (got %d, %d, %d, %d)",
+                    B, H, gh, gw);
+    if (direction < 0 || direction > 3)
+        return fail(GTR_ERR_ARG, "direction must be 0..3 (LR, RL, TB, BT), got %d", direction);
+    if (!(chunk == 0 || chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128))
+        return fail(GTR_ERR_ARG, "chunk must be 0, 16, 32, 64 or 128, got %d", chunk);
+    if (dtype < GTR_F32 || dtype > GTR_BF16)
+        return fail(GTR_ERR_ARG, "unknown dtype %d", dtype);
+    if (path < GTR_PATH_AUTO || path > GTR_PATH_SERIAL)
+        return fail(GTR_ERR_ARG, "unknown path %d", path);
+    if (!head_width_ok(dk) || !head_width_ok(dv))
+        return fail(GTR_ERR_UNSUPPORTED, "dk and dv must be 32, 64 or 128 (got %d, %d)", dk, dv);
+    const __int128 rows = static_cast<__int128>(B) * gh * gw * H;
+    if (rows * (dk > dv ? dk : dv) * 4 > (static_cast<__int128>(1) << 62) ||
+        static_cast<int64_t>(gh) * gw > (static_cast<int64_t>(1) << 40))
+        return fail(GTR_ERR_UNSUPPORTED, "tensor sizes overflow 64-bit offsets");
+    return GTR_OK;
+}
+
+gtr_status check_aliasing(const void *out, size_t out_bytes, const void *const *ins,
+                          const size_t *in_bytes, int n) {
+    const char *o0 = static_cast<const char *>(out), *o1 = o0 + out_bytes;
+    for (int i = 0; i < n; ++i) {
+        const char *a0 = static_cast<const char *>(ins[i]), *a1 = a0 + in_bytes[i];
+        if (a0 < o1 && o0 < a1) return fail(GTR_ERR_ARG, "out overlaps input %d", i);
+    }
+    return GTR_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == GTR_F32 ? 4 : 2; }
+
+// Records events around launches when the caller asked for them.
+struct Marks {
+    hipEvent_t *ev = nullptr;
+    int n = 0;
+    int launches = 0;
+    hipError_t record(hipStream_t st, int i) {
+        return (ev && i < n) ? hipEventRecord(ev[i], st) : hipSuccess;
+    }
+    hipError_t after_launch(hipStream_t st) { return record(st, ++launches); }
+};
+
+constexpr int kDefaultChunk = 64;
+constexpr int kFastMaxTokens = 2048;
+
+// Segment length of the MFMA path, in chunks: enough workgroups to fill the
+// chip (256 CUs) while keeping the per-segment state traffic small.
+int segment_chunks(int64_t n_seq, int64_t n_chunks) {
+    int sc = 1;
+    while (sc < 16 && n_seq * ((n_chunks + 2 * sc - 1) / (2 * sc)) >= 512) sc *= 2;
+    return sc;
+}
+
+gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk) {
+    const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
+    const int64_t n_seq = static_cast<int64_t>(a.B) * a.H;
+    if (n_seq * n_chunks > 0x7fffffff) return fail(GTR_ERR_UNSUPPORTED, "too many chunks");
+    const size_t ubytes = static_cast<size_t>(n_seq * n_chunks) * a.dk * a.dv * 4;
+    const size_t gbytes = static_cast<size_t>(n_seq * n_chunks) * a.dk * 4;
+    void *ws = nullptr;
+    gtr_status s = workspace(st, ubytes + gbytes, &ws);
+    if (s != GTR_OK) return s;
+    float *U = static_cast<float *>(ws);
+    float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
+    hipError_t e = mk.record(st, 0);
+    if (e == hipSuccess) e = serial_summary(a, U, G, static_cast<int>(n_chunks), st);
+    if (e == hipSuccess) e = mk.after_launch(st);
+    if (e != hipSuccess) return hip_fail(e, "chunk summary launch");
+    e = state_scan(U, G, static_cast<int>(n_seq), static_cast<int>(n_chunks), a.dk, a.dv, st);
+    if (e == hipSuccess) e = mk.after_launch(st);
+    if (e != hipSuccess) return hip_fail(e, "state scan launch");
+    e = serial_output(a, U, static_cast<int>(n_chunks), st);
+    if (e == hipSuccess) e = mk.after_launch(st);
+    if (e != hipSuccess) return hip_fail(e, "chunk output launch");
+    return GTR_OK;
+}
+
+gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
+    const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
+    const int64_t n_seq = static_cast<int64_t>(a.B) * a.H;
+    const int sc = segment_chunks(n_seq, n_chunks);
+    const int64_t n_seg = (n_chunks + sc - 1) / sc;
+    if (n_seq * n_seg > 0x7fffffff) return fail(GTR_ERR_UNSUPPORTED, "too many segments");
+    const size_t ubytes = static_cast<size_t>(n_seq * n_seg) * a.dk * a.dv * 4;
+    const size_t gbytes = static_cast<size_t>(n_seq * n_seg) * a.dk * 4;
+    void *ws = nullptr;
+    gtr_status s = workspace(st, ubytes + gbytes, &ws);
+    if (s != GTR_OK) return s;
+    float *U = static_cast<float *>(ws);
+    float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
+    hipError_t e = mk.record(st, 0);
+    if (e == hipSuccess) e = mfma_summary(a, U, G, static_cast<int>(n_seg), sc, st);
+    if (e == hipSuccess) e = mk.after_launch(st);
+    if (e != hipSuccess) return hip_fail(e, "segment summary launch");
+    e = state_scan(U, G, static_cast<int>(n_seq), static_cast<int>(n_seg), a.dk, a.dv, st);
+    if (e == hipSuccess) e = mk.after_launch(st);
+    if (e != hipSuccess) return hip_fail(e, "state scan launch");
+    e = mfma_output(a, U, static_cast<int>(n_seg), sc, st);
+    if (e == hipSuccess) e = mk.after_launch(st);
+    if (e != hipSuccess) return hip_fail(e, "chunk output launch");
+    return GTR_OK;
+}
+
+gtr_status run(const GlaArgs &a0, int path, hipStream_t st, Marks &mk) {
+    GlaArgs a = a0;
+    if (a.chunk == 0) a.chunk = kDefaultChunk;
+    const bool mfma_ok = a.dtype != GTR_F32 && mfma_supported(a);
+    if (path == GTR_PATH_AUTO) path = mfma_ok ? GTR_PATH_MFMA : GTR_PATH_SERIAL;
+    switch (path) {
+    case GTR_PATH_SERIAL: return run_serial(a, st, mk);
+    case GTR_PATH_MFMA:
+        if (!mfma_ok)
+            return fail(GTR_ERR_UNSUPPORTED,
+                        "MFMA path needs 16-bit I/O, dk = 64, dv in {64, 128}, chunk in {32, 64}");
+        return run_mfma(a, st, mk);
+    case GTR_PATH_FAST:
+        return fail(GTR_ERR_UNSUPPORTED, "single-launch path not available for these arguments");
+    default: return fail(GTR_ERR_ARG, "unknown path %d", path);
+    }
+    (void)kFastMaxTokens;
+}
+
+int device_ok() {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n <= 0) {
+        fail(GTR_ERR_HIP, "no HIP device available (%s)",
+             e != hipSuccess ? hipGetErrorString(e) : "device count is 0");
+        return 0;
+    }
+    return 1;
+}
+
+gtr_status fwd_impl(const void *q, const void *k, const void *v, const float *log_g,
+                    const void *z, const float *rms_w, void *out, const void *resid, int B,
+                    int H, int gh, int gw, int dk, int dv, int direction, int chunk, int dtype,
+                    int path, hipStream_t stream, Marks &mk) {
+    g_err.clear();
+    gtr_status s = check(q, k, v, log_g, z, rms_w, out, B, H, gh, gw, dk, dv, direction, chunk,
+                         dtype, path);
+    if (s != GTR_OK) return s;
+    const size_t rows = static_cast<size_t>(B) * gh * gw * H;
+    const size_t eb = elem_bytes(dtype);
+    const void *ins[] = {q, k, v, log_g, z, rms_w, resid ? resid : q};
+    const size_t nb[] = {rows * dk * eb, rows * dk * eb, rows * dv * eb, rows * dk * 4,
+                         rows * dv * eb, static_cast<size_t>(dv) * 4, rows * dv * eb};
+    s = check_aliasing(out, rows * dv * eb, ins, nb, 7);
+    if (s != GTR_OK) return s;
+    if (!device_ok()) return GTR_ERR_HIP;
+    GlaArgs a{q, k, v, log_g, z, rms_w, out, resid, B, H, gh, gw, dk, dv, direction, chunk,
+              dtype, static_cast<int64_t>(gh) * gw};
+    return run(a, path, stream, mk);
+}
+
+}  // namespace
+
+extern "C" {
+
+gtr_status gtr_gla_fwd(const void *q, const void *k, const void *v, const float *log_g,
+                       const void *z, const float *rms_w, void *out, int B, int H, int grid_h,
+                       int grid_w, int dk, int dv, int direction, int chunk, gtr_dtype dtype,
+                       hipStream_t stream) {
+    Marks mk;
+    return fwd_impl(q, k, v, log_g, z, rms_w, out, nullptr, B, H, grid_h, grid_w, dk, dv,
+                    direction, chunk, dtype, GTR_PATH_AUTO, stream, mk);
+}
+
+gtr_status gtr_gla_fwd_path(const void *q, const void *k, const void *v, const float *log_g,
+                            const void *z, const float *rms_w, void *out, int B, int H,
+                            int grid_h, int grid_w, int dk, int dv, int direction, int chunk,
+                            gtr_dtype dtype, int path, hipStream_t stream) {
+    Marks mk;
+    return fwd_impl(q, k, v, log_g, z, rms_w, out, nullptr, B, H, grid_h, grid_w, dk, dv,
+                    direction, chunk, dtype, path, stream, mk);
+}
+
+gtr_status gtr_gla_fwd_events(const void *q, const void *k, const void *v, const float *log_g,
+                              const void *z, const float *rms_w, void *out, int B, int H,
+                              int grid_h, int grid_w, int dk, int dv, int direction, int chunk,
+                              gtr_dtype dtype, int path, hipEvent_t *events, int n_events,
+                              int *n_launches, hipStream_t stream) {
+    if (n_events < 0 || (n_events > 0 && !events))
+        return fail(GTR_ERR_ARG, "events: need n_events >= 0 and a non-null array");
+    Marks mk;
+    mk.ev = events;
+    mk.n = n_events;
+    gtr_status s = fwd_impl(q, k, v, log_g, z, rms_w, out, nullptr, B, H, grid_h, grid_w, dk,
+                            dv, direction, chunk, dtype, path, stream, mk);
+    if (n_launches) *n_launches = mk.launches;
+    return s;
+}
+
+gtr_status gtr_gla_stack_fwd(const void *q, const void *k, const void *v, const float *log_g,
+                             const void *z, const float *rms_w, void *out, int n_blocks, int B,
+                             int H, int grid_h, int grid_w, int dk, int dv, int first_direction,
+                             int chunk, gtr_dtype dtype, hipStream_t stream) {
+    g_err.clear();
+    if (n_blocks <= 0) return fail(GTR_ERR_ARG, "n_blocks must be positive, got %d", n_blocks);
+    if (first_direction < 0 || first_direction > 3)
+        return fail(GTR_ERR_ARG, "first_direction must be 0..3, got %d", first_direction);
+    gtr_status s = check(q, k, v, log_g, z, rms_w, out, B, H, grid_h, grid_w, dk, dv,
+                         first_direction, chunk, dtype, GTR_PATH_AUTO);
+    if (s != GTR_OK) return s;
+    const size_t rows = static_cast<size_t>(B) * grid_h * grid_w * H;
+    const size_t eb = elem_bytes(dtype);
+    const size_t qk_b = rows * dk * eb, v_b = rows * dv * eb, g_b = rows * dk * 4;
+    const void *ins[] = {q, k, v, log_g, z, rms_w};
+    const size_t nb[] = {qk_b * n_blocks, qk_b * n_blocks, v_b * n_blocks, g_b * n_blocks,
+                         v_b * n_blocks, static_cast<size_t>(dv) * 4 * n_blocks};
+    s = check_aliasing(out, v_b * n_blocks, ins, nb, 6);
+    if (s != GTR_OK) return s;
+    if (!device_ok()) return GTR_ERR_HIP;
+    for (int i = 0; i < n_blocks; ++i) {
+        const char *qi = static_cast<const char *>(q) + qk_b * i;
+        const char *ki = static_cast<const char *>(k) + qk_b * i;
+        const char *vi = static_cast<const char *>(v) + v_b * i;
+        const char *zi = static_cast<const char *>(z) + v_b * i;
+        const float *gi = reinterpret_cast<const float *>(
+            reinterpret_cast<const char *>(log_g) + g_b * i);
+        const float *wi = rms_w + static_cast<size_t>(dv) * i;
+        char *oi = static_cast<char *>(out) + v_b * i;
+        const void *resid = i > 0 ? static_cast<const void *>(oi - v_b) : nullptr;
+        GlaArgs a{qi, ki, vi, gi, zi, wi, oi, resid, B, H, grid_h, grid_w, dk, dv,
+                  (first_direction + i) % 4, chunk, dtype, static_cast<int64_t>(grid_h) * grid_w};
+        Marks mk;
+        s = run(a, GTR_PATH_AUTO, stream, mk);
+        if (s != GTR_OK) {
+            std::string msg = g_err;
+            return fail(s, "block %d: %s", i, msg.c_str());
+        }
+    }
+    return GTR_OK;
+}
+
+const char *gtr_last_error(void) { return g_err.c_str(); }
+
+int gtr_version(void) { return GTR_VERSION; }
+
+void gtr_release_workspace(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (auto &kv : g_ws) {
+        if (!kv.second.ptr) continue;
+        if (hipSetDevice(kv.first.first) == hipSuccess) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(kv.second.ptr);
+        }
+    }
+    g_ws.clear();
+    if (have_cur) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

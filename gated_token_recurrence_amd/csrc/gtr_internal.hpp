@@ -1,0 +1,116 @@
+// gtr_internal.hpp -- shared declarations of libgtrscan's kernels and launchers.
+//
+// Device helpers here: I/O element loads and round-to-nearest-even stores,
+// and the scan-order map of the four directions (GTR write-up
+// "端侧实时感知新标杆！通用线性骨干网络GTR开源", Method §1: LR, RL, TB, BT, grid
+// order restored after each block's scan).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gtrscan.h"
+
+namespace gtr {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+struct GlaArgs {
+    const void *q, *k, *v;
+    const float *log_g;
+    const void *z;
+    const float *rms_w;
+    void *out;
+    const void *resid;  // previous block's output (stack residual) or nullptr
+    int B, H, gh, gw, dk, dv, direction, chunk, dtype;
+    int64_t L;
+};
+
+// ------------------------------------------------------------ element I/O --
+template <int DT> struct Elem;
+template <> struct Elem<DT_F32> { using T = float; };
+template <> struct Elem<DT_F16> { using T = _Float16; };
+template <> struct Elem<DT_BF16> { using T = uint16_t; };  // bf16 bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <int DT> __device__ __forceinline__ float ld(const void *p, int64_t i);
+template <> __device__ __forceinline__ float ld<DT_F32>(const void *p, int64_t i) {
+    return static_cast<const float *>(p)[i];
+}
+template <> __device__ __forceinline__ float ld<DT_F16>(const void *p, int64_t i) {
+    return static_cast<float>(static_cast<const _Float16 *>(p)[i]);
+}
+template <> __device__ __forceinline__ float ld<DT_BF16>(const void *p, int64_t i) {
+    return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+}
+
+template <int DT> __device__ __forceinline__ void st(void *p, int64_t i, float x);
+template <> __device__ __forceinline__ void st<DT_F32>(void *p, int64_t i, float x) {
+    static_cast<float *>(p)[i] = x;
+}
+template <> __device__ __forceinline__ void st<DT_F16>(void *p, int64_t i, float x) {
+    static_cast<_Float16 *>(p)[i] = static_cast<_Float16>(x);  // RNE conversion
+}
+template <> __device__ __forceinline__ void st<DT_BF16>(void *p, int64_t i, float x) {
+    static_cast<uint16_t *>(p)[i] = f32_to_bf16(x);
+}
+
+// Round a float to the I/O type and back (the stack residual add is rounded
+// to the I/O type before use, as a stored tensor would be).
+template <int DT> __device__ __forceinline__ float round_io(float x);
+template <> __device__ __forceinline__ float round_io<DT_F32>(float x) { return x; }
+template <> __device__ __forceinline__ float round_io<DT_F16>(float x) {
+    return static_cast<float>(static_cast<_Float16>(x));
+}
+template <> __device__ __forceinline__ float round_io<DT_BF16>(float x) {
+    return bf16_to_f32(f32_to_bf16(x));
+}
+
+// value input of one element: v, or round_io(v + resid) inside a stack
+template <int DT>
+__device__ __forceinline__ float ld_v(const GlaArgs &a, int64_t i) {
+    float x = ld<DT>(a.v, i);
+    if (a.resid) x = round_io<DT>(x + ld<DT>(a.resid, i));
+    return x;
+}
+
+// ------------------------------------------------------------- scan order --
+// Grid index p of scan step t (p = r * gw + c).
+__device__ __forceinline__ int64_t scan_to_grid(int64_t t, int64_t L, int gh, int gw, int dir) {
+    if (dir & 1) t = L - 1 - t;          // RL, BT: the reversed sequence
+    if (dir < 2) return t;               // LR, RL: row-major raster
+    int64_t c = t / gh, r = t - c * gh;  // TB, BT: column-major raster
+    return r * gw + c;
+}
+
+// Row (token-head) index of scan step t for sequence (b, h).
+__device__ __forceinline__ int64_t scan_row(const GlaArgs &a, int b, int h, int64_t t) {
+    return (static_cast<int64_t>(b) * a.L + scan_to_grid(t, a.L, a.gh, a.gw, a.direction)) * a.H + h;
+}
+
+// --------------------------------------------------------------- launchers --
+// Token-serial fp32 chunk path.
+hipError_t serial_summary(const GlaArgs &a, float *U, float *G, int n_chunks, hipStream_t s);
+hipError_t serial_output(const GlaArgs &a, const float *Sx, int n_chunks, hipStream_t s);
+// Inter-chunk (or inter-segment) state scan, in place: U[n] <- S before unit n.
+hipError_t state_scan(float *U, const float *G, int n_seq, int n_units, int dk, int dv,
+                      hipStream_t s);
+// MFMA chunk path: segments of `seg_chunks` chunks of `chunk` tokens.
+bool mfma_supported(const GlaArgs &a);
+hipError_t mfma_summary(const GlaArgs &a, float *U, float *G, int n_seg, int seg_chunks,
+                        hipStream_t s);
+hipError_t mfma_output(const GlaArgs &a, const float *Sx, int n_seg, int seg_chunks,
+                       hipStream_t s);
+
+}  // namespace gtr

@@ -1,0 +1,144 @@
+/*
+ * gtrscan.h -- C ABI of libgtrscan, the Key-only gated-linear-attention token
+ * mixer of GTR (Gated Token Recurrence) for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (GTR write-up "端侧实时感知新标杆！通用线性骨干网络GTR开源",
+ * Method §1 "骨干架构：Key-only 门控递归与四向交替扫描"; the page's formulas were
+ * lost, the prose fixes their form): for every batch image b and head h the
+ * tokens of a grid_h x grid_w patch grid are visited in one scan order, and a
+ * dk x dv state is carried with the value-side decay fixed at 1 and a
+ * data-dependent key-side forget gate g_t = exp(log_g_t):
+ *
+ *     S_0 = 0,   S_t = Diag(g_t) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+ *     out_t = o_t / sqrt(mean_j(o_t[j]^2) + GTR_RMS_EPS) * rms_w * z_t * sigmoid(z_t)
+ *
+ * (RMSNorm, then the SiLU output gate, same section), and out_t is written at
+ * token t's own grid position, so grid order is restored after the scan.  The
+ * evaluation is chunkwise (Method §4 "硬件感知分块推理算子": chunk summaries,
+ * a boundary-state scan, per-chunk outputs with the gate fused in the
+ * epilogue); the chunk size changes rounding only.
+ *
+ * Tensor layout (all contiguous, row-major, token-major grid order):
+ *   q, k   : [B, grid_h, grid_w, H, dk]  I/O type
+ *   v, z   : [B, grid_h, grid_w, H, dv]  I/O type
+ *   out    : [B, grid_h, grid_w, H, dv]  I/O type, rounded to nearest even
+ *   log_g  : [B, grid_h, grid_w, H, dk]  float32, must be <= 0 (not checked)
+ *   rms_w  : [dv]                        float32, shared by all heads
+ * Grid index of row r, column c is p = r * grid_w + c.
+ *
+ * Scan orders (directions): LR p(t) = t; RL p(t) = L-1-t (whole raster
+ * reversed); TB visits the columns left to right, each top to bottom;
+ * BT is TB reversed.  L = grid_h * grid_w.
+ *
+ * Ownership: every tensor pointer is DEVICE memory owned by the caller; the
+ * library never frees it.  out must not overlap any input.  The library keeps
+ * a grow-only workspace per (device, stream), released by
+ * gtr_release_workspace().
+ *
+ * Asynchrony: work is enqueued on `stream` (0 = the null stream) and the call
+ * returns without waiting for it.  The current HIP device must own the
+ * pointers and the stream.
+ *
+ * Errors: on any error nothing is enqueued and a message is available from
+ * gtr_last_error() (thread-local).  Data errors on the device (NaN, Inf,
+ * log_g > 0) are not checked; they propagate.
+ */
+#ifndef GTRSCAN_H
+#define GTRSCAN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GTR_VERSION 100
+#define GTR_RMS_EPS 1e-5f
+
+typedef enum {
+    GTR_OK = 0,
+    GTR_ERR_ARG = -1,          /* null pointer, non-positive size, bad enum or chunk */
+    GTR_ERR_UNSUPPORTED = -2,  /* dk/dv outside {32, 64, 128}, size overflow, path not available */
+    GTR_ERR_HIP = -3           /* no device, allocation or launch failure */
+} gtr_status;
+
+typedef enum { GTR_F32 = 0, GTR_F16 = 1, GTR_BF16 = 2 } gtr_dtype;
+
+typedef enum { GTR_LR = 0, GTR_RL = 1, GTR_TB = 2, GTR_BT = 3 } gtr_direction;
+
+/* Kernel path.  AUTO picks: the single-launch path for B == 1 and L <= 2048
+ * (16-bit I/O), the MFMA chunk path for other 16-bit I/O, and the fp32
+ * token-serial chunk path for float32 I/O or dk/dv it does not cover. */
+typedef enum {
+    GTR_PATH_AUTO = 0,
+    GTR_PATH_MFMA = 1,    /* three launches: segment summaries, state scan, chunk outputs */
+    GTR_PATH_FAST = 2,    /* one launch; B == 1, L <= 2048, 16-bit I/O */
+    GTR_PATH_SERIAL = 3   /* fp32 arithmetic, token-serial inside each chunk */
+} gtr_path;
+
+/*
+ * One mixer call (one block's token mixing).
+ *   direction : gtr_direction
+ *   chunk     : 0 (library default, 64) or one of 16, 32, 64, 128
+ *   dtype     : I/O type of q, k, v, z, out
+ * Returns GTR_OK or an error status.
+ */
+gtr_status gtr_gla_fwd(const void *q, const void *k, const void *v, const float *log_g,
+                       const void *z, const float *rms_w, void *out,
+                       int B, int H, int grid_h, int grid_w, int dk, int dv,
+                       int direction, int chunk, gtr_dtype dtype, hipStream_t stream);
+
+/* gtr_gla_fwd with an explicit kernel path (gtr_path); a path that cannot take
+ * the arguments returns GTR_ERR_UNSUPPORTED.  Used to check paths against
+ * each other. */
+gtr_status gtr_gla_fwd_path(const void *q, const void *k, const void *v, const float *log_g,
+                            const void *z, const float *rms_w, void *out,
+                            int B, int H, int grid_h, int grid_w, int dk, int dv,
+                            int direction, int chunk, gtr_dtype dtype, int path,
+                            hipStream_t stream);
+
+/* gtr_gla_fwd_path that also records `events` (hipEvent_t handles created by
+ * the caller) on `stream`: events[0] before the first kernel launch and
+ * events[i] after launch i, for as many as n_events allows.  The launches of a
+ * call are, in order: MFMA path -- segment summaries, state scan, chunk
+ * outputs; serial path -- chunk summaries, state scan, chunk outputs; fast
+ * path -- one kernel.  For timing single kernels.  *n_launches (nullable)
+ * receives the number of launches of the call. */
+gtr_status gtr_gla_fwd_events(const void *q, const void *k, const void *v, const float *log_g,
+                              const void *z, const float *rms_w, void *out,
+                              int B, int H, int grid_h, int grid_w, int dk, int dv,
+                              int direction, int chunk, gtr_dtype dtype, int path,
+                              hipEvent_t *events, int n_events, int *n_launches,
+                              hipStream_t stream);
+
+/*
+ * A stack of n_blocks mixer calls (Method §1: the scan direction cycles
+ * LR, RL, TB, BT with depth and grid order is restored after every block).
+ * Every tensor gains a leading [n_blocks] dimension: q, k, log_g, v, z as
+ * above per block, rms_w is [n_blocks, dv], and out is [n_blocks, B, grid_h,
+ * grid_w, H, dv] and receives every block's output.  Block i scans direction
+ * (first_direction + i) mod 4 and uses the value input
+ *     v_eff_i = round_io(v_i + out_{i-1})   (i > 0; float32 add),  v_eff_0 = v_0,
+ * the previous block's output fed forward as a residual.  Blocks are ordered
+ * on `stream`; there is no host synchronisation between them.
+ */
+gtr_status gtr_gla_stack_fwd(const void *q, const void *k, const void *v, const float *log_g,
+                             const void *z, const float *rms_w, void *out, int n_blocks,
+                             int B, int H, int grid_h, int grid_w, int dk, int dv,
+                             int first_direction, int chunk, gtr_dtype dtype,
+                             hipStream_t stream);
+
+/* Message of the calling thread's last error ("" if none).  Never NULL. */
+const char *gtr_last_error(void);
+
+/* GTR_VERSION of the built library. */
+int gtr_version(void);
+
+/* Frees every cached workspace after synchronising the device that owns it. */
+void gtr_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GTRSCAN_H */

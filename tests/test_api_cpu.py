@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI (no GPU needed): exports, versions, argument errors."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from gated_token_recurrence_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for hdr in os.listdir(os.path.join(ROOT, "include")):
+        if hdr.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", hdr)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(gtr_[a-z_0-9]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert {"gtr_gla_fwd", "gtr_gla_stack_fwd", "gtr_last_error"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+    assert set(_lib.EXPORTS) == set(declared)
+
+
+def test_version():
+    assert _lib.load().gtr_version() == 100
+
+
+P = [(i + 1) << 36 for i in range(7)]  # distinct far-apart fake pointers, never dereferenced
+
+
+def _call(**kw):
+    a = dict(B=1, H=2, gh=8, gw=8, dk=32, dv=32, direction=0, chunk=16, dtype=0)
+    a.update(kw)
+    lib = _lib.load()
+    return lib.gtr_gla_fwd(*P, a["B"], a["H"], a["gh"], a["gw"], a["dk"], a["dv"],
+                           a["direction"], a["chunk"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), _lib.GTR_ERR_ARG), (dict(H=-1), _lib.GTR_ERR_ARG),
+    (dict(gh=0), _lib.GTR_ERR_ARG), (dict(direction=4), _lib.GTR_ERR_ARG),
+    (dict(direction=-1), _lib.GTR_ERR_ARG), (dict(chunk=48), _lib.GTR_ERR_ARG),
+    (dict(dtype=3), _lib.GTR_ERR_ARG), (dict(dk=48), _lib.GTR_ERR_UNSUPPORTED),
+    (dict(dv=256), _lib.GTR_ERR_UNSUPPORTED),
+])
+def test_bad_arguments_are_rejected(kw, status):
+    assert _call(**kw) == status
+    assert _lib.last_error() != ""
+
+
+def test_null_pointer_is_rejected():
+    lib = _lib.load()
+    st = lib.gtr_gla_fwd(None, *P[1:], 1, 1, 8, 8, 32, 32, 0, 0, 0, None)
+    assert st == _lib.GTR_ERR_ARG and "null" in _lib.last_error()
+
+
+def test_out_aliasing_input_is_rejected():
+    lib = _lib.load()
+    st = lib.gtr_gla_fwd(*P[:6], P[0], 1, 1, 8, 8, 32, 32, 0, 0, 0, None)
+    assert st == _lib.GTR_ERR_ARG and "overlaps" in _lib.last_error()
+
+
+def test_stack_rejects_bad_block_count():
+    lib = _lib.load()
+    st = lib.gtr_gla_stack_fwd(*P, 0, 1, 1, 8, 8, 32, 32, 0, 0, 0, None)
+    assert st == _lib.GTR_ERR_ARG
+
+
+def test_unknown_path_is_rejected():
+    lib = _lib.load()
+    st = lib.gtr_gla_fwd_path(*P, 1, 1, 8, 8, 32, 32, 0, 0, 0, 9, None)
+    assert st == _lib.GTR_ERR_ARG
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device error path")
+def test_valid_call_without_device_reports_hip_error():
+    assert _call() == _lib.GTR_ERR_HIP
+    assert "device" in _lib.last_error()
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "gated_token_recurrence_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b|gtr_oracle|libgtr_oracle",
+                                     text, flags=re.M), f
