@@ -42,7 +42,7 @@ def log(msg):
 class Hip:
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so")
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreate.argtypes = [ctypes.c_void_p]
         self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
@@ -51,8 +51,9 @@ class Hip:
 
     def events(self, n):
         arr = (ctypes.c_void_p * n)()
+        base = ctypes.addressof(arr)
         for i in range(n):
-            if self.lib.hipEventCreate(ctypes.byref(arr, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+            if self.lib.hipEventCreate(base + i * ctypes.sizeof(ctypes.c_void_p)) != 0:
                 raise RuntimeError("hipEventCreate failed")
         return arr
 
@@ -245,16 +246,15 @@ LAUNCH_NAMES = {
 }
 
 
-def resolve_path(w, requested):
+def resolve_path(w, requested, chunk=0):
+    """The path the library runs: the requested one, or the one AUTO selects."""
     if requested != g.PATH_AUTO:
         return requested
-    if w.dtype == "f32":
-        return g.PATH_SERIAL
-    return g.PATH_MFMA if _mfma_available(w) else g.PATH_SERIAL
-
-
-def _mfma_available(w):
-    return w.dk == 64 and w.dv in (64, 128)
+    p = _lib.load().gtr_gla_auto_path(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, chunk,
+                                      W.DTYPE_CODE[w.dtype])
+    if p < 0:
+        raise _lib.GtrError(p, _lib.last_error())
+    return p
 
 
 def main():
@@ -280,7 +280,7 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     chunk = args.chunk or w.chunk
-    path = resolve_path(w, args.path)
+    path = resolve_path(w, args.path, chunk)
     pname = PATH_NAMES[path]
     log(f"workload {w.name}: B={w.B} grid {w.grid_h}x{w.grid_w} H={w.H} dk={w.dk} dv={w.dv} "
         f"{w.dtype} chunk {chunk} path {pname}")
@@ -311,7 +311,7 @@ def main():
     if not args.no_extra:
         for name in ("mixer_640", "mixer_640_wide"):
             we = W.WORKLOADS[name]
-            pe = resolve_path(we, g.PATH_AUTO if args.path == g.PATH_AUTO else args.path)
+            pe = resolve_path(we, args.path, we.chunk)
             try:
                 _, r = time_workload(we, dev, hip, sp, args.steps, args.warmup, pe, we.chunk,
                                      per_kernel=False)

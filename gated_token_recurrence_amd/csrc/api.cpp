@@ -5,6 +5,7 @@
 // positive log-gates) is not inspected.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <map>
@@ -126,12 +127,28 @@ struct Marks {
 constexpr int kDefaultChunk = 64;
 constexpr int kFastMaxTokens = 2048;
 
-// Segment length of the MFMA path, in chunks: enough workgroups to fill the
-// chip (256 CUs) while keeping the per-segment state traffic small.
+// Segment length of the MFMA path, in chunks.  Workgroups (one per segment)
+// run about two per CU on 256 CUs; a launch with n workgroups takes
+// ceil(n / 512) rounds of sc chunk-times each, and every segment adds about
+// one chunk-time of state traffic (summary write, scan, state read).  Pick the
+// segment length that minimises rounds * (sc + 1); ties go to longer segments.
+int g_segment_chunks = 0;  // 0: automatic (gtr_set_segment_chunks)
+
 int segment_chunks(int64_t n_seq, int64_t n_chunks) {
-    int sc = 1;
-    while (sc < 16 && n_seq * ((n_chunks + 2 * sc - 1) / (2 * sc)) >= 512) sc *= 2;
-    return sc;
+    if (g_segment_chunks > 0) return g_segment_chunks;
+    int best = 1;
+    int64_t best_cost = INT64_MAX;
+    for (int sc = 1; sc <= 64; ++sc) {
+        const int64_t n_seg = (n_chunks + sc - 1) / sc;
+        const int64_t rounds = (n_seq * n_seg + 511) / 512;
+        const int64_t cost = rounds * (sc + 1);
+        if (cost <= best_cost) {
+            best_cost = cost;
+            best = sc;
+        }
+        if (n_seg == 1) break;
+    }
+    return best;
 }
 
 gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk) {
@@ -184,11 +201,16 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
     return GTR_OK;
 }
 
+int auto_path(const GlaArgs &a) {
+    const bool mfma_ok = a.dtype != GTR_F32 && mfma_supported(a);
+    return mfma_ok ? GTR_PATH_MFMA : GTR_PATH_SERIAL;
+}
+
 gtr_status run(const GlaArgs &a0, int path, hipStream_t st, Marks &mk) {
     GlaArgs a = a0;
     if (a.chunk == 0) a.chunk = kDefaultChunk;
     const bool mfma_ok = a.dtype != GTR_F32 && mfma_supported(a);
-    if (path == GTR_PATH_AUTO) path = mfma_ok ? GTR_PATH_MFMA : GTR_PATH_SERIAL;
+    if (path == GTR_PATH_AUTO) path = auto_path(a);
     switch (path) {
     case GTR_PATH_SERIAL: return run_serial(a, st, mk);
     case GTR_PATH_MFMA:
@@ -315,9 +337,25 @@ gtr_status gtr_gla_stack_fwd(const void *q, const void *k, const void *v, const 
     return GTR_OK;
 }
 
+int gtr_gla_auto_path(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
+                      gtr_dtype dtype) {
+    g_err.clear();
+    const int fake = 1;
+    gtr_status s = check(&fake, &fake, &fake, reinterpret_cast<const float *>(&fake), &fake,
+                         reinterpret_cast<const float *>(&fake), &fake, B, H, grid_h, grid_w, dk,
+                         dv, 0, chunk, dtype, GTR_PATH_AUTO);
+    if (s != GTR_OK) return s;
+    GlaArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H,
+              grid_h, grid_w, dk, dv, 0, chunk ? chunk : kDefaultChunk, dtype,
+              static_cast<int64_t>(grid_h) * grid_w};
+    return auto_path(a);
+}
+
 const char *gtr_last_error(void) { return g_err.c_str(); }
 
 int gtr_version(void) { return GTR_VERSION; }
+
+void gtr_set_segment_chunks(int chunks) { g_segment_chunks = chunks > 0 ? chunks : 0; }
 
 void gtr_release_workspace(void) {
     std::lock_guard<std::mutex> lock(g_ws_mu);

@@ -128,11 +128,21 @@ gtr_status gtr_gla_stack_fwd(const void *q, const void *k, const void *v, const 
                              int first_direction, int chunk, gtr_dtype dtype,
                              hipStream_t stream);
 
+/* The gtr_path that GTR_PATH_AUTO selects for these arguments, or a negative
+ * gtr_status if the arguments are invalid (no device access). */
+int gtr_gla_auto_path(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
+                      gtr_dtype dtype);
+
 /* Message of the calling thread's last error ("" if none).  Never NULL. */
 const char *gtr_last_error(void);
 
 /* GTR_VERSION of the built library. */
 int gtr_version(void);
+
+/* Tuning hook: number of chunks per segment of the MFMA path (one workgroup per
+ * segment); 0 restores the automatic choice.  Process-wide; results do not
+ * depend on it beyond rounding. */
+void gtr_set_segment_chunks(int chunks);
 
 /* Frees every cached workspace after synchronising the device that owns it. */
 void gtr_release_workspace(void);

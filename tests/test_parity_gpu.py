@@ -8,13 +8,11 @@ import pytest
 import torch
 
 import gated_token_recurrence_amd as g
-from gated_token_recurrence_amd import workloads as W
+from gated_token_recurrence_amd import _lib, workloads as W
 
 from _helpers import assert_parity, errors, inputs_f64, inputs_to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
-
-DEV = "cuda"
 
 
 def _note(msg):
@@ -34,6 +32,14 @@ def _oracle(oracle_mod, x, dtype, direction, bh=None):
     return oracle_mod.fwd(f["q"], f["k"], f["v"], f["log_g"], f["z"], f["rms_w"], direction, bh=bh)
 
 
+@pytest.fixture
+def segment_chunks():
+    """Force the MFMA path's segment length; restores the automatic choice."""
+    lib = _lib.load()
+    yield lib.gtr_set_segment_chunks
+    lib.gtr_set_segment_chunks(0)
+
+
 @pytest.mark.parametrize("direction", [0, 1, 2, 3])
 def test_tiny_fp32_all_directions(oracle_mod, direction):
     w = W.WORKLOADS["tiny"]
@@ -44,7 +50,7 @@ def test_tiny_fp32_all_directions(oracle_mod, direction):
     assert_parity(got, ref, w.dtype, oracle_mod, f"tiny dir {direction}")
 
 
-SHAPES = [
+SERIAL_SHAPES = [
     # B, gh, gw, H, dk, dv, dtype, chunk
     (1, 7, 9, 2, 32, 32, "f32", 16),
     (2, 5, 13, 3, 64, 64, "f32", 32),
@@ -57,51 +63,140 @@ SHAPES = [
     (1, 70, 1, 1, 64, 64, "f16", 16),
 ]
 
+MFMA_SHAPES = [
+    (1, 17, 15, 2, 64, 64, "f16", 64),
+    (1, 17, 15, 2, 64, 64, "bf16", 64),
+    (2, 12, 12, 2, 64, 128, "bf16", 64),
+    (1, 11, 13, 2, 64, 128, "f16", 64),
+    (1, 9, 10, 3, 64, 64, "f16", 32),
+    (1, 9, 10, 1, 64, 128, "bf16", 32),
+    (1, 23, 19, 1, 64, 64, "bf16", 128),
+    (1, 21, 13, 2, 64, 64, "f16", 128),
+    (1, 1, 1, 2, 64, 64, "f16", 64),
+    (1, 1, 70, 1, 64, 64, "bf16", 32),
+    (1, 70, 1, 1, 64, 128, "f16", 64),
+]
 
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-@pytest.mark.parametrize("path", [g.PATH_SERIAL])
-def test_ragged_shapes(oracle_mod, shape, path):
+
+def _shape_case(oracle_mod, shape, path, seed):
     B, gh, gw, H, dk, dv, dtype, chunk = shape
-    x = W.make_custom(B, gh, gw, H, dk, dv, dtype, seed=1 + SHAPES.index(shape))
+    x = W.make_custom(B, gh, gw, H, dk, dv, dtype, seed=seed)
     for direction in range(4):
         _note(f"shape {shape} path {path} direction {direction}")
         got = _run(x, dtype, direction, chunk=chunk, path=path)
         ref = _oracle(oracle_mod, x, dtype, direction)
-        assert_parity(got, ref, dtype, oracle_mod, f"{shape} dir {direction}")
+        assert_parity(got, ref, dtype, oracle_mod, f"{shape} path {path} dir {direction}")
+
+
+@pytest.mark.parametrize("shape", SERIAL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_serial_path_shapes(oracle_mod, shape):
+    _shape_case(oracle_mod, shape, g.PATH_SERIAL, 1 + SERIAL_SHAPES.index(shape))
+
+
+@pytest.mark.parametrize("shape", MFMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_mfma_path_shapes(oracle_mod, shape):
+    _shape_case(oracle_mod, shape, g.PATH_MFMA, 100 + MFMA_SHAPES.index(shape))
+
+
+@pytest.mark.parametrize("sc", [1, 2, 3, 5])
+def test_mfma_segment_lengths(oracle_mod, segment_chunks, sc):
+    x = W.make_custom(1, 30, 31, 2, 64, 64, "f16", seed=17)
+    segment_chunks(sc)
+    for direction in (1, 2):
+        _note(f"segment length {sc} chunks, direction {direction}")
+        got = _run(x, "f16", direction, chunk=64, path=g.PATH_MFMA)
+        ref = _oracle(oracle_mod, x, "f16", direction)
+        assert_parity(got, ref, "f16", oracle_mod, f"segments of {sc}")
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128])
 def test_chunk_sizes_agree(oracle_mod, chunk):
     x = W.make_custom(1, 20, 20, 2, 64, 64, "f32", seed=7)
-    _note(f"chunk invariance chunk={chunk}")
+    _note(f"chunk invariance (serial) chunk={chunk}")
     got = _run(x, "f32", 2, chunk=chunk, path=g.PATH_SERIAL)
     ref = _oracle(oracle_mod, x, "f32", 2)
     assert_parity(got, ref, "f32", oracle_mod, f"chunk {chunk}")
+
+
+def test_mfma_chunk_sizes_agree(oracle_mod):
+    x = W.make_custom(1, 33, 29, 2, 64, 64, "bf16", seed=8)
+    ref = _oracle(oracle_mod, x, "bf16", 3)
+    outs = {}
+    for chunk in (32, 64, 128):
+        _note(f"chunk invariance (MFMA) chunk={chunk}")
+        outs[chunk] = _run(x, "bf16", 3, chunk=chunk, path=g.PATH_MFMA)
+        assert_parity(outs[chunk], ref, "bf16", oracle_mod, f"mfma chunk {chunk}")
 
 
 @pytest.mark.parametrize("log_g", [0.0, -1e-4, -20.0])
 def test_extreme_gates(oracle_mod, log_g):
     x = W.make_custom(1, 16, 16, 2, 64, 64, "f32", seed=3, log_g_const=log_g)
     for direction in (0, 3):
-        _note(f"constant log_g={log_g} direction={direction}")
+        _note(f"constant log_g={log_g} direction={direction} (serial)")
         got = _run(x, "f32", direction, chunk=64, path=g.PATH_SERIAL)
         ref = _oracle(oracle_mod, x, "f32", direction)
         assert_parity(got, ref, "f32", oracle_mod, f"log_g {log_g}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("log_g", [0.0, -1e-4, -0.5, -20.0])
+def test_mfma_extreme_gates(oracle_mod, dtype, log_g):
+    """Constant gates, including spans beyond the factored diagonal (pairwise tile)."""
+    x = W.make_custom(1, 16, 16, 2, 64, 64, dtype, seed=4, log_g_const=log_g)
+    for direction in (0, 3):
+        _note(f"MFMA constant log_g={log_g} {dtype} direction={direction}")
+        got = _run(x, dtype, direction, chunk=64, path=g.PATH_MFMA)
+        ref = _oracle(oracle_mod, x, dtype, direction)
+        assert_parity(got, ref, dtype, oracle_mod, f"mfma log_g {log_g}")
+
+
+def test_mfma_mixed_spans(oracle_mod):
+    """Sharp gates on a few tokens: some sub-blocks take the pairwise diagonal, others not."""
+    x = W.make_custom(1, 24, 24, 2, 64, 64, "f16", seed=5)
+    lg = x["log_g"].reshape(-1, 2, 64)
+    rng = np.random.default_rng(5)
+    hit = rng.choice(lg.shape[0], size=40, replace=False)
+    lg[hit] = -12.0
+    for direction in range(4):
+        _note(f"MFMA mixed spans direction={direction}")
+        got = _run(x, "f16", direction, chunk=64, path=g.PATH_MFMA)
+        ref = _oracle(oracle_mod, x, "f16", direction)
+        assert_parity(got, ref, "f16", oracle_mod, f"mixed spans dir {direction}")
 
 
 @pytest.mark.parametrize("name", ["mixer_640", "mixer_640_wide"])
 def test_mixer_640_workloads(oracle_mod, name):
     w = W.WORKLOADS[name]
     x = W.make_inputs(w)
-    ref_cache = {}
     for direction in range(4):
         _note(f"{name} direction {direction}")
         got = _run(x, w.dtype, direction, chunk=w.chunk)
-        ref_cache[direction] = _oracle(oracle_mod, x, w.dtype, direction)
-        rel, mx = assert_parity(got, ref_cache[direction], w.dtype, oracle_mod,
-                                f"{name} dir {direction}")
-        urel, _ = errors(got, ref_cache[direction], "f32", oracle_mod)
+        ref = _oracle(oracle_mod, x, w.dtype, direction)
+        rel, mx = assert_parity(got, ref, w.dtype, oracle_mod, f"{name} dir {direction}")
+        urel, _ = errors(got, ref, "f32", oracle_mod)
         _note(f"  rel-L2 {rel:.2e} (unrounded {urel:.2e}) max-abs {mx:.2e}")
+
+
+def test_mixer_640_serial_path_too(oracle_mod):
+    w = W.WORKLOADS["mixer_640"]
+    x = W.make_inputs(w)
+    _note("mixer_640 serial path")
+    got = _run(x, w.dtype, 2, chunk=w.chunk, path=g.PATH_SERIAL)
+    ref = _oracle(oracle_mod, x, w.dtype, 2)
+    assert_parity(got, ref, w.dtype, oracle_mod, "mixer_640 serial")
+
+
+@pytest.mark.timeout(300)
+def test_mixer_2048_full_size(oracle_mod):
+    """The 16.4K-token workload in the configuration the benchmark times, all directions."""
+    w = W.WORKLOADS["mixer_2048"]
+    x = W.make_inputs(w)
+    for direction in range(4):
+        _note(f"mixer_2048 direction {direction}")
+        got = _run(x, w.dtype, direction, chunk=w.chunk)
+        ref = _oracle(oracle_mod, x, w.dtype, direction)
+        rel, mx = assert_parity(got, ref, w.dtype, oracle_mod, f"mixer_2048 dir {direction}")
+        _note(f"  rel-L2 {rel:.2e} max-abs {mx:.2e}")
 
 
 def test_run_to_run_bitwise(oracle_mod):
@@ -113,15 +208,48 @@ def test_run_to_run_bitwise(oracle_mod):
         assert np.array_equal(a, _run(x, w.dtype, 1))
 
 
-def test_small_stack(oracle_mod):
-    nb, B, gh, gw, H, dk, dv, dtype = 5, 2, 9, 10, 2, 64, 128, "bf16"
-    blocks = [W.make_custom(B, gh, gw, H, dk, dv, dtype, seed=100 + i) for i in range(nb)]
+def _stack_case(oracle_mod, nb, B, gh, gw, H, dk, dv, dtype, chunk, first, bh=None, seeds=None):
+    if seeds is None:
+        blocks = [W.make_custom(B, gh, gw, H, dk, dv, dtype, seed=100 + i) for i in range(nb)]
+    else:
+        blocks = seeds
     stk = {key: np.stack([b[key] for b in blocks]) for key in ("q", "k", "v", "z", "log_g", "rms_w")}
     t = inputs_to_dev(stk, dtype)
-    _note("stack 5 blocks bf16")
-    out = g.gla_stack_fwd(t["q"], t["k"], t["v"], t["log_g"], t["z"], t["rms_w"], 1, chunk=32)
+    del stk
+    out = g.gla_stack_fwd(t["q"], t["k"], t["v"], t["log_g"], t["z"], t["rms_w"], first,
+                          chunk=chunk)
     torch.cuda.synchronize()
     got = to_f64(out)
-    refs = oracle_mod.stack_fwd([inputs_f64(b, dtype) for b in blocks], 1, dtype)
+    del t, out
+    refs = oracle_mod.stack_fwd([inputs_f64(b, dtype) for b in blocks], first, dtype, bh=bh)
     for i in range(nb):
-        assert_parity(got[i], refs[i], dtype, oracle_mod, f"stack block {i}")
+        gi, ri = got[i], refs[i]
+        if bh is not None:
+            sel = [(s // H, s % H) for s in bh]
+            gi = np.stack([gi[b_, :, :, h_] for b_, h_ in sel])
+            ri = np.stack([ri[b_, :, :, h_] for b_, h_ in sel])
+        rel, mx = assert_parity(gi, ri, dtype, oracle_mod, f"stack block {i}")
+        _note(f"  block {i} (direction {(first + i) % 4}): rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
+def test_small_stack_serial_shapes(oracle_mod):
+    _note("stack 5 blocks bf16 dk=32 (serial path)")
+    _stack_case(oracle_mod, 5, 2, 9, 10, 2, 32, 64, "bf16", 32, 1)
+
+
+def test_small_stack_mfma(oracle_mod):
+    _note("stack 5 blocks bf16 dk=64 dv=128 (MFMA path)")
+    _stack_case(oracle_mod, 5, 2, 9, 10, 2, 64, 128, "bf16", 64, 1)
+
+
+@pytest.mark.timeout(600)
+def test_stack_1024_full_size_sampled(oracle_mod):
+    """The 12-block stack at full size (B=8, 64x64, H=12, dk=64, dv=128, bf16), free-running;
+    the oracle follows three (batch, head) sequences through all 12 blocks."""
+    w = W.WORKLOADS["stack_1024"]
+    _note("stack_1024: generating 12 blocks of inputs")
+    blocks = [W.make_inputs(w, block=i) for i in range(w.n_blocks)]
+    bh = [0, 5 * w.H + 7, (w.B - 1) * w.H + w.H - 1]
+    _note("stack_1024: running")
+    _stack_case(oracle_mod, w.n_blocks, w.B, w.grid_h, w.grid_w, w.H, w.dk, w.dv, w.dtype,
+                w.chunk, 0, bh=bh, seeds=blocks)
