@@ -257,6 +257,27 @@ def resolve_path(w, requested, chunk=0):
     return p
 
 
+COPY_BYTES = 256 << 20
+
+
+def profile_run(w, dev, sp, steps, path, chunk):
+    """Workload calls for counter collection, preceded by a copy of known size."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    dst.copy_(src)                      # calibration: reads and writes COPY_BYTES
+    torch.cuda.synchronize(dev)
+    del src, dst
+    lib = _lib.load()
+    n_sets = W.rotation_sets(w.compulsory_bytes())
+    _, sets = device_sets(w, n_sets, dev)
+    for i in range(steps):
+        call(lib, w, sets[i % n_sets], 0, chunk, path, sp)
+    torch.cuda.synchronize(dev)
+    log(f"profile run: {steps} calls of {w.name} ({PATH_NAMES[path]} path), "
+        f"calibration copy {COPY_BYTES} bytes")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,6 +288,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="for rocprofv3 counter passes: a plain 256 MiB device copy (the "
+                         "calibration kernel), then --steps calls of the workload; no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -281,6 +305,9 @@ def main():
     w = W.WORKLOADS[args.workload]
     chunk = args.chunk or w.chunk
     path = resolve_path(w, args.path, chunk)
+    if args.profile_run:
+        profile_run(w, dev, sp, args.steps, path, chunk)
+        return
     pname = PATH_NAMES[path]
     log(f"workload {w.name}: B={w.B} grid {w.grid_h}x{w.grid_w} H={w.H} dk={w.dk} dv={w.dv} "
         f"{w.dtype} chunk {chunk} path {pname}")

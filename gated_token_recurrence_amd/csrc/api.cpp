@@ -88,6 +88,8 @@ gtr_status check(const void *q, const void *k, const void *v, const float *log_g
         return fail(GTR_ERR_ARG, "direction must be 0..3 (LR, RL, TB, BT), got %d", direction);
     if (!(chunk == 0 || chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128))
         return fail(GTR_ERR_ARG, "chunk must be 0, 16, 32, 64 or 128, got %d", chunk);
+    if (static_cast<int64_t>(gh) * gw >= (static_cast<int64_t>(1) << 31))
+        return fail(GTR_ERR_UNSUPPORTED, "grid_h * grid_w must be below 2^31 tokens");
     if (dtype < GTR_F32 || dtype > GTR_BF16)
         return fail(GTR_ERR_ARG, "unknown dtype %d", dtype);
     if (path < GTR_PATH_AUTO || path > GTR_PATH_SERIAL)
@@ -127,29 +129,7 @@ struct Marks {
 constexpr int kDefaultChunk = 64;
 constexpr int kFastMaxTokens = 2048;
 
-// Segment length of the MFMA path, in chunks.  Workgroups (one per segment)
-// run about two per CU on 256 CUs; a launch with n workgroups takes
-// ceil(n / 512) rounds of sc chunk-times each, and every segment adds about
-// one chunk-time of state traffic (summary write, scan, state read).  Pick the
-// segment length that minimises rounds * (sc + 1); ties go to longer segments.
-int g_segment_chunks = 0;  // 0: automatic (gtr_set_segment_chunks)
-
-int segment_chunks(int64_t n_seq, int64_t n_chunks) {
-    if (g_segment_chunks > 0) return g_segment_chunks;
-    int best = 1;
-    int64_t best_cost = INT64_MAX;
-    for (int sc = 1; sc <= 64; ++sc) {
-        const int64_t n_seg = (n_chunks + sc - 1) / sc;
-        const int64_t rounds = (n_seq * n_seg + 511) / 512;
-        const int64_t cost = rounds * (sc + 1);
-        if (cost <= best_cost) {
-            best_cost = cost;
-            best = sc;
-        }
-        if (n_seg == 1) break;
-    }
-    return best;
-}
+int g_chunks_per_wg = 0;  // 0: automatic (gtr_set_segment_chunks)
 
 gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk) {
     const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
@@ -176,26 +156,25 @@ gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk) {
 }
 
 gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
-    const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
+    const MfmaPlan pl = mfma_plan(a, g_chunks_per_wg);
     const int64_t n_seq = static_cast<int64_t>(a.B) * a.H;
-    const int sc = segment_chunks(n_seq, n_chunks);
-    const int64_t n_seg = (n_chunks + sc - 1) / sc;
-    if (n_seq * n_seg > 0x7fffffff) return fail(GTR_ERR_UNSUPPORTED, "too many segments");
-    const size_t ubytes = static_cast<size_t>(n_seq * n_seg) * a.dk * a.dv * 4;
-    const size_t gbytes = static_cast<size_t>(n_seq * n_seg) * a.dk * 4;
+    if (pl.n_wg > 0x7fffffff || n_seq * a.dk * a.dv / 256 > 0x7fffffff)
+        return fail(GTR_ERR_UNSUPPORTED, "too many chunks");
+    const size_t ubytes = static_cast<size_t>(pl.n_seg) * a.dk * a.dv * 4;
+    const size_t gbytes = static_cast<size_t>(pl.n_seg) * a.dk * 4;
     void *ws = nullptr;
     gtr_status s = workspace(st, ubytes + gbytes, &ws);
     if (s != GTR_OK) return s;
     float *U = static_cast<float *>(ws);
     float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
     hipError_t e = mk.record(st, 0);
-    if (e == hipSuccess) e = mfma_summary(a, U, G, static_cast<int>(n_seg), sc, st);
+    if (e == hipSuccess) e = mfma_summary(a, pl, U, G, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "segment summary launch");
-    e = state_scan(U, G, static_cast<int>(n_seq), static_cast<int>(n_seg), a.dk, a.dv, st);
+    e = state_scan_plan(U, G, pl, static_cast<int>(n_seq), a.dk, a.dv, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "state scan launch");
-    e = mfma_output(a, U, static_cast<int>(n_seg), sc, st);
+    e = mfma_output(a, pl, U, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "chunk output launch");
     return GTR_OK;
@@ -355,7 +334,7 @@ const char *gtr_last_error(void) { return g_err.c_str(); }
 
 int gtr_version(void) { return GTR_VERSION; }
 
-void gtr_set_segment_chunks(int chunks) { g_segment_chunks = chunks > 0 ? chunks : 0; }
+void gtr_set_segment_chunks(int chunks) { g_chunks_per_wg = chunks > 0 ? chunks : 0; }
 
 void gtr_release_workspace(void) {
     std::lock_guard<std::mutex> lock(g_ws_mu);

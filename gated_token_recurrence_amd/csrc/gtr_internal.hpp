@@ -106,11 +106,30 @@ hipError_t serial_output(const GlaArgs &a, const float *Sx, int n_chunks, hipStr
 // Inter-chunk (or inter-segment) state scan, in place: U[n] <- S before unit n.
 hipError_t state_scan(float *U, const float *G, int n_seq, int n_units, int dk, int dv,
                       hipStream_t s);
-// MFMA chunk path: segments of `seg_chunks` chunks of `chunk` tokens.
+// MFMA chunk path.  The B*H*N chunks (N per sequence, sequence-major) are cut
+// into ranges of Q chunks, one per workgroup; segments are the pieces of those
+// ranges within one sequence.  Segment k starts at the k-th element of the
+// sorted union of the multiples of N and of Q below T.
+struct MfmaPlan {
+    int64_t N;      // chunks per sequence
+    int64_t T;      // chunks in total
+    int64_t Q;      // chunks per workgroup range
+    int64_t n_wg;   // workgroups
+    int64_t lcm;    // lcm(N, Q)
+    int64_t n_seg;  // segments
+};
+constexpr int64_t kMfmaWorkgroups = 512;  // two per CU on 256 CUs
+
+__host__ __device__ __forceinline__ int64_t seg_id(int64_t p, const MfmaPlan &pl) {
+    return (p + pl.N - 1) / pl.N + (p + pl.Q - 1) / pl.Q - (p + pl.lcm - 1) / pl.lcm;
+}
+
 bool mfma_supported(const GlaArgs &a);
-hipError_t mfma_summary(const GlaArgs &a, float *U, float *G, int n_seg, int seg_chunks,
-                        hipStream_t s);
-hipError_t mfma_output(const GlaArgs &a, const float *Sx, int n_seg, int seg_chunks,
-                       hipStream_t s);
+MfmaPlan mfma_plan(const GlaArgs &a, int64_t chunks_per_wg);  // <= 0: automatic
+hipError_t mfma_summary(const GlaArgs &a, const MfmaPlan &pl, float *U, float *G, hipStream_t s);
+hipError_t mfma_output(const GlaArgs &a, const MfmaPlan &pl, const float *Sx, hipStream_t s);
+// State scan over the segments of a plan, in place: U[k] <- state before segment k.
+hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,
+                           int dv, hipStream_t s);
 
 }  // namespace gtr

@@ -46,7 +46,48 @@ __global__ __launch_bounds__(NT) void k_state_scan(float *__restrict__ U,
     }
 }
 
+// The same recurrence over the segments of an MFMA plan: thread = (sequence,
+// state element); the sequence's segments are seg_id(seq N) .. seg_id((seq+1) N) - 1.
+__global__ __launch_bounds__(NT) void k_state_scan_plan(float *__restrict__ U,
+                                                        const float *__restrict__ G,
+                                                        MfmaPlan pl, int64_t n_elem, int dk,
+                                                        int dv) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+    if (e >= n_elem) return;
+    const int64_t dd = static_cast<int64_t>(dk) * dv;
+    const int64_t seq = e / dd;
+    const int64_t el = e - seq * dd;
+    const int c = static_cast<int>(el / dv);
+    const int64_t s0 = seg_id(seq * pl.N, pl), s1 = seg_id((seq + 1) * pl.N, pl);
+    float s = 0.f;
+    constexpr int PF2 = 16;
+    for (int64_t k0 = s0; k0 < s1; k0 += PF2) {
+        float x[PF2], gg[PF2];
+#pragma unroll
+        for (int i = 0; i < PF2; ++i) {
+            const bool ok = k0 + i < s1;
+            x[i] = ok ? U[(k0 + i) * dd + el] : 0.f;
+            gg[i] = ok ? G[(k0 + i) * dk + c] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < PF2; ++i) {
+            if (k0 + i < s1) {
+                U[(k0 + i) * dd + el] = s;
+                s = expf(gg[i]) * s + x[i];
+            }
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,
+                           int dv, hipStream_t s) {
+    const int64_t n_elem = static_cast<int64_t>(n_seq) * dk * dv;
+    const dim3 grid(static_cast<unsigned>((n_elem + NT - 1) / NT));
+    hipLaunchKernelGGL(k_state_scan_plan, grid, dim3(NT), 0, s, U, G, pl, n_elem, dk, dv);
+    return hipGetLastError();
+}
 
 hipError_t state_scan(float *U, const float *G, int n_seq, int n_units, int dk, int dv,
                       hipStream_t s) {

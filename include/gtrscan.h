@@ -139,9 +139,10 @@ const char *gtr_last_error(void);
 /* GTR_VERSION of the built library. */
 int gtr_version(void);
 
-/* Tuning hook: number of chunks per segment of the MFMA path (one workgroup per
- * segment); 0 restores the automatic choice.  Process-wide; results do not
- * depend on it beyond rounding. */
+/* Tuning hook: number of chunks each workgroup of the MFMA path processes (its
+ * range of the sequence-major chunk list); 0 restores the automatic choice
+ * (about 512 workgroups).  Process-wide; results depend on it only through
+ * rounding. */
 void gtr_set_segment_chunks(int chunks);
 
 /* Frees every cached workspace after synchronising the device that owns it. */
