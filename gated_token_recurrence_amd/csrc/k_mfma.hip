@@ -49,7 +49,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int NT = 256;
 constexpr int DK = 64;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kSpanMax = 64.f;
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -121,12 +120,13 @@ struct Cfg {
     static constexpr int O_VT = O_KT + KT;
     static constexpr int O_P = O_VT + VT;
     static constexpr int O_TOT = O_P + PB;                      // float [NB][DK]
-    static constexpr int O_EG = O_TOT + NB * DK * 4;            // float [DK] 2^G
-    static constexpr int O_SS = O_EG + DK * 4;                  // float [4][C]
+    static constexpr int O_TAB = O_TOT + NB * DK * 4;           // float [4 waves][3][DK]
+    static constexpr int O_SS = O_TAB + 4 * 3 * DK * 4;         // float [4][C]
     static constexpr int O_ROW = O_SS + (SUM ? 0 : 4 * C * 4);  // int64 [2][C]
     static constexpr int BYTES = O_ROW + 2 * C * 8;
     static_assert(SUM || C * DK * 4 <= QT, "fallback q must fit");
     static_assert(C * DK * 4 <= KT, "fallback g must fit");
+    static_assert(BPW == 1, "one token sub-block per wave");
 };
 
 template <int DT, int DV, int NB, bool SUM>
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
     bf16 *sVt = reinterpret_cast<bf16 *>(smem + K::O_VT);
     bf16 *sP = reinterpret_cast<bf16 *>(smem + K::O_P);
     float *sTot = reinterpret_cast<float *>(smem + K::O_TOT);
-    float *sEG = reinterpret_cast<float *>(smem + K::O_EG);
+    float *sTab0 = reinterpret_cast<float *>(smem + K::O_TAB);
     float *sSS = reinterpret_cast<float *>(smem + K::O_SS);
     int64_t *sRow = reinterpret_cast<int64_t *>(smem + K::O_ROW);
     float *fQ = reinterpret_cast<float *>(smem + K::O_QT);  // fallback views
@@ -151,16 +151,30 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
+    float *sTab = sTab0 + w * 3 * DK;  // this wave's per-channel tables
     const int64_t p0 = static_cast<int64_t>(blockIdx.x) * pl.Q;
     const int64_t p1 = (p0 + pl.Q < pl.T) ? p0 + pl.Q : pl.T;
     if (p0 >= p1) return;  // the whole workgroup
 
-    auto rows_of = [&](int64_t p, int buf) {
+    // Row index ((b L + grid position) H + h) of every token of chunk ch of sequence bh.
+    const uint32_t L32 = static_cast<uint32_t>(a.L), gh = static_cast<uint32_t>(a.gh),
+                   gw = static_cast<uint32_t>(a.gw);
+    auto rows_of = [&](int64_t bh, int64_t ch, int buf) {
         if (tid < C) {
-            const int64_t bh = p / pl.N, t = (p - bh * pl.N) * C + tid;
-            sRow[buf * C + tid] =
-                (t < a.L) ? scan_row(a, static_cast<int>(bh / a.H), static_cast<int>(bh % a.H), t)
-                          : -1;
+            uint32_t t = static_cast<uint32_t>(ch) * C + tid;
+            int64_t row = -1;
+            if (t < L32) {
+                if (a.direction & 1) t = L32 - 1 - t;  // RL, BT: reversed sequence
+                uint32_t pos = t;
+                if (a.direction >= 2) {                // TB, BT: column-major raster
+                    const uint32_t c = t / gh;
+                    pos = (t - c * gh) * gw + c;
+                }
+                const uint32_t b = static_cast<uint32_t>(bh) / static_cast<uint32_t>(a.H);
+                const uint32_t h = static_cast<uint32_t>(bh) - b * static_cast<uint32_t>(a.H);
+                row = (static_cast<int64_t>(b) * a.L + pos) * a.H + h;
+            }
+            sRow[buf * C + tid] = row;
         }
     };
 
@@ -243,7 +257,9 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
         }
     }
 
-    rows_of(p0, 0);
+    int64_t bh = p0 / pl.N;  // current sequence and chunk, advanced incrementally
+    int64_t ch = p0 - bh * pl.N;
+    rows_of(bh, ch, 0);
     __syncthreads();
     prefetch_main(0);
     prefetch_z(0);
@@ -254,8 +270,7 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
 
     for (int64_t p = p0; p < p1; ++p) {
         const int cur = static_cast<int>((p - p0) & 1);
-        const int64_t bh = p / pl.N;
-        const int64_t ch = p - bh * pl.N;
+        const bool last_in_seq = (ch == pl.N - 1);
         if (p == p0 || ch == 0) {  // segment start: incoming state
             const int64_t sid = seg_id(p, pl);
 #pragma unroll
@@ -312,13 +327,21 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
                 }
             }
         }
-        if (p + 1 < p1) rows_of(p + 1, cur ^ 1);
+        if (p + 1 < p1) rows_of(last_in_seq ? bh + 1 : bh, last_in_seq ? 0 : ch + 1, cur ^ 1);
         __syncthreads();  // B1: sTot, sVt and the next chunk's rows
 
-        // ---- phase 2: chunk totals, span check, operand matrices
-        float tot_l = 0.f;  // channel l
+        // ---- phase 2: chunk totals, span check, operand matrices.
+        // Lane l computes, for channel l: r = sum of the sub-block totals before the
+        // wave's own sub-block, G = the chunk total; the wave's table holds r, G
+        // (log2 units) and 2^G, read back per channel below.
+        const int Iown = (w < NB) ? w : 0;
+        float r_l = 0.f, tot_l = 0.f;
 #pragma unroll
-        for (int J = 0; J < NB; ++J) tot_l += sTot[J * DK + l];
+        for (int J = 0; J < NB; ++J) {
+            const float t = sTot[J * DK + l];
+            if (J < Iown) r_l += t;
+            tot_l += t;
+        }
         bool slow = false;
         if (!SUM) {
             float sp2 = -tot_l;
@@ -326,10 +349,11 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
             for (int off = 32; off >= 1; off >>= 1) sp2 = fmaxf(sp2, __shfl_xor(sp2, off));
             slow = sp2 > kSpanMax;  // identical in every wave
         }
-        if (w == 0) {
-            sEG[l] = fexp2(tot_l);
-            gam += tot_l;
-        }
+        gam += tot_l;
+        sTab[l] = r_l;
+        sTab[DK + l] = tot_l;
+        sTab[2 * DK + l] = fexp2(tot_l);
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int m = 0; m < BPW; ++m) {
             const int I = w + 4 * m;
@@ -338,19 +362,15 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
 #pragma unroll
             for (int kap = 0; kap < 2; ++kap) {
                 const int c0 = 32 * kap + 8 * g;
-                float rI[8], gC[8];
+                float rI[8], gC[8], eG[8];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) { rI[s] = 0.f; gC[s] = 0.f; }
-#pragma unroll
-                for (int J = 0; J < NB; ++J) {
-                    const float4 t0 = *reinterpret_cast<const float4 *>(sTot + J * DK + c0);
-                    const float4 t1 = *reinterpret_cast<const float4 *>(sTot + J * DK + c0 + 4);
-                    const float t8[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        if (J < I) rI[s] += t8[s];
-                        gC[s] += t8[s];
-                    }
+                for (int h4 = 0; h4 < 2; ++h4) {
+                    const float4 x = *reinterpret_cast<const float4 *>(sTab + c0 + 4 * h4);
+                    const float4 y = *reinterpret_cast<const float4 *>(sTab + DK + c0 + 4 * h4);
+                    const float4 z = *reinterpret_cast<const float4 *>(sTab + 2 * DK + c0 + 4 * h4);
+                    rI[4 * h4] = x.x; rI[4 * h4 + 1] = x.y; rI[4 * h4 + 2] = x.z; rI[4 * h4 + 3] = x.w;
+                    gC[4 * h4] = y.x; gC[4 * h4 + 1] = y.y; gC[4 * h4 + 2] = y.z; gC[4 * h4 + 3] = y.w;
+                    eG[4 * h4] = z.x; eG[4 * h4 + 1] = z.y; eG[4 * h4 + 2] = z.z; eG[4 * h4 + 3] = z.w;
                 }
                 float kv[8], qv[8];
 #pragma unroll
@@ -378,7 +398,7 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
                         qh[s] = hi; ql[s] = lo;
                         split(kh_f, hi, lo);
                         kh[s] = hi; kl[s] = lo;
-                        split(kh_f * fexp2(gC[s]), hi, lo);                    // k 2^(G - a)
+                        split(kh_f * eG[s], hi, lo);                            // k 2^(G - a)
                         sKt[sw<CW>(c0 + s, i)] = hi;
                         sKt[DK * CW + sw<CW>(c0 + s, i)] = lo;
                     }
@@ -476,7 +496,7 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
                     f32x4 acc = S[dd][ct];
-                    const float4 e4 = *reinterpret_cast<const float4 *>(sEG + 16 * ct + 4 * g);
+                    const float4 e4 = *reinterpret_cast<const float4 *>(sTab + 2 * DK + 16 * ct + 4 * g);
                     acc[0] *= e4.x; acc[1] *= e4.y; acc[2] *= e4.z; acc[3] *= e4.w;
 #pragma unroll
                     for (int kt = 0; kt < C / 32; ++kt) {
@@ -624,8 +644,14 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
                         for (int r = 0; r < 4; ++r)
                             U[sid * DK * DV + (16 * ct + 4 * g + r) * DV + 16 * (w * DPW + dd) + lr] =
                                 S[dd][ct][r];
-                if (w == 0) Gs[sid * DK + l] = gam * kLn2;
+                if (w == 0) Gs[sid * DK + l] = gam;  // log2 units
             }
+        }
+        if (last_in_seq) {
+            ch = 0;
+            ++bh;
+        } else {
+            ++ch;
         }
     }
 }

@@ -46,35 +46,62 @@ __global__ __launch_bounds__(NT) void k_state_scan(float *__restrict__ U,
     }
 }
 
-// The same recurrence over the segments of an MFMA plan: thread = (sequence,
-// state element); the sequence's segments are seg_id(seq N) .. seg_id((seq+1) N) - 1.
+// The same recurrence over the segments of an MFMA plan (summed gates in log2
+// units).  Workgroup = (sequence, slice of 256 state elements); its segments
+// are seg_id(seq N) .. seg_id((seq + 1) N) - 1.  Segments are fetched in
+// batches, the next batch's loads issued before the current batch's stores, so
+// the dependent chain waits on memory about once per batch.  Loads past the
+// last segment re-read the last one (in bounds, unused).
+constexpr int SB = 16;
+
 __global__ __launch_bounds__(NT) void k_state_scan_plan(float *__restrict__ U,
                                                         const float *__restrict__ G,
-                                                        MfmaPlan pl, int64_t n_elem, int dk,
-                                                        int dv) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
-    if (e >= n_elem) return;
+                                                        MfmaPlan pl, int dk, int dv) {
     const int64_t dd = static_cast<int64_t>(dk) * dv;
-    const int64_t seq = e / dd;
-    const int64_t el = e - seq * dd;
-    const int c = static_cast<int>(el / dv);
+    const int slices = static_cast<int>(dd / NT);
+    const int64_t seq = blockIdx.x / slices;
+    const int64_t el = static_cast<int64_t>(blockIdx.x % slices) * NT + threadIdx.x;
+    // channel of this wave's 64 consecutive elements (dv >= 64): wave-uniform
+    const int c = __builtin_amdgcn_readfirstlane(static_cast<int>(el / dv));
     const int64_t s0 = seg_id(seq * pl.N, pl), s1 = seg_id((seq + 1) * pl.N, pl);
-    float s = 0.f;
-    constexpr int PF2 = 16;
-    for (int64_t k0 = s0; k0 < s1; k0 += PF2) {
-        float x[PF2], gg[PF2];
+    float *u = U + el;
+    const float *gp = G + c;
+    // batch starting at segment kb: values of segments kb .. kb + SB - 1; past the
+    // last segment the pointers stop advancing (in bounds, values unused)
+    auto fetch = [&](int64_t kb, float *xo, float *go) {
+        const int64_t base = (kb < s1) ? kb : s1 - 1;
+        const int nb = (s1 - base < SB) ? static_cast<int>(s1 - base) : SB;
+        const float *up = u + base * dd;
+        const float *gq = gp + base * dk;
 #pragma unroll
-        for (int i = 0; i < PF2; ++i) {
-            const bool ok = k0 + i < s1;
-            x[i] = ok ? U[(k0 + i) * dd + el] : 0.f;
-            gg[i] = ok ? G[(k0 + i) * dk + c] : 0.f;
+        for (int i = 0; i < SB; ++i) {
+            xo[i] = *up;
+            go[i] = *gq;
+            const bool adv = i + 1 < nb;
+            up += adv ? dd : 0;
+            gq += adv ? dk : 0;
+        }
+    };
+    float x[SB], gg[SB];
+    fetch(s0, x, gg);
+    float s = 0.f;
+    for (int64_t k0 = s0; k0 < s1; k0 += SB) {
+        float xn[SB], gn[SB];
+        fetch(k0 + SB, xn, gn);
+        const int n = (s1 - k0 < SB) ? static_cast<int>(s1 - k0) : SB;
+        float *ub = u + k0 * dd;
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+            if (i < n) {
+                *ub = s;
+                s = __builtin_amdgcn_exp2f(gg[i]) * s + x[i];
+                ub += dd;
+            }
         }
 #pragma unroll
-        for (int i = 0; i < PF2; ++i) {
-            if (k0 + i < s1) {
-                U[(k0 + i) * dd + el] = s;
-                s = expf(gg[i]) * s + x[i];
-            }
+        for (int i = 0; i < SB; ++i) {
+            x[i] = xn[i];
+            gg[i] = gn[i];
         }
     }
 }
@@ -83,9 +110,10 @@ __global__ __launch_bounds__(NT) void k_state_scan_plan(float *__restrict__ U,
 
 hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,
                            int dv, hipStream_t s) {
-    const int64_t n_elem = static_cast<int64_t>(n_seq) * dk * dv;
-    const dim3 grid(static_cast<unsigned>((n_elem + NT - 1) / NT));
-    hipLaunchKernelGGL(k_state_scan_plan, grid, dim3(NT), 0, s, U, G, pl, n_elem, dk, dv);
+    if ((static_cast<int64_t>(dk) * dv) % NT != 0 || dv < 64) return hipErrorInvalidValue;
+    const int64_t n_wg = static_cast<int64_t>(n_seq) * (static_cast<int64_t>(dk) * dv / NT);
+    hipLaunchKernelGGL(k_state_scan_plan, dim3(static_cast<unsigned>(n_wg)), dim3(NT), 0, s, U, G,
+                       pl, dk, dv);
     return hipGetLastError();
 }
 
