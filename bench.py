@@ -164,57 +164,80 @@ def time_workload(w, dev, hip, stream_ptr, steps, warmup, path, chunk, direction
         res["us_per_call_evented_p90"] = float(np.percentile(calls, 90))
 
     if graph:
-        # hipGraph replay of one call per buffer set (the pages' own kernel
-        # benchmark used graph launch).
-        s = torch.cuda.Stream(device=dev)
-        sp = s.cuda_stream
-        with torch.cuda.stream(s):
-            for i in range(n_sets):
-                call(lib, w, sets[i], direction, chunk, path, sp)
-        torch.cuda.synchronize(dev)
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr, stream=s):
-            for i in range(n_sets):
-                call(lib, w, sets[i], direction, chunk, path, sp)
-        torch.cuda.synchronize(dev)
-        reps = max(1, steps // n_sets)
-        for _ in range(2):
-            gr.replay()
-        torch.cuda.synchronize(dev)
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(reps):
-            gr.replay()
-        t1.record()
-        torch.cuda.synchronize(dev)
-        res["us_per_call_graph"] = t0.elapsed_time(t1) * 1e3 / (reps * n_sets)
-        del gr
+        try:
+            res["us_per_call_graph"] = graph_time(lib, w, sets, n_sets, dev, direction, chunk,
+                                                  path, steps)
+        except Exception as exc:  # e.g. a launch kind that stream capture does not take
+            res["us_per_call_graph"] = None
+            res["graph_error"] = str(exc)[:200]
+            torch.cuda.synchronize(dev)
     del sets
     torch.cuda.empty_cache()
     return x, res
 
 
+def graph_time(lib, w, sets, n_sets, dev, direction, chunk, path, steps):
+    """hipGraph replay of one call per buffer set (the pages' own kernel benchmark
+    used graph launch); microseconds per call."""
+    s = torch.cuda.Stream(device=dev)
+    sp = s.cuda_stream
+    with torch.cuda.stream(s):
+        for i in range(n_sets):
+            call(lib, w, sets[i], direction, chunk, path, sp)
+    torch.cuda.synchronize(dev)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        for i in range(n_sets):
+            call(lib, w, sets[i], direction, chunk, path, sp)
+    torch.cuda.synchronize(dev)
+    reps = max(1, steps // n_sets)
+    for _ in range(2):
+        gr.replay()
+    torch.cuda.synchronize(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        gr.replay()
+    t1.record()
+    torch.cuda.synchronize(dev)
+    out = t0.elapsed_time(t1) * 1e3 / (reps * n_sets)
+    del gr
+    return out
+
+
 # ----------------------------------------------------------- CPU baseline --
 def cpu_baseline(w: W.Workload, x: dict, target_s: float = 12.0):
-    """The fp64 oracle (test infrastructure, untuned) on a bounded sample of heads."""
+    """The fp64 oracle (test infrastructure, untuned) on a bounded sample of the
+    same workload: whole calls repeated for about target_s seconds, or, when one
+    call would take longer, the first (batch, head) sequences that fit."""
     import oracle
     oracle.build(force=False)
     f = {key: W.io_to_f64(x[key], w.dtype) for key in ("q", "k", "v", "z")}
     lg = x["log_g"].astype(np.float64)
     rw = x["rms_w"].astype(np.float64)
+    n_seq = w.B * w.H
     t0 = time.perf_counter()
     oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0, bh=[0])
-    t1 = time.perf_counter() - t0
-    n = int(min(w.B * w.H, max(1, target_s / max(t1, 1e-6))))
-    t0 = time.perf_counter()
-    oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0, bh=list(range(n)))
-    dt = time.perf_counter() - t0
-    tokens = n * w.L / w.H  # grid tokens with all heads counted once
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{n} of {w.B * w.H} (batch, head) sequences of {w.name} "
-                      f"({n * w.L} token-heads, LR scan), {dt:.1f} s",
-            "us_per_call_equiv": dt / n * w.B * w.H * 1e6}
+    t_one = time.perf_counter() - t0
+    if t_one * n_seq <= target_s:
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < target_s:
+            oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0)
+            reps += 1
+        dt = time.perf_counter() - t0
+        per_call = dt / reps
+        sample = f"{reps} whole calls of {w.name} (LR scan), {dt:.1f} s"
+    else:
+        n = max(1, int(target_s / t_one))
+        t0 = time.perf_counter()
+        oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0, bh=list(range(n)))
+        dt = time.perf_counter() - t0
+        per_call = dt / n * n_seq
+        sample = (f"{n} of {n_seq} (batch, head) sequences of {w.name} (LR scan), {dt:.1f} s, "
+                  f"scaled to the whole call")
+    return {"value": w.tokens / per_call, "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle", "sample": sample, "us_per_call": per_call * 1e6}
 
 
 # --------------------------------------------------------------- roofline --
@@ -313,7 +336,7 @@ def main():
         f"{w.dtype} chunk {chunk} path {pname}")
     x, res = time_workload(w, dev, hip, sp, args.steps, args.warmup, path, chunk)
     log(f"  {res['us_per_call']:.2f} us/call (rotating {res['n_sets']} sets), "
-        f"hot {res['us_per_call_hot']:.2f}, graph {res.get('us_per_call_graph', 0):.2f}, "
+        f"hot {res['us_per_call_hot']:.2f}, graph {res.get('us_per_call_graph')}, "
         f"launches {['%.2f' % t for t in res['launch_us_mean']]}")
 
     comp = w.compulsory_bytes()
@@ -346,13 +369,15 @@ def main():
                 extra[name] = {"error": str(exc)}
                 continue
             extra[name] = {"us_per_call": round(r["us_per_call"], 3),
-                           "us_per_call_graph": round(r["us_per_call_graph"], 3),
+                           "us_per_call_graph": (round(r["us_per_call_graph"], 3)
+                                                 if r["us_per_call_graph"] else None),
                            "us_per_call_hot": round(r["us_per_call_hot"], 3),
                            "tokens_per_s": round(we.tokens / (r["us_per_call"] * 1e-6)),
                            "hbm_frac": round(we.compulsory_bytes() / (r["us_per_call"] * 1e-6)
                                              / 1e9 / HBM_PEAK_GBS, 4),
                            "path": PATH_NAMES[pe]}
-            log(f"  {name}: {r['us_per_call']:.2f} us/call, graph {r['us_per_call_graph']:.2f}")
+            log(f"  {name}: {r['us_per_call']:.2f} us/call, graph {r['us_per_call_graph']}"
+                f"{' (' + r['graph_error'] + ')' if r.get('graph_error') else ''}")
     cpu = None
     if not args.no_cpu:
         log("  timing the fp64 oracle on the host (bounded sample)")
@@ -378,7 +403,8 @@ def main():
                    "path": pname, "global_batch": w.B, "seq_len": w.L, "parallelism": "none"},
         "us_per_call": round(us, 3),
         "us_per_call_hot": round(res["us_per_call_hot"], 3),
-        "us_per_call_graph": round(res["us_per_call_graph"], 3),
+        "us_per_call_graph": (round(res["us_per_call_graph"], 3)
+                              if res["us_per_call_graph"] else None),
         "us_per_call_p10_p50_p90": [round(res["us_per_call_evented_p10"], 3),
                                     round(res["us_per_call_evented_median"], 3),
                                     round(res["us_per_call_evented_p90"], 3)],

@@ -180,9 +180,32 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
     return GTR_OK;
 }
 
+// The single-launch path: batch one, at most kFastMaxTokens tokens, and a grid
+// that fits on the device at once.
+bool fast_ok(const GlaArgs &a) {
+    if (a.dtype == GTR_F32 || !mfma_supported(a)) return false;
+    if (a.B != 1 || a.L > kFastMaxTokens) return false;
+    return fast_chunks(a) <= fast_capacity(a);
+}
+
 int auto_path(const GlaArgs &a) {
+    if (fast_ok(a)) return GTR_PATH_FAST;
     const bool mfma_ok = a.dtype != GTR_F32 && mfma_supported(a);
     return mfma_ok ? GTR_PATH_MFMA : GTR_PATH_SERIAL;
+}
+
+gtr_status run_fast(const GlaArgs &a, hipStream_t st, Marks &mk) {
+    const size_t T = static_cast<size_t>(fast_chunks(a));
+    void *ws = nullptr;
+    gtr_status s = workspace(st, T * a.dk * a.dv * 4 + T * a.dk * 4, &ws);
+    if (s != GTR_OK) return s;
+    float *U = static_cast<float *>(ws);
+    float *G = U + T * a.dk * a.dv;
+    hipError_t e = mk.record(st, 0);
+    if (e == hipSuccess) e = fast_launch(a, U, G, st);
+    if (e == hipSuccess) e = mk.after_launch(st);
+    if (e != hipSuccess) return hip_fail(e, "single-launch kernel");
+    return GTR_OK;
 }
 
 gtr_status run(const GlaArgs &a0, int path, hipStream_t st, Marks &mk) {
@@ -198,10 +221,14 @@ gtr_status run(const GlaArgs &a0, int path, hipStream_t st, Marks &mk) {
                         "MFMA path needs 16-bit I/O, dk = 64, dv in {64, 128}, chunk in {32, 64}");
         return run_mfma(a, st, mk);
     case GTR_PATH_FAST:
-        return fail(GTR_ERR_UNSUPPORTED, "single-launch path not available for these arguments");
+        if (!fast_ok(a))
+            return fail(GTR_ERR_UNSUPPORTED,
+                        "single-launch path needs 16-bit I/O, dk = 64, dv in {64, 128}, chunk in "
+                        "{32, 64}, B = 1, at most %d tokens, and a grid that fits the device",
+                        kFastMaxTokens);
+        return run_fast(a, st, mk);
     default: return fail(GTR_ERR_ARG, "unknown path %d", path);
     }
-    (void)kFastMaxTokens;
 }
 
 int device_ok() {

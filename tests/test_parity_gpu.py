@@ -168,15 +168,64 @@ def test_mfma_mixed_spans(oracle_mod):
 
 @pytest.mark.parametrize("name", ["mixer_640", "mixer_640_wide"])
 def test_mixer_640_workloads(oracle_mod, name):
+    """The 1.6K-token workloads on the three-launch MFMA path, every direction."""
     w = W.WORKLOADS[name]
     x = W.make_inputs(w)
     for direction in range(4):
         _note(f"{name} direction {direction}")
-        got = _run(x, w.dtype, direction, chunk=w.chunk)
+        got = _run(x, w.dtype, direction, chunk=w.chunk, path=g.PATH_MFMA)
         ref = _oracle(oracle_mod, x, w.dtype, direction)
         rel, mx = assert_parity(got, ref, w.dtype, oracle_mod, f"{name} dir {direction}")
         urel, _ = errors(got, ref, "f32", oracle_mod)
         _note(f"  rel-L2 {rel:.2e} (unrounded {urel:.2e}) max-abs {mx:.2e}")
+
+
+FAST_SHAPES = [
+    (1, 17, 15, 2, 64, 64, "f16", 64),
+    (1, 17, 15, 2, 64, 64, "bf16", 32),
+    (1, 11, 13, 3, 64, 128, "bf16", 64),
+    (1, 9, 10, 2, 64, 128, "f16", 32),
+    (1, 1, 1, 2, 64, 64, "f16", 64),
+    (1, 1, 70, 1, 64, 64, "bf16", 64),
+    (1, 45, 45, 1, 64, 64, "f16", 64),
+]
+
+
+@pytest.mark.parametrize("shape", FAST_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fast_path_shapes(oracle_mod, shape):
+    _shape_case(oracle_mod, shape, g.PATH_FAST, 200 + FAST_SHAPES.index(shape))
+
+
+@pytest.mark.parametrize("name", ["mixer_640", "mixer_640_wide"])
+def test_fast_path_workloads(oracle_mod, name):
+    """The 1.6K-token workloads on the single-launch path, every direction."""
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w)
+    lib = _lib.load()
+    assert lib.gtr_gla_auto_path(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk,
+                                 W.DTYPE_CODE[w.dtype]) == g.PATH_FAST
+    for direction in range(4):
+        _note(f"{name} fast path direction {direction}")
+        got = _run(x, w.dtype, direction, chunk=w.chunk, path=g.PATH_FAST)
+        ref = _oracle(oracle_mod, x, w.dtype, direction)
+        rel, mx = assert_parity(got, ref, w.dtype, oracle_mod, f"{name} fast dir {direction}")
+        _note(f"  rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
+@pytest.mark.parametrize("log_g", [0.0, -0.5, -20.0])
+def test_fast_path_extreme_gates(oracle_mod, log_g):
+    x = W.make_custom(1, 16, 16, 2, 64, 64, "bf16", seed=6, log_g_const=log_g)
+    for direction in (1, 2):
+        _note(f"fast path constant log_g={log_g} direction={direction}")
+        got = _run(x, "bf16", direction, chunk=64, path=g.PATH_FAST)
+        ref = _oracle(oracle_mod, x, "bf16", direction)
+        assert_parity(got, ref, "bf16", oracle_mod, f"fast log_g {log_g}")
+
+
+def test_fast_path_rejects_batches(oracle_mod):
+    x = W.make_custom(2, 8, 8, 1, 64, 64, "f16", seed=9)
+    with pytest.raises(g.GtrError):
+        _run(x, "f16", 0, chunk=64, path=g.PATH_FAST)
 
 
 def test_mixer_640_serial_path_too(oracle_mod):
