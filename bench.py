@@ -301,6 +301,60 @@ def profile_run(w, dev, sp, steps, path, chunk):
         f"calibration copy {COPY_BYTES} bytes")
 
 
+KERNEL_KEYS = {  # launch name -> substring of the kernel symbol
+    "segment_summary": "true>", "chunk_output": "false>", "state_scan": "state_scan",
+    "fast_single_launch": "k_fast",
+}
+
+
+def _counter_values(csv_path):
+    """Per (kernel, counter) list of per-dispatch values from a rocprofv3
+    counter-collection CSV (FETCH_SIZE / WRITE_SIZE are in KiB)."""
+    import csv
+    vals = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(
+                float(r["Counter_Value"]))
+    return vals
+
+
+def _find(vals, counter, key, reduce):
+    hits = [v for (kn, c), v in vals.items() if c == counter and key in kn]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {key!r} for {counter}, found {len(hits)}")
+    return reduce(hits[0])
+
+
+def _mean(v):
+    return sum(v) / len(v)
+
+
+def ingest_counters(fetch_csv, write_csv, workload, path_name, kernel):
+    """Writes profiles/traffic_<path>_<workload>.json from two counter runs of
+    ``bench.py --profile-run`` (FETCH_SIZE, then WRITE_SIZE).  Each counter is
+    scaled by the ratio of the calibration copy's known bytes to what the same
+    counter read for it."""
+    fetch, write = _counter_values(fetch_csv), _counter_values(write_csv)
+    # the calibration copy is the largest copy dispatch (uploads of inputs are smaller)
+    copy_f = _find(fetch, "FETCH_SIZE", "copyBuffer", max) * 1024
+    copy_w = _find(write, "WRITE_SIZE", "copyBuffer", max) * 1024
+    f_scale, w_scale = COPY_BYTES / copy_f, COPY_BYTES / copy_w
+    kf = _find(fetch, "FETCH_SIZE", KERNEL_KEYS[kernel], _mean) * 1024 * f_scale
+    kw = _find(write, "WRITE_SIZE", KERNEL_KEYS[kernel], _mean) * 1024 * w_scale
+    rec = {"workload": workload, "path": path_name, "kernel": kernel,
+           "fetch_bytes_per_launch": round(kf), "write_bytes_per_launch": round(kw),
+           "bytes_per_launch": round(kf + kw),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "calibration_copy_bytes": COPY_BYTES, "sources_hash": kernel_sources_hash(),
+           "fetch_csv": os.path.relpath(fetch_csv, ROOT), "write_csv": os.path.relpath(write_csv, ROOT)}
+    out = os.path.join(ROOT, "profiles", f"traffic_{path_name}_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,7 +368,17 @@ def main():
     ap.add_argument("--profile-run", action="store_true",
                     help="for rocprofv3 counter passes: a plain 256 MiB device copy (the "
                          "calibration kernel), then --steps calls of the workload; no timing")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic record for --workload from two rocprofv3 counter "
+                         "CSVs of --profile-run (FETCH_SIZE, WRITE_SIZE); no GPU needed")
+    ap.add_argument("--kernel", default="chunk_output",
+                    help="launch whose traffic --ingest-counters records")
     args = ap.parse_args()
+    if args.ingest_counters:
+        wi = W.WORKLOADS[args.workload]
+        pn = PATH_NAMES[resolve_path(wi, args.path, args.chunk or wi.chunk)]
+        ingest_counters(*args.ingest_counters, args.workload, pn, args.kernel)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -361,23 +425,25 @@ def main():
     if not args.no_extra:
         for name in ("mixer_640", "mixer_640_wide"):
             we = W.WORKLOADS[name]
-            pe = resolve_path(we, args.path, we.chunk)
-            try:
-                _, r = time_workload(we, dev, hip, sp, args.steps, args.warmup, pe, we.chunk,
-                                     per_kernel=False)
-            except Exception as exc:  # report, do not hide
-                extra[name] = {"error": str(exc)}
-                continue
-            extra[name] = {"us_per_call": round(r["us_per_call"], 3),
-                           "us_per_call_graph": (round(r["us_per_call_graph"], 3)
-                                                 if r["us_per_call_graph"] else None),
-                           "us_per_call_hot": round(r["us_per_call_hot"], 3),
-                           "tokens_per_s": round(we.tokens / (r["us_per_call"] * 1e-6)),
-                           "hbm_frac": round(we.compulsory_bytes() / (r["us_per_call"] * 1e-6)
-                                             / 1e9 / HBM_PEAK_GBS, 4),
-                           "path": PATH_NAMES[pe]}
-            log(f"  {name}: {r['us_per_call']:.2f} us/call, graph {r['us_per_call_graph']}"
-                f"{' (' + r['graph_error'] + ')' if r.get('graph_error') else ''}")
+            pa = resolve_path(we, args.path, we.chunk)
+            for pe in dict.fromkeys([pa, g.PATH_FAST]):
+                key = name if pe == pa else f"{name}@{PATH_NAMES[pe]}"
+                try:
+                    _, r = time_workload(we, dev, hip, sp, args.steps, args.warmup, pe, we.chunk,
+                                         per_kernel=False)
+                except Exception as exc:  # report, do not hide
+                    extra[key] = {"error": str(exc)}
+                    continue
+                extra[key] = {"us_per_call": round(r["us_per_call"], 3),
+                              "us_per_call_graph": (round(r["us_per_call_graph"], 3)
+                                                    if r["us_per_call_graph"] else None),
+                              "us_per_call_hot": round(r["us_per_call_hot"], 3),
+                              "tokens_per_s": round(we.tokens / (r["us_per_call"] * 1e-6)),
+                              "hbm_frac": round(we.compulsory_bytes() / (r["us_per_call"] * 1e-6)
+                                                / 1e9 / HBM_PEAK_GBS, 4),
+                              "path": PATH_NAMES[pe]}
+                log(f"  {key}: {r['us_per_call']:.2f} us/call, graph {r['us_per_call_graph']}"
+                    f"{' (' + r['graph_error'] + ')' if r.get('graph_error') else ''}")
     cpu = None
     if not args.no_cpu:
         log("  timing the fp64 oracle on the host (bounded sample)")

@@ -73,6 +73,39 @@ gtr_status workspace(hipStream_t stream, size_t bytes, void **out) {
     return GTR_OK;
 }
 
+// Zero-initialised counters of the single-launch path, per (device, stream).
+// Every launch leaves them zero; growing synchronises the stream first.
+std::map<std::pair<int, hipStream_t>, Workspace> g_ctr;
+
+gtr_status counters(hipStream_t stream, size_t n, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Workspace &w = g_ctr[std::make_pair(dev, stream)];
+    const size_t bytes = n * sizeof(unsigned);
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            e = hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+        }
+        e = hipMalloc(&w.ptr, bytes);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return hip_fail(e, "hipMalloc(counters)");
+        }
+        e = hipMemset(w.ptr, 0, bytes);
+        if (e != hipSuccess) return hip_fail(e, "hipMemset(counters)");
+        w.bytes = bytes;
+    }
+    *out = w.ptr;
+    return GTR_OK;
+}
+
 // --------------------------------------------------------------- validation --
 bool head_width_ok(int d) { return d == 32 || d == 64 || d == 128; }
 
@@ -180,29 +213,31 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
     return GTR_OK;
 }
 
-// The single-launch path: batch one, at most kFastMaxTokens tokens, and a grid
-// that fits on the device at once.
+// The single-launch path: batch one, at most kFastMaxTokens tokens.
 bool fast_ok(const GlaArgs &a) {
-    if (a.dtype == GTR_F32 || !mfma_supported(a)) return false;
-    if (a.B != 1 || a.L > kFastMaxTokens) return false;
-    return fast_chunks(a) <= fast_capacity(a);
+    if (a.dtype == GTR_F32 || !fast_supported(a)) return false;
+    return a.B == 1 && a.L <= kFastMaxTokens;
 }
 
+// AUTO takes the matrix-core path for 16-bit I/O and the token-serial path
+// otherwise.  The single-launch path is taken only when asked for: on MI355X the
+// three-launch path is measured faster at 1.6K tokens too, because per-chunk
+// latency, not launch overhead, bounds both.
 int auto_path(const GlaArgs &a) {
-    if (fast_ok(a)) return GTR_PATH_FAST;
     const bool mfma_ok = a.dtype != GTR_F32 && mfma_supported(a);
     return mfma_ok ? GTR_PATH_MFMA : GTR_PATH_SERIAL;
 }
 
 gtr_status run_fast(const GlaArgs &a, hipStream_t st, Marks &mk) {
     const size_t T = static_cast<size_t>(fast_chunks(a));
-    void *ws = nullptr;
+    void *ws = nullptr, *ctr = nullptr;
     gtr_status s = workspace(st, T * a.dk * a.dv * 4 + T * a.dk * 4, &ws);
+    if (s == GTR_OK) s = counters(st, static_cast<size_t>(fast_counters(a)), &ctr);
     if (s != GTR_OK) return s;
     float *U = static_cast<float *>(ws);
     float *G = U + T * a.dk * a.dv;
     hipError_t e = mk.record(st, 0);
-    if (e == hipSuccess) e = fast_launch(a, U, G, st);
+    if (e == hipSuccess) e = fast_launch(a, U, G, static_cast<unsigned *>(ctr), st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "single-launch kernel");
     return GTR_OK;
@@ -224,7 +259,7 @@ gtr_status run(const GlaArgs &a0, int path, hipStream_t st, Marks &mk) {
         if (!fast_ok(a))
             return fail(GTR_ERR_UNSUPPORTED,
                         "single-launch path needs 16-bit I/O, dk = 64, dv in {64, 128}, chunk in "
-                        "{32, 64}, B = 1, at most %d tokens, and a grid that fits the device",
+                        "{32, 64}, B = 1 and at most %d tokens",
                         kFastMaxTokens);
         return run_fast(a, st, mk);
     default: return fail(GTR_ERR_ARG, "unknown path %d", path);
@@ -367,14 +402,16 @@ void gtr_release_workspace(void) {
     std::lock_guard<std::mutex> lock(g_ws_mu);
     int cur = 0;
     const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-    for (auto &kv : g_ws) {
-        if (!kv.second.ptr) continue;
-        if (hipSetDevice(kv.first.first) == hipSuccess) {
-            (void)hipDeviceSynchronize();
-            (void)hipFree(kv.second.ptr);
+    for (auto *m : {&g_ws, &g_ctr}) {
+        for (auto &kv : *m) {
+            if (!kv.second.ptr) continue;
+            if (hipSetDevice(kv.first.first) == hipSuccess) {
+                (void)hipDeviceSynchronize();
+                (void)hipFree(kv.second.ptr);
+            }
         }
+        m->clear();
     }
-    g_ws.clear();
     if (have_cur) (void)hipSetDevice(cur);
 }
 

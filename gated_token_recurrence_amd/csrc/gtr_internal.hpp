@@ -128,10 +128,13 @@ bool mfma_supported(const GlaArgs &a);
 MfmaPlan mfma_plan(const GlaArgs &a, int64_t chunks_per_wg);  // <= 0: automatic
 hipError_t mfma_summary(const GlaArgs &a, const MfmaPlan &pl, float *U, float *G, hipStream_t s);
 hipError_t mfma_output(const GlaArgs &a, const MfmaPlan &pl, const float *Sx, hipStream_t s);
-// Single-launch path (cooperative launch, one workgroup per chunk).
+// Single-launch path (one workgroup per chunk, chunks handed out by ticket).
 int64_t fast_chunks(const GlaArgs &a);    // workgroups the launch needs
-int64_t fast_capacity(const GlaArgs &a);  // workgroups that fit at once (0: unavailable)
-hipError_t fast_launch(const GlaArgs &a, float *U, float *G, hipStream_t s);
+int64_t fast_counters(const GlaArgs &a);  // 32-bit counters the launch needs
+bool fast_supported(const GlaArgs &a);    // shape has a kernel and <= 64 chunks per sequence
+// U: [chunks][dk][dv] fp32; G: [chunks][dk]; cnt: fast_counters() words, zero before
+// the first launch (each launch leaves them zero).
+hipError_t fast_launch(const GlaArgs &a, float *U, float *G, unsigned *cnt, hipStream_t s);
 // State scan over the segments of a plan, in place: U[k] <- state before segment k.
 hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,
                            int dv, hipStream_t s);

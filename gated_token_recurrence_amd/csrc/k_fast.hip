@@ -4,37 +4,52 @@
 // "硬件感知分块推理算子": chunk summaries, a light boundary-state scan and
 // per-chunk outputs.  The page benchmarks its operator with graph launch at
 // about 1.6K tokens, where launch overhead is a large share of the time; this
-// kernel runs all three phases in one cooperative launch, one workgroup per
-// chunk, with two grid-wide barriers between them:
-//   1. every workgroup stages its chunk (operands stay in LDS), computes the
-//      chunk summary U_n = sum_t (k_t 2^(G - a_t)) v_t^T from a zero state and
-//      writes U_n and the chunk's summed log2-gate G_n;
-//   2. the summaries are scanned over the chunks of each sequence, spread over
-//      all threads of the grid: U_n <- S before chunk n;
-//   3. every workgroup reads its incoming state and produces its outputs from
-//      the operands still in LDS.
-// The launch needs every workgroup resident at once; the host only takes this
-// path when the grid fits.
-#include <hip/hip_cooperative_groups.h>
-
+// kernel runs the phases in one launch, one workgroup per chunk:
+//   1. a workgroup takes the next chunk from a ticket counter, stages it
+//      (operands stay in LDS), computes the chunk summary
+//      U_n = sum_t (k_t 2^(G - a_t)) v_t^T from a zero state, writes U_n and the
+//      chunk's decay 2^(G_n) per key channel, and raises the chunk's ready flag;
+//   2. it waits for the ready flags of the chunks before it in its sequence and
+//      builds its incoming state S_n = sum_{m < n} Diag(2^(G_{m+1} + ... +
+//      G_{n-1})) U_m directly in the registers that hold the state;
+//   3. it produces its outputs from that state and the operands still in LDS.
+// Chunks are handed out in ticket order, so a workgroup only waits for
+// workgroups that took their tickets earlier and are running; those wait only
+// for earlier ones in turn, so every wait ends whatever the grid size and
+// whatever else runs on the device (the waits are also bounded).  The last
+// workgroup of a sequence to finish clears that sequence's flags, and the last
+// workgroup of the launch clears the ticket counters, so the next launch (or
+// graph replay) starts from zero.
 #include "mfma_common.hpp"
 
 namespace gtr {
 namespace {
 
 using namespace mf;
-namespace cg = cooperative_groups;
 
+constexpr unsigned kSpinLimit = 1u << 24;  // bounded wait (far beyond any real wait)
+
+// Counter block: [0] ticket, [1] finished workgroups, then per sequence one
+// finished-workgroup count, then one ready flag per chunk.
 template <int DT, int DV, int NB>
 __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float *__restrict__ U,
                                                                  float *__restrict__ Gs,
-                                                                 int64_t N) {
+                                                                 unsigned *__restrict__ cnt,
+                                                                 int N) {
     using T = Tile<DT, DV, NB, false>;
     __shared__ __attribute__((aligned(16))) char smem[T::K::BYTES];
     T t;
     t.init(a, smem);
-    const int64_t p = blockIdx.x;  // this workgroup's chunk
-    const int64_t bh = p / N, ch = p - bh * N;
+    const int n_seq = a.B * a.H, T_all = n_seq * N;
+    unsigned *ticket = cnt, *finished = cnt + 1, *seq_done = cnt + 2, *ready = cnt + 2 + n_seq;
+    // the ticket is passed through the first LDS word (Q~ tile, first written in phase 2)
+    int *s_ticket = reinterpret_cast<int *>(smem);
+    if (t.tid == 0)
+        *s_ticket = static_cast<int>(
+            __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    const int p = *s_ticket;  // this workgroup's chunk
+    const int bh = p / N, ch = p - bh * N;
     constexpr int64_t dd = static_cast<int64_t>(DK) * DV;
 
     // ---- 1. stage the chunk; its summary from a zero state
@@ -48,50 +63,56 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
     const bool slow = t.phase2(&gam);
     __syncthreads();
     t.zero_state();
-    if (!slow)
-        t.s_update();
-    else
-        t.serial();  // token by token from zero: the final state is the summary
-    t.store_state(U + p * dd);
-    if (t.w == 0) Gs[p * DK + t.l] = gam;
+    if (ch + 1 < N) {  // the last chunk's summary is never read
+        if (!slow)
+            t.s_update();
+        else
+            t.serial();  // token by token from zero: the final state is the summary
+        t.store_state(U + p * dd);
+        if (t.w == 0) Gs[static_cast<int64_t>(p) * DK + t.l] = fexp2(gam);
+        __syncthreads();  // every thread's summary stores are issued
+        if (t.tid == 0) {
+            // agent-scope release: this XCD's L2 is written back once, then the flag
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_store(ready + p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    t.zero_state();
 
-    cg::this_grid().sync();
-
-    // ---- 2. exclusive scan of the summaries over each sequence's chunks
-    {
-        const int64_t n_seq = static_cast<int64_t>(gridDim.x) / N;
-        const int64_t total = n_seq * dd;
-        const int64_t stride = static_cast<int64_t>(gridDim.x) * NT;
-        for (int64_t e = p * NT + t.tid; e < total; e += stride) {
-            const int64_t seq = e / dd, el = e - seq * dd;
-            const int c = static_cast<int>(el / DV);
-            float *u = U + seq * N * dd + el;
-            const float *gp = Gs + seq * N * DK + c;
-            float s = 0.f;
-            constexpr int SB = 16;
-            for (int64_t n0 = 0; n0 < N; n0 += SB) {
-                float x[SB], gg[SB];
-#pragma unroll
-                for (int i = 0; i < SB; ++i) {
-                    const int64_t n = (n0 + i < N) ? n0 + i : N - 1;
-                    x[i] = u[n * dd];
-                    gg[i] = gp[n * DK];
-                }
-#pragma unroll
-                for (int i = 0; i < SB; ++i) {
-                    if (n0 + i < N) {
-                        u[(n0 + i) * dd] = s;
-                        s = fexp2(gg[i]) * s + x[i];
-                    }
-                }
+    // ---- 2. wait for the chunks before this one (lane m of wave 0 polls chunk m's
+    // flag with cache-bypassing loads), then one acquire for the workgroup
+    if (ch > 0) {
+        if (t.w == 0) {
+            const unsigned *fl = ready + static_cast<int64_t>(bh) * N;
+            unsigned spins = 0;
+            bool mine = t.l >= ch;  // lanes past the predecessors are done
+            while (true) {
+                if (!mine)
+                    mine = __hip_atomic_load(fl + t.l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+                if (__builtin_amdgcn_read_exec() == __ballot(mine) || ++spins >= kSpinLimit) break;
+                __builtin_amdgcn_s_sleep(2);
             }
+            if (t.l == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        __syncthreads();
+
+        // S <- Diag(2^G_m) S + U_m over the chunks m before this one, in order
+        const float *ub = U + static_cast<int64_t>(bh) * N * dd, *eb = Gs + static_cast<int64_t>(bh) * N * DK;
+        constexpr int MB = DV == 64 ? 4 : 2;  // chunks whose loads are in flight together
+        for (int m0 = 0; m0 < ch; m0 += MB) {
+            typename T::StateIn in[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int m = (m0 + i < ch) ? m0 + i : ch - 1;  // clamped, then skipped
+                t.state_in_load(in[i], ub + m * dd, eb + static_cast<int64_t>(m) * DK);
+            }
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                if (m0 + i < ch) t.state_in_apply(in[i]);
         }
     }
 
-    cg::this_grid().sync();
-
     // ---- 3. outputs from the incoming state and the staged operands
-    t.load_state(U + p * dd);
     if (!slow) {
         t.inter();
         t.scores();
@@ -104,6 +125,23 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
     t.sum_squares();
     __syncthreads();
     t.epilogue();
+
+    // ---- counters back to zero: a sequence's flags once all its chunks have
+    // passed their waits, the tickets once every workgroup has finished
+    if (t.tid == 0) {
+        if (__hip_atomic_fetch_add(seq_done + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            static_cast<unsigned>(N) - 1) {
+            for (int m = 0; m < N; ++m)
+                __hip_atomic_store(ready + static_cast<int64_t>(bh) * N + m, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(seq_done + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (__hip_atomic_fetch_add(finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            static_cast<unsigned>(T_all) - 1) {
+            __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 template <int DT, int DV, int NB>
@@ -127,30 +165,23 @@ int64_t fast_chunks(const GlaArgs &a) {
     return static_cast<int64_t>(a.B) * a.H * N;
 }
 
-// Workgroups of this variant that can be resident at once on the current
-// device (0 if cooperative launch is unavailable).
-int64_t fast_capacity(const GlaArgs &a) {
-    if (!mfma_supported(a)) return 0;
-    const void *k = pick(a);
-    if (!k) return 0;
-    int dev = 0, coop = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop)
-        return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, NT, 0) != hipSuccess) return 0;
-    return static_cast<int64_t>(cus) * per_cu;
+int64_t fast_counters(const GlaArgs &a) {
+    return 2 + static_cast<int64_t>(a.B) * a.H + fast_chunks(a);
 }
 
-hipError_t fast_launch(const GlaArgs &a, float *U, float *G, hipStream_t s) {
+bool fast_supported(const GlaArgs &a) {
+    return mfma_supported(a) && pick(a) != nullptr && (a.L + a.chunk - 1) / a.chunk <= 64;
+}
+
+hipError_t fast_launch(const GlaArgs &a, float *U, float *G, unsigned *cnt, hipStream_t s) {
     const void *k = pick(a);
-    if (!k) return hipErrorInvalidValue;
-    GlaArgs args = a;
-    int64_t N = (a.L + a.chunk - 1) / a.chunk;
-    void *params[] = {&args, &U, &G, &N};
-    return hipLaunchCooperativeKernel(k, dim3(static_cast<unsigned>(fast_chunks(a))), dim3(NT),
-                                      params, 0, s);
+    const int64_t N = (a.L + a.chunk - 1) / a.chunk;
+    if (!k || N > 64) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(reinterpret_cast<void (*)(GlaArgs, float *, float *, unsigned *, int)>(
+                           const_cast<void *>(k)),
+                       dim3(static_cast<unsigned>(fast_chunks(a))), dim3(NT), 0, s, a, U, G, cnt,
+                       static_cast<int>(N));
+    return hipGetLastError();
 }
 
 }  // namespace gtr

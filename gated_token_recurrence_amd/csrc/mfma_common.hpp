@@ -284,6 +284,36 @@ struct Tile {
                     dst[(16 * ct + 4 * g + r) * DV + 16 * (w * DPW + dd) + lr] = S[dd][ct][r];
     }
 
+    // One step of a scan over chunk summaries, in the state's register layout:
+    // S <- Diag(e) S + u, with u a [DK][DV] summary and e the per-channel decay.
+    struct StateIn {
+        f32x4 e[4];
+        float u[DPW][4][4];
+    };
+    __device__ __forceinline__ void state_in_load(StateIn &x, const float *u, const float *e) const {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const float4 d = *reinterpret_cast<const float4 *>(e + 16 * ct + 4 * g);
+            x.e[ct] = f32x4{d.x, d.y, d.z, d.w};
+        }
+#pragma unroll
+        for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x.u[dd][ct][r] = u[(16 * ct + 4 * g + r) * DV + 16 * (w * DPW + dd) + lr];
+    }
+    __device__ __forceinline__ void state_in_apply(const StateIn &x) {
+#pragma unroll
+        for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[dd][ct][r] = fmaf(S[dd][ct][r], x.e[ct][r], x.u[dd][ct][r]);
+    }
+
     // ---- phase 1: cumulative gates within the sub-block (registers), block totals,
     // V^T into LDS.  Consumes the prefetched inputs except q and k.
     __device__ __forceinline__ void phase1() {

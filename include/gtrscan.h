@@ -66,13 +66,14 @@ typedef enum { GTR_F32 = 0, GTR_F16 = 1, GTR_BF16 = 2 } gtr_dtype;
 
 typedef enum { GTR_LR = 0, GTR_RL = 1, GTR_TB = 2, GTR_BT = 3 } gtr_direction;
 
-/* Kernel path.  AUTO picks: the single-launch path for B == 1 and L <= 2048
- * (16-bit I/O), the MFMA chunk path for other 16-bit I/O, and the fp32
- * token-serial chunk path for float32 I/O or dk/dv it does not cover. */
+/* Kernel path.  AUTO picks the MFMA chunk path for 16-bit I/O with dk = 64,
+ * dv in {64, 128}, chunk in {32, 64}, and the fp32 token-serial chunk path
+ * otherwise (float32 I/O, other dk/dv or chunk).  The single-launch path runs
+ * only when asked for. */
 typedef enum {
     GTR_PATH_AUTO = 0,
     GTR_PATH_MFMA = 1,    /* three launches: segment summaries, state scan, chunk outputs */
-    GTR_PATH_FAST = 2,    /* one launch; B == 1, L <= 2048, 16-bit I/O */
+    GTR_PATH_FAST = 2,    /* one launch; B == 1, L <= 2048, 16-bit I/O, MFMA shapes */
     GTR_PATH_SERIAL = 3   /* fp32 arithmetic, token-serial inside each chunk */
 } gtr_path;
 
