@@ -189,9 +189,10 @@ gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk) {
 }
 
 gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
-    const MfmaPlan pl = mfma_plan(a, g_chunks_per_wg);
+    MfmaPlan pl, po;
+    mfma_plans(a, g_chunks_per_wg, &pl, &po);
     const int64_t n_seq = static_cast<int64_t>(a.B) * a.H;
-    if (pl.n_wg > 0x7fffffff || n_seq * a.dk * a.dv / 256 > 0x7fffffff)
+    if (pl.n_wg > 0x7fffffff || n_seq * a.dk * a.dv > 0x7fffffff)
         return fail(GTR_ERR_UNSUPPORTED, "too many chunks");
     const size_t ubytes = static_cast<size_t>(pl.n_seg) * a.dk * a.dv * 4;
     const size_t gbytes = static_cast<size_t>(pl.n_seg) * a.dk * 4;
@@ -207,7 +208,7 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
     e = state_scan_plan(U, G, pl, static_cast<int>(n_seq), a.dk, a.dv, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "state scan launch");
-    e = mfma_output(a, pl, U, st);
+    e = mfma_output(a, po, pl, U, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "chunk output launch");
     return GTR_OK;

@@ -118,16 +118,23 @@ struct MfmaPlan {
     int64_t lcm;    // lcm(N, Q)
     int64_t n_seg;  // segments
 };
-constexpr int64_t kMfmaWorkgroups = 512;  // two per CU on 256 CUs
+constexpr int64_t kMfmaWorkgroups = 512;      // output kernel: two per CU on 256 CUs
+constexpr int64_t kSummaryWorkgroups = 1024;  // summary kernel: four per CU
 
 __host__ __device__ __forceinline__ int64_t seg_id(int64_t p, const MfmaPlan &pl) {
     return (p + pl.N - 1) / pl.N + (p + pl.Q - 1) / pl.Q - (p + pl.lcm - 1) / pl.lcm;
 }
 
 bool mfma_supported(const GlaArgs &a);
-MfmaPlan mfma_plan(const GlaArgs &a, int64_t chunks_per_wg);  // <= 0: automatic
-hipError_t mfma_summary(const GlaArgs &a, const MfmaPlan &pl, float *U, float *G, hipStream_t s);
-hipError_t mfma_output(const GlaArgs &a, const MfmaPlan &pl, const float *Sx, hipStream_t s);
+MfmaPlan mfma_plan(const GlaArgs &a, int64_t chunks_per_wg);
+// Plans of the summary kernel (ps: its ranges are the scan's segments) and of the
+// output kernel (po: ranges of a whole number of ps ranges, so every po segment
+// starts where a ps segment does).  chunks_per_wg > 0 forces both to that size.
+void mfma_plans(const GlaArgs &a, int64_t chunks_per_wg, MfmaPlan *ps, MfmaPlan *po);
+hipError_t mfma_summary(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t s);
+// Sx: incoming state of every ps segment
+hipError_t mfma_output(const GlaArgs &a, const MfmaPlan &po, const MfmaPlan &ps, const float *Sx,
+                       hipStream_t s);
 // Single-launch path (one workgroup per chunk, chunks handed out by ticket).
 int64_t fast_chunks(const GlaArgs &a);    // workgroups the launch needs
 int64_t fast_counters(const GlaArgs &a);  // 32-bit counters the launch needs

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
         __syncthreads();
         t.serial();
     }
-    t.sum_squares();
+    t.out_stage();
     __syncthreads();
     t.epilogue();
 

@@ -35,10 +35,9 @@ namespace {
 using namespace mf;
 
 template <int DT, int DV, int NB, bool SUM>
-__global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, float *__restrict__ U,
-                                                                  float *__restrict__ Gs,
-                                                                  const float *__restrict__ Sx,
-                                                                  MfmaPlan pl) {
+__global__ __launch_bounds__(NT, SUM ? (DV == 128 ? 2 : 4) : (DV == 128 ? 1 : 2)) void k_chunk(
+    GlaArgs a, float *__restrict__ U, float *__restrict__ Gs, const float *__restrict__ Sx,
+    MfmaPlan pl, MfmaPlan ps) {
     using T = Tile<DT, DV, NB, SUM>;
     __shared__ __attribute__((aligned(16))) char smem[T::K::BYTES];
     T t;
@@ -62,7 +61,7 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
             if (SUM)
                 t.zero_state();
             else
-                t.load_state(Sx + seg_id(p, pl) * DK * DV);
+                t.load_state(Sx + seg_id(p, ps) * DK * DV);
             gam = 0.f;
         }
         t.phase1();
@@ -91,8 +90,8 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
                 __syncthreads();  // pairs with B3
                 t.serial();
             }
-            t.sum_squares();
-            __syncthreads();  // B4: sums of squares
+            t.out_stage();
+            __syncthreads();  // B4: output tile
             t.epilogue();
             if (p + 1 < p1) t.prefetch_z(cur ^ 1);
         }
@@ -107,30 +106,30 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_chunk(GlaArgs a, floa
 
 template <bool SUM, int DT, int DV, int NB>
 hipError_t launch_t(const GlaArgs &a, float *U, float *G, const float *Sx, const MfmaPlan &pl,
-                    hipStream_t st) {
+                    const MfmaPlan &ps, hipStream_t st) {
     hipLaunchKernelGGL((k_chunk<DT, DV, NB, SUM>), dim3(static_cast<unsigned>(pl.n_wg)), dim3(NT),
-                       0, st, a, U, G, Sx, pl);
+                       0, st, a, U, G, Sx, pl, ps);
     return hipGetLastError();
 }
 
 template <bool SUM, int DT>
 hipError_t launch_dt(const GlaArgs &a, float *U, float *G, const float *Sx, const MfmaPlan &pl,
-                     hipStream_t st) {
+                     const MfmaPlan &ps, hipStream_t st) {
     if (a.dv == 64) {
-        if (a.chunk == 32) return launch_t<SUM, DT, 64, 2>(a, U, G, Sx, pl, st);
-        if (a.chunk == 64) return launch_t<SUM, DT, 64, 4>(a, U, G, Sx, pl, st);
+        if (a.chunk == 32) return launch_t<SUM, DT, 64, 2>(a, U, G, Sx, pl, ps, st);
+        if (a.chunk == 64) return launch_t<SUM, DT, 64, 4>(a, U, G, Sx, pl, ps, st);
     } else if (a.dv == 128) {
-        if (a.chunk == 32) return launch_t<SUM, DT, 128, 2>(a, U, G, Sx, pl, st);
-        if (a.chunk == 64) return launch_t<SUM, DT, 128, 4>(a, U, G, Sx, pl, st);
+        if (a.chunk == 32) return launch_t<SUM, DT, 128, 2>(a, U, G, Sx, pl, ps, st);
+        if (a.chunk == 64) return launch_t<SUM, DT, 128, 4>(a, U, G, Sx, pl, ps, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <bool SUM>
 hipError_t launch(const GlaArgs &a, float *U, float *G, const float *Sx, const MfmaPlan &pl,
-                  hipStream_t st) {
-    if (a.dtype == DT_F16) return launch_dt<SUM, DT_F16>(a, U, G, Sx, pl, st);
-    if (a.dtype == DT_BF16) return launch_dt<SUM, DT_BF16>(a, U, G, Sx, pl, st);
+                  const MfmaPlan &ps, hipStream_t st) {
+    if (a.dtype == DT_F16) return launch_dt<SUM, DT_F16>(a, U, G, Sx, pl, ps, st);
+    if (a.dtype == DT_BF16) return launch_dt<SUM, DT_BF16>(a, U, G, Sx, pl, ps, st);
     return hipErrorInvalidValue;
 }
 
@@ -154,10 +153,6 @@ MfmaPlan mfma_plan(const GlaArgs &a, int64_t chunks_per_wg) {
     MfmaPlan pl;
     pl.N = (a.L + a.chunk - 1) / a.chunk;
     pl.T = static_cast<int64_t>(a.B) * a.H * pl.N;
-    if (chunks_per_wg <= 0) {
-        const int64_t target = kMfmaWorkgroups < pl.T ? kMfmaWorkgroups : pl.T;
-        chunks_per_wg = (pl.T + target - 1) / target;
-    }
     pl.Q = chunks_per_wg;
     pl.n_wg = (pl.T + pl.Q - 1) / pl.Q;
     pl.lcm = pl.N / gcd64(pl.N, pl.Q) * pl.Q;
@@ -165,13 +160,30 @@ MfmaPlan mfma_plan(const GlaArgs &a, int64_t chunks_per_wg) {
     return pl;
 }
 
-hipError_t mfma_summary(const GlaArgs &a, const MfmaPlan &pl, float *U, float *G,
-                        hipStream_t s) {
-    return launch<true>(a, U, G, nullptr, pl, s);
+void mfma_plans(const GlaArgs &a, int64_t chunks_per_wg, MfmaPlan *ps, MfmaPlan *po) {
+    const int64_t N = (a.L + a.chunk - 1) / a.chunk;
+    const int64_t T = static_cast<int64_t>(a.B) * a.H * N;
+    int64_t q1 = chunks_per_wg, q2 = chunks_per_wg;
+    if (chunks_per_wg <= 0) {
+        const int64_t t1 = kSummaryWorkgroups < T ? kSummaryWorkgroups : T;
+        q1 = (T + t1 - 1) / t1;
+        const int64_t t2 = kMfmaWorkgroups < T ? kMfmaWorkgroups : T;
+        const int64_t want = (T + t2 - 1) / t2;
+        const int64_t m = (want + q1 / 2) / q1;
+        q2 = q1 * (m > 1 ? m : 1);
+    }
+    *ps = mfma_plan(a, q1);
+    *po = mfma_plan(a, q2);
 }
 
-hipError_t mfma_output(const GlaArgs &a, const MfmaPlan &pl, const float *Sx, hipStream_t s) {
-    return launch<false>(a, nullptr, nullptr, Sx, pl, s);
+hipError_t mfma_summary(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G,
+                        hipStream_t s) {
+    return launch<true>(a, U, G, nullptr, ps, ps, s);
+}
+
+hipError_t mfma_output(const GlaArgs &a, const MfmaPlan &po, const MfmaPlan &ps, const float *Sx,
+                       hipStream_t s) {
+    return launch<false>(a, nullptr, nullptr, Sx, po, ps, s);
 }
 
 }  // namespace gtr

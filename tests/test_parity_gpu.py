@@ -111,6 +111,18 @@ def test_mfma_workgroup_ranges(oracle_mod, segment_chunks, sc):
         assert_parity(got, ref, "f16", oracle_mod, f"segments of {sc}")
 
 
+@pytest.mark.parametrize("chunk,sc", [(64, 1), (32, 1), (64, 3), (32, 5)])
+def test_mfma_long_segment_chains(oracle_mod, segment_chunks, chunk, sc):
+    """One long sequence cut into many segments: 257 and 513 segments (the
+    boundary-state scan's wider part split and its plain chain), 86 and 103."""
+    x = W.make_custom(1, 128, 128, 1, 64, 64, "f16", seed=23)
+    segment_chunks(sc)
+    _note(f"16384 tokens, chunk {chunk}, {sc} chunks per workgroup")
+    got = _run(x, "f16", 2, chunk=chunk, path=g.PATH_MFMA)
+    ref = _oracle(oracle_mod, x, "f16", 2)
+    assert_parity(got, ref, "f16", oracle_mod, f"long chain chunk {chunk} sc {sc}")
+
+
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128])
 def test_chunk_sizes_agree(oracle_mod, chunk):
     x = W.make_custom(1, 20, 20, 2, 64, 64, "f32", seed=7)
