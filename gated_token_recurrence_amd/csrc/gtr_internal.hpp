@@ -119,7 +119,7 @@ struct MfmaPlan {
     int64_t n_seg;  // segments
 };
 constexpr int64_t kMfmaWorkgroups = 512;      // output kernel: two per CU on 256 CUs
-constexpr int64_t kSummaryWorkgroups = 1024;  // summary kernel: four per CU
+constexpr int64_t kSummaryWorkgroups = 512;   // summary kernel (finer ranges only lengthen the scan)
 
 __host__ __device__ __forceinline__ int64_t seg_id(int64_t p, const MfmaPlan &pl) {
     return (p + pl.N - 1) / pl.N + (p + pl.Q - 1) / pl.Q - (p + pl.lcm - 1) / pl.lcm;

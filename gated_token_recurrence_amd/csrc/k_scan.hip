@@ -106,34 +106,38 @@ __global__ __launch_bounds__(NT) void k_state_scan_plan(float *__restrict__ U,
     }
 }
 
-// The same recurrence with each element's chain of segments cut into P parts
-// of at most M segments, so that memory latency is paid about once: a part
-// loads all its segments at once and folds them into its own (decay product,
-// partial state); the parts' folds are combined through LDS; each part then
-// writes its exclusive prefixes.  Workgroup: NT / P consecutive state elements
-// of one sequence x P parts.
-template <int P, int M>
-__global__ __launch_bounds__(NT) void k_scan_parts(float *__restrict__ U,
-                                                   const float *__restrict__ G, MfmaPlan pl,
-                                                   int dk, int dv) {
-    constexpr int EPW = NT / P;
-    __shared__ float sA[P][EPW], sB[P][EPW];
+// The same recurrence with each element's chain of segments cut into 4 parts,
+// one per wave, so that memory latency is paid about once: a wave loads all the
+// segments of its part at once (64 consecutive state elements of one key
+// channel: one 256-byte row per segment, and the decay as a wave-uniform value)
+// and folds them into its own (decay product, partial state); the parts' folds
+// are combined through LDS; each wave then writes its exclusive prefixes.
+// Workgroup: (sequence, 64-element slice of the state).
+template <int M>
+__global__ __launch_bounds__(NT) void k_scan_rows(float *__restrict__ U,
+                                                  const float *__restrict__ G, MfmaPlan pl,
+                                                  int dk, int dv) {
+    __shared__ float sA[4][64], sB[4][64];
     const int64_t dd = static_cast<int64_t>(dk) * dv;
-    const int part = threadIdx.x / EPW, le = threadIdx.x % EPW;
-    const int64_t ge = static_cast<int64_t>(blockIdx.x) * EPW + le;  // dd % EPW == 0
-    const int64_t seq = ge / dd, el = ge - seq * dd;
-    const int c = static_cast<int>(el / dv);
+    const int64_t slices = dd / 64;
+    const int64_t seq = blockIdx.x / slices;
+    const int lane = threadIdx.x & 63;
+    const int part = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t el0 = (blockIdx.x - seq * slices) * 64;
+    const int64_t el = el0 + lane;
+    const int c = static_cast<int>(el0 / dv);  // the slice's key channel
     const int64_t s0 = seg_id(seq * pl.N, pl), s1 = seg_id((seq + 1) * pl.N, pl);
-    const int64_t len = (s1 - s0 + P - 1) / P;  // <= M (checked by the host)
+    const int64_t len = (s1 - s0 + 3) / 4;  // <= M (checked by the host)
     const int64_t kb = s0 + part * len;
-    const int64_t ke = (kb + len < s1) ? kb + len : s1;
+    const int n = static_cast<int>(kb < s1 ? (kb + len < s1 ? len : s1 - kb) : 0);
     float x[M], e[M];
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-        const int64_t k = kb + i;
-        const bool ok = k < ke;
-        x[i] = ok ? U[k * dd + el] : 0.f;
-        e[i] = ok ? __builtin_amdgcn_exp2f(G[k * dk + c]) : 1.f;
+        const int64_t k = (i < n) ? kb + i : s1 - 1;  // in bounds; unused past n
+        const float xv = U[k * dd + el];
+        const float gv = G[k * dk + c];
+        x[i] = (i < n) ? xv : 0.f;
+        e[i] = (i < n) ? __builtin_amdgcn_exp2f(gv) : 1.f;
     }
     float A = 1.f, B = 0.f;
 #pragma unroll
@@ -141,16 +145,15 @@ __global__ __launch_bounds__(NT) void k_scan_parts(float *__restrict__ U,
         B = e[i] * B + x[i];
         A *= e[i];
     }
-    sA[part][le] = A;
-    sB[part][le] = B;
+    sA[part][lane] = A;
+    sB[part][lane] = B;
     __syncthreads();
     float s = 0.f;  // state before this part's first segment
-    for (int q = 0; q < part; ++q) s = sA[q][le] * s + sB[q][le];
+    for (int q = 0; q < part; ++q) s = sA[q][lane] * s + sB[q][lane];
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-        const int64_t k = kb + i;
-        if (k < ke) {
-            U[k * dd + el] = s;
+        if (i < n) {
+            U[(kb + i) * dd + el] = s;
             s = e[i] * s + x[i];
         }
     }
@@ -164,12 +167,11 @@ hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_s
     if (dd % NT != 0 || dv < 64) return hipErrorInvalidValue;
     const int64_t n_el = static_cast<int64_t>(n_seq) * dd;
     const int64_t most = (pl.N + pl.Q - 1) / pl.Q + 1;  // segments of one sequence, at most
-    if (most <= 8 * 16) {
-        hipLaunchKernelGGL((k_scan_parts<8, 16>), dim3(static_cast<unsigned>(n_el / (NT / 8))),
-                           dim3(NT), 0, s, U, G, pl, dk, dv);
-    } else if (most <= 32 * 16) {
-        hipLaunchKernelGGL((k_scan_parts<32, 16>), dim3(static_cast<unsigned>(n_el / (NT / 32))),
-                           dim3(NT), 0, s, U, G, pl, dk, dv);
+    const dim3 rows_grid(static_cast<unsigned>(n_el / 64));
+    if (most <= 4 * 16) {
+        hipLaunchKernelGGL((k_scan_rows<16>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);
+    } else if (most <= 4 * 32) {
+        hipLaunchKernelGGL((k_scan_rows<32>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);
     } else {
         hipLaunchKernelGGL(k_state_scan_plan, dim3(static_cast<unsigned>(n_el / NT)), dim3(NT), 0,
                            s, U, G, pl, dk, dv);

@@ -114,7 +114,7 @@ def test_mfma_workgroup_ranges(oracle_mod, segment_chunks, sc):
 @pytest.mark.parametrize("chunk,sc", [(64, 1), (32, 1), (64, 3), (32, 5)])
 def test_mfma_long_segment_chains(oracle_mod, segment_chunks, chunk, sc):
     """One long sequence cut into many segments: 257 and 513 segments (the
-    boundary-state scan's wider part split and its plain chain), 86 and 103."""
+    boundary-state scan's plain chain) and 87 and 104 (its four-part split)."""
     x = W.make_custom(1, 128, 128, 1, 64, 64, "f16", seed=23)
     segment_chunks(sc)
     _note(f"16384 tokens, chunk {chunk}, {sc} chunks per workgroup")
