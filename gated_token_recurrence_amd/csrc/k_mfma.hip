@@ -26,7 +26,8 @@
 //
 // The per-chunk steps (operand staging, matrix products, token-serial fallback,
 // epilogue) live in mfma_common.hpp.  The next chunk's inputs are loaded into
-// registers while the current one is computed.
+// registers while the current one is computed: log_g and v as soon as phase 1
+// has consumed the current ones, q and k after phase 2, z after the epilogue.
 #include "mfma_common.hpp"
 
 namespace gtr {
@@ -66,10 +67,11 @@ __global__ __launch_bounds__(NT, SUM ? (DV == 128 ? 2 : 4) : (DV == 128 ? 1 : 2)
         }
         t.phase1();
         if (p + 1 < p1) t.rows_of(last_in_seq ? bh + 1 : bh, last_in_seq ? 0 : ch + 1, cur ^ 1);
-        __syncthreads();  // B1: block totals, V^T, the next chunk's rows
+        __syncthreads();  // B1: block totals, V, the next chunk's rows
+        if (p + 1 < p1) t.prefetch_gv(cur ^ 1);  // phase 1 consumed log_g and v
         const bool slow = t.phase2(&gam);
+        if (p + 1 < p1) t.prefetch_qk(cur ^ 1);  // phase 2 consumed q and k
         __syncthreads();  // B2: operand matrices
-        if (p + 1 < p1) t.prefetch_main(cur ^ 1);
 
         if (SUM) {
             t.s_update();

@@ -300,10 +300,46 @@ struct Tile {
         }
     }
 
-    __device__ __forceinline__ void prefetch_main(int buf) {
+    __device__ __forceinline__ int64_t own_row(int buf) const {
+        const int64_t row = sRow[buf * C + 16 * w + lr];
+        return row < 0 ? ~row : row;
+    }
+
+    // next chunk's inputs, in two parts: log_g and v (consumed by phase 1), then
+    // q and k (consumed by phase 2)
+    __device__ __forceinline__ void prefetch_gv(int buf) {
         if (!own) return;
-        int64_t row = sRow[buf * C + 16 * w + lr];
-        row = row < 0 ? ~row : row;
+        const int64_t row = own_row(buf);
+#pragma unroll
+        for (int kap = 0; kap < 2; ++kap) {
+            const int c0 = 32 * kap + 8 * g;
+            pg[2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
+            pg[2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
+        }
+#pragma unroll
+        for (int vm = 0; vm < DV / 32; ++vm) {
+            const int d0 = 8 * (g + 4 * vm);
+            uint4 x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + row * DV + d0);
+            if (a.resid) {  // stack residual: v + out_prev, rounded to the I/O type
+                const uint4 y = *reinterpret_cast<const uint4 *>(
+                    static_cast<const uint16_t *>(a.resid) + row * DV + d0);
+                uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+                const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = f2h<DT>(h2f<DT>(xs[e] & 0xffffu) + h2f<DT>(ys[e] & 0xffffu));
+                    const uint32_t hi = f2h<DT>(h2f<DT>(xs[e] >> 16) + h2f<DT>(ys[e] >> 16));
+                    xs[e] = lo | (hi << 16);
+                }
+                x = make_uint4(xs[0], xs[1], xs[2], xs[3]);
+            }
+            pv[vm] = x;
+        }
+    }
+
+    __device__ __forceinline__ void prefetch_qk(int buf) {
+        if (!own) return;
+        const int64_t row = own_row(buf);
 #pragma unroll
         for (int kap = 0; kap < 2; ++kap) {
             const int c0 = 32 * kap + 8 * g;
@@ -312,32 +348,12 @@ struct Tile {
                                                            row * DK + c0);
             pk[kap] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) +
                                                        row * DK + c0);
-            pg[2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
-            pg[2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
         }
-#pragma unroll
-        for (int vm = 0; vm < DV / 32; ++vm) {
-            const int d0 = 8 * (g + 4 * vm);
-            uint4 x;
-            {
-                x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + row * DV +
-                                                     d0);
-                if (a.resid) {  // stack residual: v + out_prev, rounded to the I/O type
-                    const uint4 y = *reinterpret_cast<const uint4 *>(
-                        static_cast<const uint16_t *>(a.resid) + row * DV + d0);
-                    uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-                    const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = f2h<DT>(h2f<DT>(xs[e] & 0xffffu) + h2f<DT>(ys[e] & 0xffffu));
-                        const uint32_t hi = f2h<DT>(h2f<DT>(xs[e] >> 16) + h2f<DT>(ys[e] >> 16));
-                        xs[e] = lo | (hi << 16);
-                    }
-                    x = make_uint4(xs[0], xs[1], xs[2], xs[3]);
-                }
-            }
-            pv[vm] = x;
-        }
+    }
+
+    __device__ __forceinline__ void prefetch_main(int buf) {
+        prefetch_gv(buf);
+        prefetch_qk(buf);
     }
 
     __device__ __forceinline__ void prefetch_z(int buf) {
