@@ -208,7 +208,7 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
     e = state_scan_plan(U, G, pl, static_cast<int>(n_seq), a.dk, a.dv, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "state scan launch");
-    e = mfma_output(a, po, pl, U, st);
+    e = rows_supported(a) ? rows_output(a, po, pl, U, st) : mfma_output(a, po, pl, U, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "chunk output launch");
     return GTR_OK;

@@ -135,6 +135,11 @@ hipError_t mfma_summary(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G
 // Sx: incoming state of every ps segment
 hipError_t mfma_output(const GlaArgs &a, const MfmaPlan &po, const MfmaPlan &ps, const float *Sx,
                        hipStream_t s);
+// Chunk outputs with token-row ownership per wave (k_rows.hip): 16-bit I/O,
+// dk = 64, dv in {64, 128}, chunk 64.  Same plans and incoming states as mfma_output.
+bool rows_supported(const GlaArgs &a);
+hipError_t rows_output(const GlaArgs &a, const MfmaPlan &po, const MfmaPlan &ps, const float *Sx,
+                       hipStream_t s);
 // Single-launch path (one workgroup per chunk, chunks handed out by ticket).
 int64_t fast_chunks(const GlaArgs &a);    // workgroups the launch needs
 int64_t fast_counters(const GlaArgs &a);  // 32-bit counters the launch needs

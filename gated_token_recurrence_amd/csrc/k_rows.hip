@@ -1,0 +1,617 @@
+// k_rows.hip -- chunk-output kernel with token-row ownership (16-bit I/O, dk = 64,
+// chunk 64, dv in {64, 128}).
+//
+// GTR write-up ("端侧实时感知新标杆！通用线性骨干网络GTR开源"), Method §4
+// "硬件感知分块推理算子": per-chunk outputs whose score tile stays on chip, with
+// the output gate fused into the epilogue; Method §1 gives the recurrence, the
+// readout, RMSNorm and the SiLU(z) gate.  With a_i the in-chunk inclusive
+// cumulative log2-gate and G = a at the chunk's last token:
+//   o_i   = (q_i 2^a_i)^T S + sum_{j <= i} (sum_c (q_ic 2^a_ic)(k_jc 2^-a_jc)) v_j
+//   S_new = Diag(2^G) (S + sum_j (k_j 2^-a_j) v_j^T)
+// A chunk whose decay span exceeds kSpanMax (log2 units) runs token by token in
+// fp32 instead (S_t = Diag(g_t) S + k_t v_t^T, o_t = S_t^T q_t).
+//
+// Work split inside a workgroup of four waves: wave w owns the chunk's tokens
+// [16 w, 16 w + 16) -- it loads them, forms their operands, computes all of their
+// output columns and runs their epilogue -- and the state columns of value
+// tiles NS w .. NS w + NS - 1.  So:
+//   * Q~ = q 2^a of a wave's own tokens is already in the MFMA operand layout
+//     where it is formed and never goes through LDS;
+//   * a wave's score tiles P^T_J = K^_J Q~_w^T (J <= w) stay in registers and
+//     feed the intra-chunk product directly (their register order is the k-slot
+//     order of the V^T operand);
+//   * every output column of a token is in one wave, so RMSNorm needs only
+//     cross-lane sums and the epilogue stores whole 64-byte half rows.
+// What the waves share through LDS: K^ (hi, lo) for the scores and the state
+// update, V for the intra product and the state update, and the state S^T
+// (hi, lo) that every wave reads for Q~ S.  Three barriers per chunk.
+//
+// Value-column map.  MFMA tile dd of the output O^T (16 value columns) holds in
+// its row m the value column dcol(dd, m) = colB(dd, m / 4) + m % 4 with
+// colB(dd, k) = 32 (dd / 2) + 8 k + 4 ((dd & 1) ^ (k & 1)).  Then lane group g
+// of a token holds the columns [32 e + 8 g, 32 e + 8 g + 8) of tiles 2e, 2e + 1
+// (the first four from tile 2e + (g & 1)), i.e. whole 16-byte pieces, and the
+// transposing V reads that produce this order are free of bank conflicts under
+// the swizzle swv.  The state tiles use the same map for their columns.
+#include "mfma_common.hpp"
+
+namespace gtr {
+namespace {
+
+using namespace mf;
+
+// Token-major V matrix [token][64 columns]: 16-byte pieces XORed by
+// fv(row) = r1 | r3 << 1 | r2 << 2 (bit i of the row = ri).
+__device__ __forceinline__ int swv(int row, int col) {
+    const int f = ((row >> 1) & 1) | (((row >> 3) & 1) << 1) | (((row >> 2) & 1) << 2);
+    return row * 64 + ((((col >> 3) ^ f) << 3) | (col & 7));
+}
+
+// S^T matrix [value column][64 key channels]: pieces XORed by r1 | (r4 r3) << 1.
+__device__ __forceinline__ int sws(int row, int col) {
+    const int f = ((row >> 1) & 1) | (((row >> 3) & 3) << 1);
+    return row * 64 + ((((col >> 3) ^ f) << 3) | (col & 7));
+}
+
+__device__ __forceinline__ int colB(int dd, int k) {
+    return 32 * (dd >> 1) + 8 * k + 4 * ((dd & 1) ^ (k & 1));
+}
+__device__ __forceinline__ int dcol(int dd, int m) { return colB(dd, m >> 2) + (m & 3); }
+
+template <int DT, int DV>
+struct RowTile {
+    static constexpr int C = 64, NB = 4;
+    static constexpr int ND = DV / 16;  // value tiles
+    static constexpr int NS = ND / 4;   // state tiles per wave
+    static constexpr int VP = DV / 64;  // 64-column planes of V
+    static constexpr int NV = (DT == DT_F16) ? 2 : 1;  // V as bf16 hi (+ lo for fp16)
+    static constexpr int NE = DV / 32;  // 16-byte value pieces per lane (epilogue, V loads)
+    static constexpr int MAT = C * 64;
+    // LDS carve-up (bytes).  Token-serial chunks reuse K (raw q, k) and S (fp32
+    // gates, then the output exchange).
+    static constexpr int O_K = 0;                           // K^ hi, lo
+    static constexpr int O_V = O_K + 2 * MAT * 2;           // V [part][plane][64][64]
+    static constexpr int O_S = O_V + NV * VP * MAT * 2;     // S^T hi, lo [2][DV][64]
+    static constexpr int O_TOT = O_S + 2 * DV * 64 * 2;     // float [NB][DK]
+    static constexpr int O_TAB = O_TOT + NB * DK * 4;       // float [4 waves][2][DK]
+    static constexpr int O_RW = O_TAB + 4 * 2 * DK * 4;     // float [DV]
+    static constexpr int BYTES = O_RW + DV * 4;
+    static_assert(C * DK * 4 <= 2 * DV * 64 * 2, "fp32 gates must fit the state area");
+    static_assert(ND * 4 * 64 * 16 <= 2 * DV * 64 * 2, "output exchange must fit the state area");
+
+    GlaArgs a;
+    uint16_t *sK, *sV, *sS;
+    float *sTot, *sTab, *sRw;
+    int w, l, lr, g;
+
+    // this lane's token: rows (negative = past the end, ~row of the last token)
+    int64_t rowC, rowN;
+    // next chunk's inputs of this lane's token
+    uint4 pq[2], pk[2], pv[NE], pz[NE];
+    float4 pg[4];
+    float cs[16];
+    // state tiles (S[s][ct][r] = S[16 ct + 4 g + r][dcol(NS w + s, lr)]) and the
+    // output tiles of this wave's tokens (O[dd][r] = O^T[dcol(dd, 4 g + r)][token lr])
+    f32x4 S[NS][4];
+    f32x4 O[ND];
+    s16x8 qh[2], ql[2];  // Q~ of this wave's tokens, B-operand layout
+
+    __device__ __forceinline__ void init(const GlaArgs &args, char *smem) {
+        a = args;
+        sK = reinterpret_cast<uint16_t *>(smem + O_K);
+        sV = reinterpret_cast<uint16_t *>(smem + O_V);
+        sS = reinterpret_cast<uint16_t *>(smem + O_S);
+        sTot = reinterpret_cast<float *>(smem + O_TOT);
+        sRw = reinterpret_cast<float *>(smem + O_RW);
+        const int tid = threadIdx.x;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        l = tid & 63;
+        lr = l & 15;
+        g = l >> 4;
+        sTab = reinterpret_cast<float *>(smem + O_TAB) + w * 2 * DK;
+        if (tid < DV) sRw[tid] = a.rms_w[tid];  // read after later barriers
+    }
+
+    // Row index ((b L + grid position) H + h) of this lane's token of chunk ch of
+    // sequence bh.  A token past the end of the sequence reads the last token's
+    // row (finite values that reach only masked scores, its own unstored output
+    // and the state after the sequence's last chunk, which is never used).
+    __device__ __forceinline__ int64_t row_of(int64_t bh, int64_t ch) const {
+        const uint32_t L32 = static_cast<uint32_t>(a.L);
+        const uint32_t t0 = static_cast<uint32_t>(ch) * C + 16 * w + lr;
+        uint32_t t = t0 < L32 ? t0 : L32 - 1;
+        if (a.direction & 1) t = L32 - 1 - t;  // RL, BT: reversed sequence
+        uint32_t pos = t;
+        if (a.direction >= 2) {                // TB, BT: column-major raster
+            const uint32_t gh = static_cast<uint32_t>(a.gh);
+            const uint32_t c = t / gh;
+            pos = (t - c * gh) * static_cast<uint32_t>(a.gw) + c;
+        }
+        const int64_t b = bh / a.H;
+        const int64_t h = bh - b * a.H;
+        const int64_t row = (b * a.L + pos) * a.H + h;
+        return t0 < L32 ? row : ~row;
+    }
+    __device__ __forceinline__ static int64_t live(int64_t row) { return row < 0 ? ~row : row; }
+
+    __device__ __forceinline__ void prefetch_gv(int64_t rw) {
+        const int64_t row = live(rw);
+#pragma unroll
+        for (int kap = 0; kap < 2; ++kap) {
+            const int c0 = 32 * kap + 8 * g;
+            pg[2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
+            pg[2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int d0 = 32 * e + 8 * g;
+            uint4 x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + row * DV + d0);
+            if (a.resid) {  // stack residual: v + out_prev, rounded to the I/O type
+                const uint4 y = *reinterpret_cast<const uint4 *>(
+                    static_cast<const uint16_t *>(a.resid) + row * DV + d0);
+                uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+                const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t lo = f2h<DT>(h2f<DT>(xs[u] & 0xffffu) + h2f<DT>(ys[u] & 0xffffu));
+                    const uint32_t hi = f2h<DT>(h2f<DT>(xs[u] >> 16) + h2f<DT>(ys[u] >> 16));
+                    xs[u] = lo | (hi << 16);
+                }
+                x = make_uint4(xs[0], xs[1], xs[2], xs[3]);
+            }
+            pv[e] = x;
+        }
+    }
+
+    __device__ __forceinline__ void prefetch_qk(int64_t rw) {
+        const int64_t row = live(rw);
+#pragma unroll
+        for (int kap = 0; kap < 2; ++kap) {
+            const int c0 = 32 * kap + 8 * g;
+            pq[kap] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + row * DK + c0);
+            pk[kap] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + row * DK + c0);
+        }
+    }
+
+    __device__ __forceinline__ void prefetch_z(int64_t rw) {
+        const int64_t row = live(rw);
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            pz[e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.z) + row * DV +
+                                                     32 * e + 8 * g);
+    }
+
+    // incoming state (fp32 [DK][DV]) of the owned tiles
+    __device__ __forceinline__ void load_state(const float *src) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int d = dcol(NS * w + s, lr);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[s][ct][r] = src[(16 * ct + 4 * g + r) * DV + d];
+        }
+    }
+
+    // ---- phase 1: the state S^T (hi, lo) of the owned tiles into LDS; cumulative
+    // gates of the wave's tokens (registers, natural-log units) and their totals;
+    // V into LDS.
+    __device__ __forceinline__ void phase1() {
+        uint16_t *sh = sS, *sl = sS + DV * 64;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int d = dcol(NS * w + s, lr);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const float x[4] = {S[s][ct][0], S[s][ct][1], S[s][ct][2], S[s][ct][3]};
+                uint32_t hi[2], lo[2];
+                split_pk<false>(x, hi, lo);
+                const int off = sws(d, 16 * ct + 4 * g);
+                *reinterpret_cast<uint2 *>(sh + off) = make_uint2(hi[0], hi[1]);
+                *reinterpret_cast<uint2 *>(sl + off) = make_uint2(lo[0], lo[1]);
+            }
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            cs[4 * q4] = pg[q4].x; cs[4 * q4 + 1] = pg[q4].y;
+            cs[4 * q4 + 2] = pg[q4].z; cs[4 * q4 + 3] = pg[q4].w;
+        }
+        row_scan(cs);
+        if (lr == 15) {
+#pragma unroll
+            for (int kap = 0; kap < 2; ++kap) {
+                float *dst = sTot + w * DK + 32 * kap + 8 * g;
+                *reinterpret_cast<float4 *>(dst) =
+                    make_float4(cs[8 * kap], cs[8 * kap + 1], cs[8 * kap + 2], cs[8 * kap + 3]);
+                *reinterpret_cast<float4 *>(dst + 4) =
+                    make_float4(cs[8 * kap + 4], cs[8 * kap + 5], cs[8 * kap + 6], cs[8 * kap + 7]);
+            }
+        }
+        const int i = 16 * w + lr;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int d0 = 32 * e + 8 * g;
+            uint16_t *m = sV + (d0 >> 6) * MAT + swv(i, d0 & 63);
+            if (NV == 1) {
+                *reinterpret_cast<uint4 *>(m) = pv[e];
+            } else {  // fp16 values as bf16 hi + lo (exact)
+                float x[8];
+                unpack8<DT>(pv[e], x);
+                uint32_t hi[4], lo[4];
+                split_pk<false>(x, hi, lo);
+                *reinterpret_cast<uint4 *>(m) = u4(hi);
+                *reinterpret_cast<uint4 *>(m + VP * MAT) = u4(lo);
+            }
+        }
+    }
+
+    // ---- phase 2 (after phase 1 everywhere): chunk totals, span check, operands.
+    // Lane l computes for channel l the sum r of the sub-block totals before the
+    // wave's tokens and the chunk's decay 2^G; Q~ stays in registers, K^ (hi, lo)
+    // goes to LDS.  Returns whether the chunk runs token by token (the same in
+    // every wave).
+    __device__ __forceinline__ bool phase2() {
+        float r_l = 0.f, tot_l = 0.f;
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+            const float t = sTot[J * DK + l];
+            if (J < w) r_l += t;
+            tot_l += t;
+        }
+        r_l *= kLog2e;
+        tot_l *= kLog2e;
+        float sp2 = -tot_l;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) sp2 = fmaxf(sp2, __shfl_xor(sp2, off));
+        const bool slow = sp2 > kSpanMax;
+        sTab[l] = r_l;
+        sTab[DK + l] = fexp2(tot_l);
+        __builtin_amdgcn_wave_barrier();
+        const int i = 16 * w + lr;
+#pragma unroll
+        for (int kap = 0; kap < 2; ++kap) {
+            const int c0 = 32 * kap + 8 * g;
+            if (!slow) {
+                float rI[8];
+#pragma unroll
+                for (int h4 = 0; h4 < 2; ++h4) {
+                    const float4 x = *reinterpret_cast<const float4 *>(sTab + c0 + 4 * h4);
+                    rI[4 * h4] = x.x; rI[4 * h4 + 1] = x.y; rI[4 * h4 + 2] = x.z; rI[4 * h4 + 3] = x.w;
+                }
+                float qt[8], kh[8];
+                unpack8<DT>(pq[kap], qt);
+                unpack8<DT>(pk[kap], kh);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float aa = fmaf(cs[8 * kap + s], kLog2e, rI[s]);
+                    qt[s] *= fexp2(aa);   // q 2^a
+                    kh[s] *= fexp2(-aa);  // k 2^-a
+                }
+                uint32_t qhi[4], qlo[4], khi[4], klo[4];
+                split_pk<false>(qt, qhi, qlo);
+                split_pk<false>(kh, khi, klo);
+                qh[kap] = __builtin_bit_cast(s16x8, u4(qhi));
+                ql[kap] = __builtin_bit_cast(s16x8, u4(qlo));
+                const int off = swn(i, c0);
+                *reinterpret_cast<uint4 *>(sK + off) = u4(khi);
+                *reinterpret_cast<uint4 *>(sK + MAT + off) = u4(klo);
+            } else {
+                // token-serial operands, [token][channel] without swizzle: q and k as
+                // stored (K area), g = 2^(a_i - a_{i-1}) in fp32 (state area)
+                *reinterpret_cast<uint4 *>(sK + i * DK + c0) = pq[kap];
+                *reinterpret_cast<uint4 *>(sK + MAT + i * DK + c0) = pk[kap];
+                float *fG = reinterpret_cast<float *>(sS);
+                float gg[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float up = __shfl_up(cs[8 * kap + s], 1, 16);
+                    const float prev = (lr == 0) ? 0.f : up;
+                    gg[s] = fexp2((cs[8 * kap + s] - prev) * kLog2e);
+                }
+                *reinterpret_cast<float4 *>(fG + i * DK + c0) = make_float4(gg[0], gg[1], gg[2], gg[3]);
+                *reinterpret_cast<float4 *>(fG + i * DK + c0 + 4) = make_float4(gg[4], gg[5], gg[6], gg[7]);
+            }
+        }
+        return slow;
+    }
+
+    // V^T operand of value tile dd, V part p: lane row / column dcol(dd, lr), k
+    // slots = tokens rb + 4 g + s (s < 4) and rb + 16 + 4 g + (s - 4), by two
+    // transposing reads (lane i's slot j comes from source lane 4 j + i / 4).
+    __device__ __forceinline__ s16x8 op_v(int p, int dd, int rb) const {
+        const uint16_t *m = sV + (p * VP + (dd >> 2)) * MAT;
+        const int r = rb + 4 * g + (lr >> 2);
+        const int c = colB(dd, lr & 3) & 63;
+        const s16x4 x0 = ld_tr(m + swv(r, c));
+        const s16x4 x1 = ld_tr(m + swv(r + 16, c));
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+
+    // K^T operand (A rows = channels cb + lr), same token slots
+    __device__ __forceinline__ s16x8 op_k(const uint16_t *m, int rb, int cb) const {
+        const int r = rb + 4 * g + (lr >> 2);
+        const int c = cb + 4 * (lr & 3);
+        const s16x4 x0 = ld_tr(m + swn(r, c));
+        const s16x4 x1 = ld_tr(m + swn(r + 16, c));
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+
+    // ---- products of a chunk (after phase 2 everywhere)
+    __device__ __forceinline__ void compute() {
+        // inter-chunk readout O^T = S^T Q~_w^T
+        const uint16_t *sh = sS, *sl = sS + DV * 64;
+#pragma unroll
+        for (int dd = 0; dd < ND; ++dd) {
+            O[dd] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int d = dcol(dd, lr);
+#pragma unroll
+            for (int kap = 0; kap < 2; ++kap) {
+                const int off = sws(d, 32 * kap + 8 * g);
+                const s16x8 ah = *reinterpret_cast<const s16x8 *>(sh + off);
+                const s16x8 al = *reinterpret_cast<const s16x8 *>(sl + off);
+                O[dd] = mma<false>(ah, qh[kap], O[dd]);
+                O[dd] = mma<false>(ah, ql[kap], O[dd]);
+                O[dd] = mma<false>(al, qh[kap], O[dd]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keeps the operand loads of each step near it
+        // causal score tiles P^T_J[j][i] = K^_J Q~_w^T, J <= w, kept as hi + lo
+        uint32_t ph[NB][2], pl[NB][2];
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+            ph[J][0] = ph[J][1] = pl[J][0] = pl[J][1] = 0u;
+            if (J <= w) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kap = 0; kap < 2; ++kap) {
+                    const int off = swn(16 * J + lr, 32 * kap + 8 * g);
+                    const s16x8 kh = *reinterpret_cast<const s16x8 *>(sK + off);
+                    const s16x8 kl = *reinterpret_cast<const s16x8 *>(sK + MAT + off);
+                    acc = mma<false>(kh, qh[kap], acc);
+                    acc = mma<false>(kh, ql[kap], acc);
+                    acc = mma<false>(kl, qh[kap], acc);
+                }
+                float x[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = (J == w && 4 * g + r > lr) ? 0.f : acc[r];  // j <= i
+                split_pk<false>(x, ph[J], pl[J]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // intra-chunk readout O^T += V^T P^T, 32 tokens per step
+#pragma unroll
+        for (int kt = 0; kt < NB / 2; ++kt) {
+            if (2 * kt <= w) {
+                const s16x8 bh = __builtin_bit_cast(
+                    s16x8, make_uint4(ph[2 * kt][0], ph[2 * kt][1], ph[2 * kt + 1][0], ph[2 * kt + 1][1]));
+                const s16x8 bl = __builtin_bit_cast(
+                    s16x8, make_uint4(pl[2 * kt][0], pl[2 * kt][1], pl[2 * kt + 1][0], pl[2 * kt + 1][1]));
+#pragma unroll
+                for (int dd = 0; dd < ND; ++dd) {
+                    const s16x8 av = op_v(0, dd, 32 * kt);
+                    O[dd] = mma<false>(av, bh, O[dd]);
+                    O[dd] = mma<false>(av, bl, O[dd]);
+                    if (NV == 2) O[dd] = mma<false>(op_v(NV - 1, dd, 32 * kt), bh, O[dd]);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // state update of the owned tiles: S = Diag(2^G) (S + K^^T V)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int dd = NS * w + s;
+#pragma unroll
+            for (int kt = 0; kt < NB / 2; ++kt) {
+                s16x8 bv[NV];
+#pragma unroll
+                for (int p = 0; p < NV; ++p) bv[p] = op_v(p, dd, 32 * kt);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    const s16x8 akh = op_k(sK, 32 * kt, 16 * ct);
+                    const s16x8 akl = op_k(sK + MAT, 32 * kt, 16 * ct);
+                    S[s][ct] = mma<false>(akh, bv[0], S[s][ct]);
+                    S[s][ct] = mma<false>(akl, bv[0], S[s][ct]);
+                    if (NV == 2) S[s][ct] = mma<false>(akh, bv[NV - 1], S[s][ct]);
+                }
+            }
+        }
+        decay();
+    }
+
+    __device__ __forceinline__ void decay() {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const float4 e4 = *reinterpret_cast<const float4 *>(sTab + DK + 16 * ct + 4 * g);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                S[s][ct][0] *= e4.x; S[s][ct][1] *= e4.y; S[s][ct][2] *= e4.z; S[s][ct][3] *= e4.w;
+            }
+        }
+    }
+
+    // ---- token-serial chunk: S and o from the fp32 operands of phase 2, for the
+    // owned tiles and every token; the tiles are then exchanged through LDS so
+    // that each wave holds all columns of its own tokens.
+    __device__ __forceinline__ void serial() {
+        const uint16_t *fQ = sK, *fK = sK + MAT;
+        const float *fG = reinterpret_cast<const float *>(sS);
+        f32x4 Os[NS][NB];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) Os[s][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < C; ++t) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int d = dcol(NS * w + s, lr);
+                const uint16_t *vm = sV + (d >> 6) * MAT + swv(t, d & 63);
+                float vd;
+                if (NV == 2)
+                    vd = __uint_as_float(static_cast<uint32_t>(vm[0]) << 16) +
+                         __uint_as_float(static_cast<uint32_t>(vm[VP * MAT]) << 16);
+                else
+                    vd = h2f<DT>(vm[0]);
+                float part = 0.f;
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const int c = 16 * ct + 4 * g;
+                    const float4 gq = *reinterpret_cast<const float4 *>(fG + t * DK + c);
+                    const uint2 kq = *reinterpret_cast<const uint2 *>(fK + t * DK + c);
+                    const uint2 qq = *reinterpret_cast<const uint2 *>(fQ + t * DK + c);
+                    const float gg[4] = {gq.x, gq.y, gq.z, gq.w};
+                    const float kk[4] = {h2f<DT>(kq.x & 0xffffu), h2f<DT>(kq.x >> 16),
+                                         h2f<DT>(kq.y & 0xffffu), h2f<DT>(kq.y >> 16)};
+                    const float q4[4] = {h2f<DT>(qq.x & 0xffffu), h2f<DT>(qq.x >> 16),
+                                         h2f<DT>(qq.y & 0xffffu), h2f<DT>(qq.y >> 16)};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        S[s][ct][r] = gg[r] * S[s][ct][r] + kk[r] * vd;
+                        part += S[s][ct][r] * q4[r];
+                    }
+                }
+                part += __shfl_xor(part, 16);
+                part += __shfl_xor(part, 32);
+                // o_t at column dcol(dd, lr) is now in every lane group; lane (t % 16, g)
+                // takes the columns dcol(dd, 4 g + r) = colB(dd, g) + r
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = __shfl(part, 4 * g + r);
+                    if (lr == (t & 15)) {
+#pragma unroll
+                        for (int tb = 0; tb < NB; ++tb)
+                            if (tb == (t >> 4)) Os[s][tb][r] = x;
+                    }
+                }
+            }
+        }
+        __syncthreads();  // every wave is done with the gates in the state area
+        f32x4 *X = reinterpret_cast<f32x4 *>(sS);  // [dd][tb][lane]
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) X[((NS * w + s) * NB + tb) * 64 + l] = Os[s][tb];
+        __syncthreads();
+#pragma unroll
+        for (int dd = 0; dd < ND; ++dd) O[dd] = X[(dd * NB + w) * 64 + l];
+    }
+
+    // ---- epilogue: y = o / sqrt(mean_j o_j^2 + eps) * rms_w * z * sigmoid(z) for the
+    // wave's tokens, stored at the token's grid position
+    __device__ __forceinline__ void epilogue() {
+        float ss = 0.f;
+#pragma unroll
+        for (int dd = 0; dd < ND; ++dd)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ss += O[dd][r] * O[dd][r];
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + GTR_RMS_EPS);
+        const bool odd = g & 1;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int d0 = 32 * e + 8 * g;
+            const f32x4 lo4 = odd ? O[2 * e + 1] : O[2 * e];
+            const f32x4 hi4 = odd ? O[2 * e] : O[2 * e + 1];
+            const float o[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            const float4 w0 = *reinterpret_cast<const float4 *>(sRw + d0);
+            const float4 w1 = *reinterpret_cast<const float4 *>(sRw + d0 + 4);
+            const float rw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            uint32_t yb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t h[2];
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const int k = 2 * u + v;
+                    const float zz = h2f<DT>(half16(pz[e], k));
+                    const float silu = zz * frcp(1.0f + fexp2(-zz * kLog2e));
+                    h[v] = f2h<DT>(o[k] * inv * rw[k] * silu);
+                }
+                yb[u] = h[0] | (h[1] << 16);
+            }
+            if (rowC >= 0)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + rowC * DV + d0) =
+                    make_uint4(yb[0], yb[1], yb[2], yb[3]);
+        }
+    }
+};
+
+template <int DT, int DV>
+__global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const float *__restrict__ Sx,
+                                                               MfmaPlan pl, MfmaPlan ps) {
+    using R = RowTile<DT, DV>;
+    __shared__ __attribute__((aligned(16))) char smem[R::BYTES];
+    R t;
+    t.init(a, smem);
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * pl.Q;
+    const int64_t p1 = (p0 + pl.Q < pl.T) ? p0 + pl.Q : pl.T;
+    if (p0 >= p1) return;  // the whole workgroup
+
+    int64_t bh = p0 / pl.N;  // current sequence and chunk, advanced incrementally
+    int64_t ch = p0 - bh * pl.N;
+    t.rowC = t.row_of(bh, ch);
+    t.prefetch_gv(t.rowC);
+    t.prefetch_qk(t.rowC);
+    t.prefetch_z(t.rowC);
+
+    for (int64_t p = p0; p < p1; ++p) {
+        const bool last_in_seq = (ch == pl.N - 1);
+        const bool more = p + 1 < p1;
+        if (p == p0 || ch == 0) t.load_state(Sx + seg_id(p, ps) * DK * DV);  // segment start
+        t.phase1();
+        __syncthreads();  // B1: state, gate totals, V
+        if (more) {
+            t.rowN = t.row_of(last_in_seq ? bh + 1 : bh, last_in_seq ? 0 : ch + 1);
+            t.prefetch_gv(t.rowN);  // phase 1 consumed log_g and v
+        }
+        const bool slow = t.phase2();
+        if (more) t.prefetch_qk(t.rowN);  // phase 2 consumed q and k
+        __syncthreads();  // B2: K^
+        if (!slow)
+            t.compute();
+        else
+            t.serial();
+        t.epilogue();
+        if (more) {
+            t.prefetch_z(t.rowN);
+            t.rowC = t.rowN;
+        }
+        __syncthreads();  // B3: LDS is rewritten by the next chunk
+        if (last_in_seq) {
+            ch = 0;
+            ++bh;
+        } else {
+            ++ch;
+        }
+    }
+}
+
+template <int DT, int DV>
+hipError_t launch_rows(const GlaArgs &a, const float *Sx, const MfmaPlan &po, const MfmaPlan &ps,
+                       hipStream_t st) {
+    hipLaunchKernelGGL((k_rows<DT, DV>), dim3(static_cast<unsigned>(po.n_wg)), dim3(NT), 0, st, a, Sx,
+                       po, ps);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool rows_supported(const GlaArgs &a) {
+    return (a.dtype == DT_F16 || a.dtype == DT_BF16) && a.dk == DK && (a.dv == 64 || a.dv == 128) &&
+           a.chunk == 64;
+}
+
+hipError_t rows_output(const GlaArgs &a, const MfmaPlan &po, const MfmaPlan &ps, const float *Sx,
+                       hipStream_t s) {
+    if (a.dtype == DT_F16) {
+        if (a.dv == 64) return launch_rows<DT_F16, 64>(a, Sx, po, ps, s);
+        if (a.dv == 128) return launch_rows<DT_F16, 128>(a, Sx, po, ps, s);
+    } else if (a.dtype == DT_BF16) {
+        if (a.dv == 64) return launch_rows<DT_BF16, 64>(a, Sx, po, ps, s);
+        if (a.dv == 128) return launch_rows<DT_BF16, 128>(a, Sx, po, ps, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gtr
