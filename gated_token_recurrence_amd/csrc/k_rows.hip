@@ -497,7 +497,8 @@ struct RowTile {
     }
 
     // ---- epilogue: y = o / sqrt(mean_j o_j^2 + eps) * rms_w * z * sigmoid(z) for the
-    // wave's tokens, stored at the token's grid position
+    // wave's tokens, stored at the token's grid position (pairs rounded to nearest
+    // even by the packed conversion)
     __device__ __forceinline__ void epilogue() {
         float ss = 0.f;
 #pragma unroll
@@ -517,22 +518,18 @@ struct RowTile {
             const float4 w0 = *reinterpret_cast<const float4 *>(sRw + d0);
             const float4 w1 = *reinterpret_cast<const float4 *>(sRw + d0 + 4);
             const float rw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-            uint32_t yb[4];
+            float zz[8];
+            unpack8<DT>(pz[e], zz);
+            float y[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                uint32_t h[2];
-#pragma unroll
-                for (int v = 0; v < 2; ++v) {
-                    const int k = 2 * u + v;
-                    const float zz = h2f<DT>(half16(pz[e], k));
-                    const float silu = zz * frcp(1.0f + fexp2(-zz * kLog2e));
-                    h[v] = f2h<DT>(o[k] * inv * rw[k] * silu);
-                }
-                yb[u] = h[0] | (h[1] << 16);
+            for (int k = 0; k < 8; ++k) {
+                const float silu = zz[k] * frcp(1.0f + fexp2(-zz[k] * kLog2e));
+                y[k] = (o[k] * inv) * (rw[k] * silu);
             }
+            const uint4 yb = make_uint4(pk2<DT == DT_F16>(y[0], y[1]), pk2<DT == DT_F16>(y[2], y[3]),
+                                        pk2<DT == DT_F16>(y[4], y[5]), pk2<DT == DT_F16>(y[6], y[7]));
             if (rowC >= 0)
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + rowC * DV + d0) =
-                    make_uint4(yb[0], yb[1], yb[2], yb[3]);
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + rowC * DV + d0) = yb;
         }
     }
 };
