@@ -202,7 +202,7 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
     float *U = static_cast<float *>(ws);
     float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
     hipError_t e = mk.record(st, 0);
-    if (e == hipSuccess) e = mfma_summary(a, pl, U, G, st);
+    if (e == hipSuccess) e = sum_supported(a) ? sum_launch(a, pl, U, G, st) : mfma_summary(a, pl, U, G, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "segment summary launch");
     e = state_scan_plan(U, G, pl, static_cast<int>(n_seq), a.dk, a.dv, st);

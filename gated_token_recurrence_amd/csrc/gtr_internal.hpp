@@ -135,6 +135,10 @@ hipError_t mfma_summary(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G
 // Sx: incoming state of every ps segment
 hipError_t mfma_output(const GlaArgs &a, const MfmaPlan &po, const MfmaPlan &ps, const float *Sx,
                        hipStream_t s);
+// Segment summaries with per-wave partial sums (k_sum.hip): 16-bit I/O, dk = 64,
+// dv = 64, chunk 64.  Same plan and outputs as mfma_summary.
+bool sum_supported(const GlaArgs &a);
+hipError_t sum_launch(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t s);
 // Chunk outputs with token-row ownership per wave (k_rows.hip): 16-bit I/O,
 // dk = 64, dv in {64, 128}, chunk 64.  Same plans and incoming states as mfma_output.
 bool rows_supported(const GlaArgs &a);

@@ -58,7 +58,7 @@ __device__ __forceinline__ int colB(int dd, int k) {
 }
 __device__ __forceinline__ int dcol(int dd, int m) { return colB(dd, m >> 2) + (m & 3); }
 
-template <int DT, int DV>
+template <int DT, int DV, bool RES>
 struct RowTile {
     static constexpr int C = 64, NB = 4;
     static constexpr int ND = DV / 16;  // value tiles
@@ -88,6 +88,7 @@ struct RowTile {
     int64_t rowC, rowN;
     // next chunk's inputs of this lane's token
     uint4 pq[2], pk[2], pv[NE], pz[NE];
+    uint4 pr[RES ? NE : 1];  // previous block's output, added to v where v is consumed
     float4 pg[4];
     float cs[16];
     // state tiles (S[s][ct][r] = S[16 ct + 4 g + r][dcol(NS w + s, lr)]) and the
@@ -116,7 +117,7 @@ struct RowTile {
     // sequence bh.  A token past the end of the sequence reads the last token's
     // row (finite values that reach only masked scores, its own unstored output
     // and the state after the sequence's last chunk, which is never used).
-    __device__ __forceinline__ int64_t row_of(int64_t bh, int64_t ch) const {
+    __device__ __forceinline__ int64_t row_of(uint32_t b, uint32_t h, int64_t ch) const {
         const uint32_t L32 = static_cast<uint32_t>(a.L);
         const uint32_t t0 = static_cast<uint32_t>(ch) * C + 16 * w + lr;
         uint32_t t = t0 < L32 ? t0 : L32 - 1;
@@ -127,9 +128,7 @@ struct RowTile {
             const uint32_t c = t / gh;
             pos = (t - c * gh) * static_cast<uint32_t>(a.gw) + c;
         }
-        const int64_t b = bh / a.H;
-        const int64_t h = bh - b * a.H;
-        const int64_t row = (b * a.L + pos) * a.H + h;
+        const int64_t row = (static_cast<int64_t>(b) * a.L + pos) * a.H + h;
         return t0 < L32 ? row : ~row;
     }
     __device__ __forceinline__ static int64_t live(int64_t row) { return row < 0 ? ~row : row; }
@@ -145,21 +144,9 @@ struct RowTile {
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
             const int d0 = 32 * e + 8 * g;
-            uint4 x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + row * DV + d0);
-            if (a.resid) {  // stack residual: v + out_prev, rounded to the I/O type
-                const uint4 y = *reinterpret_cast<const uint4 *>(
-                    static_cast<const uint16_t *>(a.resid) + row * DV + d0);
-                uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-                const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t lo = f2h<DT>(h2f<DT>(xs[u] & 0xffffu) + h2f<DT>(ys[u] & 0xffffu));
-                    const uint32_t hi = f2h<DT>(h2f<DT>(xs[u] >> 16) + h2f<DT>(ys[u] >> 16));
-                    xs[u] = lo | (hi << 16);
-                }
-                x = make_uint4(xs[0], xs[1], xs[2], xs[3]);
-            }
-            pv[e] = x;
+            pv[e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + row * DV + d0);
+            if constexpr (RES)
+                pr[e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.resid) + row * DV + d0);
         }
     }
 
@@ -191,6 +178,15 @@ struct RowTile {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[s][ct][r] = src[(16 * ct + 4 * g + r) * DV + d];
         }
+    }
+
+    // Waits for the incoming state here, at the segment start: the chunk loop then
+    // never holds a load that is outstanding on one path into it and not the other.
+    __device__ __forceinline__ void state_ready() {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) asm volatile("" ::"v"(S[s][ct]));
     }
 
     // ---- phase 1: the state S^T (hi, lo) of the owned tiles into LDS; cumulative
@@ -232,11 +228,13 @@ struct RowTile {
         for (int e = 0; e < NE; ++e) {
             const int d0 = 32 * e + 8 * g;
             uint16_t *m = sV + (d0 >> 6) * MAT + swv(i, d0 & 63);
+            uint4 vx = pv[e];
+            if constexpr (RES) vx = add_io<DT>(vx, pr[e]);  // stack residual
             if (NV == 1) {
-                *reinterpret_cast<uint4 *>(m) = pv[e];
+                *reinterpret_cast<uint4 *>(m) = vx;
             } else {  // fp16 values as bf16 hi + lo (exact)
                 float x[8];
-                unpack8<DT>(pv[e], x);
+                unpack8<DT>(vx, x);
                 uint32_t hi[4], lo[4];
                 split_pk<false>(x, hi, lo);
                 *reinterpret_cast<uint4 *>(m) = u4(hi);
@@ -534,10 +532,10 @@ struct RowTile {
     }
 };
 
-template <int DT, int DV>
+template <int DT, int DV, bool RES>
 __global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const float *__restrict__ Sx,
                                                                MfmaPlan pl, MfmaPlan ps) {
-    using R = RowTile<DT, DV>;
+    using R = RowTile<DT, DV, RES>;
     __shared__ __attribute__((aligned(16))) char smem[R::BYTES];
     R t;
     t.init(a, smem);
@@ -545,41 +543,52 @@ __global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const 
     const int64_t p1 = (p0 + pl.Q < pl.T) ? p0 + pl.Q : pl.T;
     if (p0 >= p1) return;  // the whole workgroup
 
-    int64_t bh = p0 / pl.N;  // current sequence and chunk, advanced incrementally
-    int64_t ch = p0 - bh * pl.N;
-    t.rowC = t.row_of(bh, ch);
+    // current image b, head h and chunk ch, advanced incrementally (no divisions
+    // in the loop)
+    const int64_t bh0 = p0 / pl.N;
+    int64_t ch = p0 - bh0 * pl.N;
+    uint32_t b = static_cast<uint32_t>(bh0 / a.H), h = static_cast<uint32_t>(bh0 % a.H);
+    t.rowC = t.row_of(b, h, ch);
     t.prefetch_gv(t.rowC);
     t.prefetch_qk(t.rowC);
     t.prefetch_z(t.rowC);
 
-    for (int64_t p = p0; p < p1; ++p) {
-        const bool last_in_seq = (ch == pl.N - 1);
-        const bool more = p + 1 < p1;
-        if (p == p0 || ch == 0) t.load_state(Sx + seg_id(p, ps) * DK * DV);  // segment start
-        t.phase1();
-        __syncthreads();  // B1: state, gate totals, V
-        if (more) {
-            t.rowN = t.row_of(last_in_seq ? bh + 1 : bh, last_in_seq ? 0 : ch + 1);
+    // Segments (the range's pieces within one sequence) in an outer loop, so that
+    // the incoming state is loaded outside the chunk loop: the chunk loop then
+    // issues the same loads every time and the wait-count bookkeeping never has to
+    // drain the load queue.
+    for (int64_t p = p0; p < p1;) {
+        const int64_t pe = (p - ch + pl.N < p1) ? p - ch + pl.N : p1;  // segment end
+        t.load_state(Sx + seg_id(p, ps) * DK * DV);
+        t.state_ready();
+        for (; p < pe; ++p) {
+            const bool last_in_seq = (ch == pl.N - 1);
+            const bool more = p + 1 < p1;
+            t.phase1();
+            __syncthreads();  // B1: state, gate totals, V
+            // The next chunk's loads are issued on every chunk (on the range's last
+            // one they re-read its own rows, unused).
+            uint32_t nb = b, nh = h;
+            if (last_in_seq && ++nh == static_cast<uint32_t>(a.H)) {
+                nh = 0;
+                ++nb;
+            }
+            t.rowN = more ? t.row_of(nb, nh, last_in_seq ? 0 : ch + 1) : t.rowC;
             t.prefetch_gv(t.rowN);  // phase 1 consumed log_g and v
-        }
-        const bool slow = t.phase2();
-        if (more) t.prefetch_qk(t.rowN);  // phase 2 consumed q and k
-        __syncthreads();  // B2: K^
-        if (!slow)
-            t.compute();
-        else
-            t.serial();
-        t.epilogue();
-        if (more) {
+            const bool slow = t.phase2();
+            t.prefetch_qk(t.rowN);  // phase 2 consumed q and k
+            __syncthreads();  // B2: K^
+            if (!slow)
+                t.compute();
+            else
+                t.serial();
+            t.epilogue();
             t.prefetch_z(t.rowN);
             t.rowC = t.rowN;
-        }
-        __syncthreads();  // B3: LDS is rewritten by the next chunk
-        if (last_in_seq) {
-            ch = 0;
-            ++bh;
-        } else {
-            ++ch;
+            __syncthreads();  // B3: LDS is rewritten by the next chunk
+            ch = last_in_seq ? 0 : ch + 1;
+            b = nb;
+            h = nh;
         }
     }
 }
@@ -587,8 +596,11 @@ __global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const 
 template <int DT, int DV>
 hipError_t launch_rows(const GlaArgs &a, const float *Sx, const MfmaPlan &po, const MfmaPlan &ps,
                        hipStream_t st) {
-    hipLaunchKernelGGL((k_rows<DT, DV>), dim3(static_cast<unsigned>(po.n_wg)), dim3(NT), 0, st, a, Sx,
-                       po, ps);
+    const dim3 grid(static_cast<unsigned>(po.n_wg));
+    if (a.resid)
+        hipLaunchKernelGGL((k_rows<DT, DV, true>), grid, dim3(NT), 0, st, a, Sx, po, ps);
+    else
+        hipLaunchKernelGGL((k_rows<DT, DV, false>), grid, dim3(NT), 0, st, a, Sx, po, ps);
     return hipGetLastError();
 }
 

@@ -1,0 +1,371 @@
+// k_sum.hip -- segment summaries with per-wave partial sums (16-bit I/O, dk = 64,
+// dv = 64, chunk 64).
+//
+// GTR write-up ("端侧实时感知新标杆！通用线性骨干网络GTR开源"), Method §4
+// "硬件感知分块推理算子": the chunk summaries that the boundary-state scan
+// combines, formed on the matrix units.  For a segment (consecutive chunks of
+// one sequence) the summary is the state its tokens build from zero,
+//   U = sum_t (prod_{s > t in segment} g_s) k_t v_t^T,
+// and its summed log2-gate.  A workgroup walks its chunks last to first, so the
+// decay from a token to the segment's end is known when the token is reached:
+// with R the summed log2-gate of the segment's later chunks, G the chunk's and
+// a_t the in-chunk inclusive cumulative one, token t enters as
+//   k_t 2^(R + G - a_t) v_t^T,
+// and the factor never exceeds 1, so k 2^(...) is held as hi + lo of the I/O
+// type (fp16 or bf16), v enters the products as stored, and the sums need no
+// rescaling.
+//
+// The sum over a chunk's tokens is split by token: wave w takes tokens
+// [16 w, 16 w + 16) of every chunk and keeps its own partial U (all dk x dv
+// entries, in MFMA accumulators).  Its operands K~^T and V (16 tokens each) go
+// through a wave-private LDS area and come back with the transposing load as
+// 16x16x16 MFMA operands, so the only cross-wave exchange per chunk is the
+// sub-block gate totals (one barrier).  At a segment's end the four partials
+// are added through LDS.
+#include <type_traits>
+
+#include "mfma_common.hpp"
+
+namespace gtr {
+namespace {
+
+using namespace mf;
+
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+
+// D += A B, 16x16x16, raw 16-bit operands (4 per lane)
+template <bool F16>
+__device__ __forceinline__ f32x4 mma16(s16x4 a, s16x4 b, f32x4 c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int DT, int DV, bool RES>
+struct SumTile {
+    static constexpr bool F16 = DT == DT_F16;
+    static constexpr int C = 64, NB = 4;
+    static constexpr int ND = DV / 16;  // value tiles
+    static constexpr int NE = DV / 32;  // 16-byte value pieces per lane
+    static constexpr int VP = DV / 64;  // 64-column planes of V
+    static constexpr int SUB = 16 * 64;  // elements of one [16 tokens][64 columns] matrix
+    // LDS (bytes): per wave K~ hi, lo and V ([16][64] each, V per plane); gate
+    // totals (two chunk buffers); per-wave tables.  The segment-end reduction
+    // reuses the start of the area for the four [64][64] fp32 partials.
+    static constexpr int WAVE_BYTES = (2 + VP) * SUB * 2;
+    static constexpr int O_W = 0;
+    static constexpr int O_TOT = O_W + 4 * WAVE_BYTES;      // float [2][NB][DK]
+    static constexpr int O_TAB = O_TOT + 2 * NB * DK * 4;   // float [4 waves][2][DK]
+    static constexpr int BYTES_MAIN = O_TAB + 4 * 2 * DK * 4;
+    static constexpr int RED_BYTES = 4 * 64 * 68 * 4;       // one 64-column plane at a time
+    static constexpr int BYTES = BYTES_MAIN > RED_BYTES ? BYTES_MAIN : RED_BYTES;
+
+    GlaArgs a;
+    char *smem;
+    uint16_t *sKh, *sKl, *sV;
+    float *sTab;
+    int w, l, lr, g;
+    // inputs of the next two chunks (register sets alternate by chunk); pr: the
+    // previous block's output, added to v where v is consumed
+    uint4 pk[2][2], pv[2][NE], pr[2][RES ? NE : 1];
+    float4 pg[2][4];
+    float cs[16];
+    f32x4 U[4][ND];  // U[ct][dt][r] = partial U[16 ct + 4 g + r][16 dt + lr]
+    float R;         // summed log2-gate of the segment's chunks after this one, channel l
+
+    __device__ __forceinline__ void init(const GlaArgs &args, char *sm) {
+        a = args;
+        smem = sm;
+        const int tid = threadIdx.x;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        l = tid & 63;
+        lr = l & 15;
+        g = l >> 4;
+        uint16_t *base = reinterpret_cast<uint16_t *>(sm + O_W + w * WAVE_BYTES);
+        sKh = base;
+        sKl = base + SUB;
+        sV = base + 2 * SUB;
+        sTab = reinterpret_cast<float *>(sm + O_TAB) + w * 2 * DK;
+    }
+
+    // row ((b L + grid position) H + h) of this lane's token of chunk ch of
+    // sequence (b, h); a token past the end of the sequence takes the last token's
+    // row (its values reach only the sequence's final state, which is never used)
+    __device__ __forceinline__ int64_t row_of(uint32_t b, uint32_t h, int64_t ch) const {
+        const uint32_t L32 = static_cast<uint32_t>(a.L);
+        const uint32_t t0 = static_cast<uint32_t>(ch) * C + 16 * w + lr;
+        uint32_t t = t0 < L32 ? t0 : L32 - 1;
+        if (a.direction & 1) t = L32 - 1 - t;
+        uint32_t pos = t;
+        if (a.direction >= 2) {
+            const uint32_t gh = static_cast<uint32_t>(a.gh);
+            const uint32_t c = t / gh;
+            pos = (t - c * gh) * static_cast<uint32_t>(a.gw) + c;
+        }
+        return (static_cast<int64_t>(b) * a.L + pos) * a.H + h;
+    }
+
+    template <int S>
+    __device__ __forceinline__ void prefetch_g(int64_t row) {
+#pragma unroll
+        for (int kap = 0; kap < 2; ++kap) {
+            const int c0 = 32 * kap + 8 * g;
+            pg[S][2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
+            pg[S][2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
+        }
+    }
+
+    template <int S>
+    __device__ __forceinline__ void prefetch_kv(int64_t row) {
+#pragma unroll
+        for (int kap = 0; kap < 2; ++kap)
+            pk[S][kap] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + row * DK +
+                                                       32 * kap + 8 * g);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int d0 = 32 * e + 8 * g;
+            pv[S][e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + row * DV + d0);
+            if constexpr (RES)
+                pr[S][e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.resid) + row * DV + d0);
+        }
+    }
+
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) U[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        R = 0.f;
+    }
+
+    // cumulative gates of the wave's tokens (natural-log units) and the sub-block
+    // totals into buffer buf
+    template <int buf>
+    __device__ __forceinline__ void gates() {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            cs[4 * q4] = pg[buf][q4].x; cs[4 * q4 + 1] = pg[buf][q4].y;
+            cs[4 * q4 + 2] = pg[buf][q4].z; cs[4 * q4 + 3] = pg[buf][q4].w;
+        }
+        row_scan(cs);
+        if (lr == 15) {
+            float *tot = reinterpret_cast<float *>(smem + O_TOT) + (buf * NB + w) * DK;
+#pragma unroll
+            for (int kap = 0; kap < 2; ++kap) {
+                float *dst = tot + 32 * kap + 8 * g;
+                *reinterpret_cast<float4 *>(dst) =
+                    make_float4(cs[8 * kap], cs[8 * kap + 1], cs[8 * kap + 2], cs[8 * kap + 3]);
+                *reinterpret_cast<float4 *>(dst + 4) =
+                    make_float4(cs[8 * kap + 4], cs[8 * kap + 5], cs[8 * kap + 6], cs[8 * kap + 7]);
+            }
+        }
+    }
+
+    // (after the barrier) the table, K~ = k 2^(R + G - a) and V into the wave's LDS area
+    template <int buf>
+    __device__ __forceinline__ void stage() {
+        const float *tot = reinterpret_cast<const float *>(smem + O_TOT) + buf * NB * DK;
+        float r_l = 0.f, tot_l = 0.f;
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+            const float t = tot[J * DK + l];
+            if (J < w) r_l += t;
+            tot_l += t;
+        }
+        tot_l *= kLog2e;
+        sTab[l] = R + tot_l - r_l * kLog2e;  // R + G - r (log2), channel l
+        R += tot_l;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int kap = 0; kap < 2; ++kap) {
+            const int c0 = 32 * kap + 8 * g;
+            float gr[8], kt[8];
+#pragma unroll
+            for (int h4 = 0; h4 < 2; ++h4) {
+                const float4 x = *reinterpret_cast<const float4 *>(sTab + c0 + 4 * h4);
+                gr[4 * h4] = x.x; gr[4 * h4 + 1] = x.y; gr[4 * h4 + 2] = x.z; gr[4 * h4 + 3] = x.w;
+            }
+            unpack8<DT>(pk[buf][kap], kt);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) kt[s] *= fexp2(fmaf(-cs[8 * kap + s], kLog2e, gr[s]));
+            uint32_t hi[4], lo[4];
+            split_pk<F16>(kt, hi, lo);
+            const int off = swn(lr, c0);
+            *reinterpret_cast<uint4 *>(sKh + off) = u4(hi);
+            *reinterpret_cast<uint4 *>(sKl + off) = u4(lo);
+        }
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int d0 = 32 * e + 8 * g;
+            uint4 x = pv[buf][e];
+            if constexpr (RES) x = add_io<DT>(x, pr[buf][e]);  // stack residual
+            *reinterpret_cast<uint4 *>(sV + (d0 >> 6) * SUB + swn(lr, d0 & 63)) = x;
+        }
+    }
+
+    // transposing read of a [16 tokens][64] matrix: lane column cb + lr, tokens
+    // 4 g .. 4 g + 3 (the k slots of a 16x16x16 operand)
+    __device__ __forceinline__ s16x4 op16(const uint16_t *m, int cb) const {
+        return ld_tr(m + swn(4 * g + (lr >> 2), cb + 4 * (lr & 3)));
+    }
+
+    // U += K~^T V over the wave's 16 tokens
+    __device__ __forceinline__ void accumulate() {
+        s16x4 bv[ND];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) bv[dt] = op16(sV + (dt >> 2) * SUB, 16 * (dt & 3));
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const s16x4 ah = op16(sKh, 16 * ct);
+            const s16x4 al = op16(sKl, 16 * ct);
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) {
+                U[ct][dt] = mma16<F16>(ah, bv[dt], U[ct][dt]);
+                U[ct][dt] = mma16<F16>(al, bv[dt], U[ct][dt]);
+            }
+        }
+    }
+
+    // segment end: the four partials added through LDS, one 64-column plane at a
+    // time ([wave][column][channel], rows padded to 68 floats); wave w then sums
+    // channels [16 w, 16 w + 16) for every column (lane = column) and stores them
+    // as whole 256-byte rows
+    __device__ __forceinline__ void finish(float *dst, float *gdst) {
+        constexpr int RS = 68;
+        float *red = reinterpret_cast<float *>(smem);  // [4][64 columns][RS]
+#pragma unroll
+        for (int pl = 0; pl < VP; ++pl) {
+            __syncthreads();  // the LDS area is free (operands, previous plane)
+            {
+                float *m = red + w * 64 * RS + lr * RS + 4 * g;
+#pragma unroll
+                for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        *reinterpret_cast<f32x4 *>(m + 16 * d4 * RS + 16 * ct) = U[ct][4 * pl + d4];
+            }
+            __syncthreads();
+            const float *m = red + l * RS + 16 * w;
+            float sum[16];
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                f32x4 x = *reinterpret_cast<const f32x4 *>(m + 4 * j4);
+#pragma unroll
+                for (int q = 1; q < 4; ++q) {
+                    const f32x4 y = *reinterpret_cast<const f32x4 *>(m + q * 64 * RS + 4 * j4);
+                    x[0] += y[0]; x[1] += y[1]; x[2] += y[2]; x[3] += y[3];
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sum[4 * j4 + r] = x[r];
+            }
+            float *o = dst + (16 * w) * DV + 64 * pl + l;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[j * DV] = sum[j];
+        }
+        if (w == 0) gdst[l] = R;
+        __syncthreads();  // the LDS area is rewritten by the next chunk
+    }
+};
+
+template <int DT, int DV, bool RES>
+__global__ __launch_bounds__(NT, 2) void k_sum(GlaArgs a, float *__restrict__ Uo, float *__restrict__ Gs,
+                                              MfmaPlan pl) {
+    using T = SumTile<DT, DV, RES>;
+    __shared__ __attribute__((aligned(16))) char smem[T::BYTES];
+    T t;
+    t.init(a, smem);
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * pl.Q;
+    const int64_t p1 = (p0 + pl.Q < pl.T) ? p0 + pl.Q : pl.T;
+    if (p0 >= p1) return;  // the whole workgroup
+
+    // Chunks last to first.  Cursors (b, h, ch): the current chunk's image, head and
+    // index in its sequence; (fb, fh, fch): the chunk two before it, whose inputs
+    // are loaded while the current one is worked on (register set = chunk parity,
+    // which also picks the gate-total buffer).  Tracked incrementally: no divisions
+    // in the loop.
+    struct Cur {
+        uint32_t b, h;
+        int64_t ch;
+    };
+    const int64_t bh1 = (p1 - 1) / pl.N;
+    Cur cur{static_cast<uint32_t>(bh1 / a.H), static_cast<uint32_t>(bh1 % a.H), (p1 - 1) - bh1 * pl.N};
+    Cur far = cur;
+    auto back = [&](Cur &c) {
+        if (c.ch == 0) {
+            c.ch = pl.N - 1;
+            if (c.h == 0) {
+                c.h = static_cast<uint32_t>(a.H) - 1;
+                --c.b;
+            } else {
+                --c.h;
+            }
+        } else {
+            --c.ch;
+        }
+    };
+    {
+        const int64_t row = t.row_of(far.b, far.h, far.ch);
+        t.template prefetch_g<0>(row);
+        t.template prefetch_kv<0>(row);
+        back(far);
+        const int64_t row1 = (p1 - 2 >= p0) ? t.row_of(far.b, far.h, far.ch) : row;
+        t.template prefetch_g<1>(row1);
+        t.template prefetch_kv<1>(row1);
+        back(far);  // now two before the current chunk
+    }
+    t.zero();
+    auto step = [&](auto S_, int64_t p) {
+        constexpr int S = decltype(S_)::value;
+        // Loads are issued every step (past the range's first chunk they re-read
+        // the current chunk's rows, unused), so that the wait-count bookkeeping
+        // sees the same load sequence each time and never has to drain the queue.
+        const bool ahead = p - 2 >= p0;
+        const int64_t row = ahead ? t.row_of(far.b, far.h, far.ch) : t.row_of(cur.b, cur.h, cur.ch);
+        t.template gates<S>();
+        t.template prefetch_g<S>(row);  // the gates are consumed
+        __syncthreads();  // the chunk's sub-block totals
+        t.template stage<S>();
+        t.template prefetch_kv<S>(row);  // k and v are consumed
+        t.accumulate();
+        if (p == p0 || cur.ch == 0) {  // the segment's first chunk: its summary is complete
+            const int64_t sid = seg_id(p, pl);
+            t.finish(Uo + sid * DK * DV, Gs + sid * DK);
+            t.zero();
+        }
+        back(cur);
+        if (ahead) back(far);
+    };
+    for (int64_t p = p1 - 1; p >= p0; p -= 2) {
+        step(std::integral_constant<int, 0>{}, p);
+        if (p - 1 < p0) break;
+        step(std::integral_constant<int, 1>{}, p - 1);
+    }
+}
+
+template <int DT, int DV>
+hipError_t launch_sum(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(ps.n_wg));
+    if (a.resid)
+        hipLaunchKernelGGL((k_sum<DT, DV, true>), grid, dim3(NT), 0, st, a, U, G, ps);
+    else
+        hipLaunchKernelGGL((k_sum<DT, DV, false>), grid, dim3(NT), 0, st, a, U, G, ps);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool sum_supported(const GlaArgs &a) {
+    // dv = 128 would need more registers than two workgroups per CU allow
+    return (a.dtype == DT_F16 || a.dtype == DT_BF16) && a.dk == DK && a.dv == 64 && a.chunk == 64;
+}
+
+hipError_t sum_launch(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t s) {
+    if (a.dv != 64) return hipErrorInvalidValue;
+    if (a.dtype == DT_F16) return launch_sum<DT_F16, 64>(a, ps, U, G, s);
+    if (a.dtype == DT_BF16) return launch_sum<DT_BF16, 64>(a, ps, U, G, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gtr

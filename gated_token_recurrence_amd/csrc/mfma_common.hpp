@@ -157,6 +157,22 @@ template <> __device__ __forceinline__ uint32_t f2h<DT_F16>(float x) {
 }
 template <> __device__ __forceinline__ uint32_t f2h<DT_BF16>(float x) { return f32_to_bf16(x); }
 
+// x + y element-wise on eight 16-bit values of the I/O type, each sum rounded to
+// the I/O type (the stack residual v + out_prev)
+template <int DT>
+__device__ __forceinline__ uint4 add_io(const uint4 &x, const uint4 &y) {
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+    const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t lo = f2h<DT>(h2f<DT>(xs[u] & 0xffffu) + h2f<DT>(ys[u] & 0xffffu));
+        const uint32_t hi = f2h<DT>(h2f<DT>(xs[u] >> 16) + h2f<DT>(ys[u] >> 16));
+        o[u] = lo | (hi << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __device__ __forceinline__ uint32_t half16(const uint4 &u, int s) {
     const uint32_t w = (s < 2) ? u.x : (s < 4) ? u.y : (s < 6) ? u.z : u.w;
     return (s & 1) ? (w >> 16) : (w & 0xffffu);
