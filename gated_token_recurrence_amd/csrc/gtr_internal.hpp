@@ -122,6 +122,11 @@ constexpr int64_t kMfmaWorkgroups = 512;      // output kernel: two per CU on 25
 constexpr int64_t kSummaryWorkgroups = 512;   // summary kernel (finer ranges only lengthen the scan)
 
 __host__ __device__ __forceinline__ int64_t seg_id(int64_t p, const MfmaPlan &pl) {
+    if (p < (int64_t{1} << 31) && pl.lcm < (int64_t{1} << 31)) {  // every sum below 2^32
+        const uint32_t u = static_cast<uint32_t>(p), n = static_cast<uint32_t>(pl.N),
+                       q = static_cast<uint32_t>(pl.Q), m = static_cast<uint32_t>(pl.lcm);
+        return static_cast<int64_t>((u + n - 1) / n + (u + q - 1) / q) - (u + m - 1) / m;
+    }
     return (p + pl.N - 1) / pl.N + (p + pl.Q - 1) / pl.Q - (p + pl.lcm - 1) / pl.lcm;
 }
 

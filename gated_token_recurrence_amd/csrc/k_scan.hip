@@ -119,13 +119,14 @@ __global__ __launch_bounds__(NT) void k_scan_rows(float *__restrict__ U,
                                                   int dk, int dv) {
     __shared__ float sA[4][64], sB[4][64];
     const int64_t dd = static_cast<int64_t>(dk) * dv;
-    const int64_t slices = dd / 64;
-    const int64_t seq = blockIdx.x / slices;
+    const uint32_t slices = static_cast<uint32_t>(dk * dv / 64);  // 32-bit: no long division
+    const uint32_t seq32 = blockIdx.x / slices;
+    const int64_t seq = seq32;
     const int lane = threadIdx.x & 63;
     const int part = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int64_t el0 = (blockIdx.x - seq * slices) * 64;
+    const uint32_t el0 = (blockIdx.x - seq32 * slices) * 64;
     const int64_t el = el0 + lane;
-    const int c = static_cast<int>(el0 / dv);  // the slice's key channel
+    const int c = static_cast<int>(el0 / static_cast<uint32_t>(dv));  // the slice's key channel
     const int64_t s0 = seg_id(seq * pl.N, pl), s1 = seg_id((seq + 1) * pl.N, pl);
     const int64_t len = (s1 - s0 + 3) / 4;  // <= M (checked by the host)
     const int64_t kb = s0 + part * len;
