@@ -301,9 +301,11 @@ def profile_run(w, dev, sp, steps, path, chunk):
         f"calibration copy {COPY_BYTES} bytes")
 
 
-KERNEL_KEYS = {  # launch name -> substring of the kernel symbol
-    "segment_summary": "true>", "chunk_output": "false>", "state_scan": "state_scan",
-    "fast_single_launch": "k_fast",
+KERNEL_KEYS = {  # launch name -> test on the kernel symbol
+    "segment_summary": lambda n: "k_sum<" in n or ("k_chunk<" in n and "true>" in n),
+    "chunk_output": lambda n: "k_rows<" in n or ("k_chunk<" in n and "false>" in n),
+    "state_scan": lambda n: "scan" in n,
+    "fast_single_launch": lambda n: "k_fast" in n,
 }
 
 
@@ -320,7 +322,8 @@ def _counter_values(csv_path):
 
 
 def _find(vals, counter, key, reduce):
-    hits = [v for (kn, c), v in vals.items() if c == counter and key in kn]
+    match = key if callable(key) else (lambda n: key in n)
+    hits = [v for (kn, c), v in vals.items() if c == counter and match(kn)]
     if len(hits) != 1:
         raise SystemExit(f"expected one kernel matching {key!r} for {counter}, found {len(hits)}")
     return reduce(hits[0])
