@@ -23,6 +23,14 @@ Recipe (per workload, per block of a stack):
   rms_w = 1 (tiny workload) or 1 + 0.1 * N(0, 1)
   saturated (wide mixer only): round(0.1 * H * dk) of the (h, c) key channels,
   chosen without replacement, get log_g = -1e-4 * U[0, 1) for every token.
+
+Low-rank gate inputs (the gate formed inside the library from rank-r
+features; GTR paper, Method §1):
+  seed = 1000 * workload_id + 500 + block; draw order: q, k, v, z, feat,
+  gate_w, gate_b, rms_w
+  feat ~ N(0, 1) [B, grid_h, grid_w, r] and gate_w ~ N(0, 1) / sqrt(r)
+  [r, H * dk], both rounded to the I/O type; gate_b ~ N(0, 0.5^2) float32
+  [H * dk], plus an optional per-channel shift; tau = 16, r = 16.
 """
 from __future__ import annotations
 
@@ -69,6 +77,15 @@ class Workload:
         if residual:
             per += self.dv * s
         return self.B * self.L * self.H * per + 4 * self.dv
+
+    def compulsory_bytes_lowrank(self, rank: int = 16) -> int:
+        """Bytes of one call with the gate formed from rank-r features: q, k, v, z
+        read and out written per token-head, the features per token, the
+        projection and bias once."""
+        s = DTYPE_BYTES[self.dtype]
+        per_th = (2 * self.dk + 3 * self.dv) * s
+        return (self.B * self.L * (self.H * per_th + rank * s)
+                + rank * self.H * self.dk * s + 4 * self.H * self.dk + 4 * self.dv)
 
     def algorithmic_flops(self, chunk: int | None = None) -> int:
         """Chunkwise work: K^T V summary, Q.S_prev, causal scores and P.V."""
@@ -177,6 +194,39 @@ def make_custom(B: int, grid_h: int, grid_w: int, H: int, dk: int, dv: int, dtyp
     out["rms_w"] = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
     out["_workload"] = w
     return out
+
+
+def make_lowrank(B: int, grid_h: int, grid_w: int, H: int, dk: int, dv: int, dtype: str,
+                 seed: int, rank: int = 16, tau: float = 16.0, scale: float = 0.125,
+                 feat_scale: float = 1.0, bias_shift=None) -> dict:
+    """Inputs of a call whose gate comes from rank-r features.
+
+    ``bias_shift``: optional float array [H * dk] added to gate_b (saturated
+    channels take a large positive shift, fast-decaying ones a negative one).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    qk_shape = (B, grid_h, grid_w, H, dk)
+    v_shape = (B, grid_h, grid_w, H, dv)
+    out = {}
+    for name, shape in (("q", qk_shape), ("k", qk_shape), ("v", v_shape), ("z", v_shape)):
+        out[name] = cast_io(rng.standard_normal(shape) * scale, dtype)
+    out["feat"] = cast_io(rng.standard_normal((B, grid_h, grid_w, rank)) * feat_scale, dtype)
+    out["gate_w"] = cast_io(rng.standard_normal((rank, H * dk)) / math.sqrt(rank), dtype)
+    b = rng.standard_normal(H * dk) * 0.5
+    if bias_shift is not None:
+        b = b + np.asarray(bias_shift, dtype=np.float64)
+    out["gate_b"] = b.astype(np.float32)
+    out["tau"] = float(tau)
+    out["rms_w"] = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
+    return out
+
+
+def make_lowrank_inputs(w: Workload, block: int = 0, rank: int = 16, tau: float = 16.0,
+                        B: int | None = None) -> dict:
+    """A workload's shapes with low-rank gate inputs (seed 1000 * id + 500 + block)."""
+    Bn = w.B if B is None else B
+    return make_lowrank(Bn, w.grid_h, w.grid_w, w.H, w.dk, w.dv, w.dtype,
+                        seed=1000 * w.wid + 500 + block, rank=rank, tau=tau, scale=w.scale)
 
 
 def rotation_sets(bytes_per_set: int, min_total: int = 512 << 20) -> int:

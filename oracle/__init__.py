@@ -11,6 +11,12 @@ block i scans in direction (first + i) mod 4 (Method §1: LR, RL, TB, BT cycle
 with depth) and takes ``v_i + out_{i-1}``, rounded to the I/O type, as its
 value input (the residual feed of the stacked workload).
 
+``lowrank_log_g`` forms the forget gate from rank-r gate features (Method §1:
+a light low-rank projection of the input with a temperature; rank and
+temperature are lost on the page, the library takes them as arguments):
+x = feat W + b per head channel, log g = logsigmoid(x) / tau.  ``fwd_lowrank``
+is ``fwd`` with that gate.
+
 ``round_io`` is this package's own IEEE round-to-nearest-even to the I/O type.
 """
 from __future__ import annotations
@@ -93,6 +99,38 @@ def fwd(q, k, v, log_g, z, rms_w, direction: int, eps: float = RMS_EPS,
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments")
     return out
+
+
+# ------------------------------------------------------------ low-rank gate --
+def logsigmoid(x) -> np.ndarray:
+    """log(1 / (1 + exp(-x))) in float64, without overflow for either sign:
+    log sigma(x) = min(x, 0) - log(1 + exp(-|x|))."""
+    x = _f64(x)
+    return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+
+def lowrank_log_g(feat, gate_w, gate_b, tau: float, H: int, dk: int) -> np.ndarray:
+    """Forget gate from rank-r features (Method §1, the gate projection).
+
+    feat: [B, gh, gw, r] (one feature vector per token, shared by the heads);
+    gate_w: [r, H*dk]; gate_b: [H*dk]; tau > 0.  Head h, key channel c takes
+    column h*dk + c:  log_g[..., h, c] = logsigmoid(feat . gate_w[:, h*dk + c]
+    + gate_b[h*dk + c]) / tau.  Returns float64 [B, gh, gw, H, dk].
+    """
+    feat, gate_w, gate_b = _f64(feat), _f64(gate_w), _f64(gate_b)
+    r = feat.shape[-1]
+    if gate_w.shape != (r, H * dk) or gate_b.shape != (H * dk,) or not tau > 0:
+        raise ValueError("gate shapes or temperature")
+    x = feat @ gate_w + gate_b                      # [B, gh, gw, H*dk]
+    return (logsigmoid(x) / float(tau)).reshape(feat.shape[:-1] + (H, dk))
+
+
+def fwd_lowrank(q, k, v, feat, gate_w, gate_b, tau, z, rms_w, direction: int,
+                eps: float = RMS_EPS, bh=None) -> np.ndarray:
+    """``fwd`` with the gate formed by ``lowrank_log_g`` (never rounded)."""
+    H, dk = q.shape[3], q.shape[4]
+    return fwd(q, k, v, lowrank_log_g(feat, gate_w, gate_b, tau, H, dk), z, rms_w,
+               direction, eps=eps, bh=bh)
 
 
 # ------------------------------------------------------------------ rounding --
