@@ -176,6 +176,67 @@ def time_workload(w, dev, hip, stream_ptr, steps, warmup, path, chunk, direction
     return x, res
 
 
+def _io_tensor(a, dtype):
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" \
+        else torch.from_numpy(a)
+
+
+def time_lowrank(w, dev, hip, stream_ptr, steps, warmup, chunk, direction=0, rank=16):
+    """Whole-call and per-launch timing of gtr_gla_lowrank_fwd on the workload's shapes
+    with rank-r gate features (rotating buffer sets, as for the main workload)."""
+    lib = _lib.load()
+    x = W.make_lowrank_inputs(w, rank=rank)
+    per_set = w.compulsory_bytes_lowrank(rank)
+    n_sets = W.rotation_sets(per_set)
+    base = {key: _io_tensor(x[key], w.dtype) for key in ("q", "k", "v", "z", "feat", "gate_w")}
+    base["gate_b"] = torch.from_numpy(x["gate_b"])
+    base["rms_w"] = torch.from_numpy(x["rms_w"])
+    sets = []
+    for _ in range(n_sets):
+        st = {key: val.to(dev) for key, val in base.items()}
+        st["out"] = torch.empty_like(st["v"])
+        sets.append(st)
+    torch.cuda.synchronize(dev)
+
+    def run(s, events=None, n_events=0, nl=None):
+        st = lib.gtr_gla_lowrank_fwd(
+            s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(), s["feat"].data_ptr(),
+            s["gate_w"].data_ptr(), s["gate_b"].data_ptr(), x["tau"], rank, s["z"].data_ptr(),
+            s["rms_w"].data_ptr(), s["out"].data_ptr(), w.B, w.H, w.grid_h, w.grid_w, w.dk,
+            w.dv, direction, chunk, W.DTYPE_CODE[w.dtype], g.PATH_AUTO, events, n_events, nl,
+            stream_ptr)
+        _lib.check(st)
+
+    for i in range(warmup):
+        run(sets[i % n_sets])
+    torch.cuda.synchronize(dev)
+    ev = hip.events(2)
+    hip.record(ev[0], stream_ptr)
+    for i in range(steps):
+        run(sets[i % n_sets])
+    hip.record(ev[1], stream_ptr)
+    us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+    torch.cuda.synchronize(dev)
+    hip.destroy(ev)
+    nl = ctypes.c_int(0)
+    probe = hip.events(8)
+    run(sets[0], probe, 8, ctypes.byref(nl))
+    torch.cuda.synchronize(dev)
+    hip.destroy(probe)
+    n_ev = nl.value + 1
+    evs = [hip.events(n_ev) for _ in range(steps)]
+    for i in range(steps):
+        run(sets[i % n_sets], evs[i], n_ev, None)
+    torch.cuda.synchronize(dev)
+    per = [[hip.elapsed_ms(e[j], e[j + 1]) * 1e3 for j in range(n_ev - 1)] for e in evs]
+    for e in evs:
+        hip.destroy(e)
+    del sets
+    torch.cuda.empty_cache()
+    return {"us_per_call": us, "n_sets": n_sets, "launches": nl.value,
+            "launch_us_mean": [statistics.fmean(p[j] for p in per) for j in range(n_ev - 1)]}
+
+
 def graph_time(lib, w, sets, n_sets, dev, direction, chunk, path, steps):
     """hipGraph replay of one call per buffer set (the pages' own kernel benchmark
     used graph launch); microseconds per call."""
@@ -447,6 +508,28 @@ def main():
                               "path": PATH_NAMES[pe]}
                 log(f"  {key}: {r['us_per_call']:.2f} us/call, graph {r['us_per_call_graph']}"
                     f"{' (' + r['graph_error'] + ')' if r.get('graph_error') else ''}")
+    lowrank = None
+    if not args.no_extra and w.dtype != "f32":
+        # the same shapes with the gate formed from rank-16 features inside the kernels
+        try:
+            r = time_lowrank(w, dev, hip, sp, args.steps, args.warmup, chunk)
+            lb = w.compulsory_bytes_lowrank(16)
+            lnames = (LAUNCH_NAMES[pname] if r["launches"] == 3
+                      else ("gate_projection",) + tuple(LAUNCH_NAMES[pname]))
+            lowrank = {"workload": f"{w.name} shapes, log_g formed from rank-16 fp16 gate "
+                                   f"features (tau 16) in the kernels",
+                       "us_per_call": round(r["us_per_call"], 3),
+                       "tokens_per_s": round(w.tokens / (r["us_per_call"] * 1e-6), 1),
+                       "algorithmic_bytes": lb,
+                       "whole_call_frac": round(lb / (r["us_per_call"] * 1e-6) / 1e9
+                                                / HBM_PEAK_GBS, 4),
+                       "launch_us_mean": {n: round(t, 3) for n, t in
+                                          zip(lnames, r["launch_us_mean"])},
+                       "rotating_sets": r["n_sets"]}
+            log(f"  lowrank gate: {r['us_per_call']:.2f} us/call, launches "
+                f"{['%.2f' % t for t in r['launch_us_mean']]}")
+        except Exception as exc:  # report, do not hide
+            lowrank = {"error": str(exc)[:300]}
     cpu = None
     if not args.no_cpu:
         log("  timing the fp64 oracle on the host (bounded sample)")
@@ -482,6 +565,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra_1p6k": extra,
+        "lowrank_gate": lowrank,
     }
     print(json.dumps(line), flush=True)
 

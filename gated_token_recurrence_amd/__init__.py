@@ -3,7 +3,8 @@
 Python binding of libgtrscan (``include/gtrscan.h``).  torch supplies device
 memory and the current stream; the mixer itself runs in the library's HIP
 kernels.  ``gla_fwd`` is one block's mixer call, ``gla_stack_fwd`` a stack of
-blocks with the direction cycle and the residual feed.
+blocks with the direction cycle and the residual feed, ``gla_lowrank_fwd`` a
+mixer call whose forget gate the library forms from rank-r gate features.
 """
 from __future__ import annotations
 
@@ -12,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import (GtrError, PATH_AUTO, PATH_FAST, PATH_MFMA, PATH_SERIAL)  # noqa: F401
 
-__all__ = ["gla_fwd", "gla_stack_fwd", "GtrError", "DIRECTIONS", "dtype_code", "version"]
+__all__ = ["gla_fwd", "gla_stack_fwd", "gla_lowrank_fwd", "GtrError", "DIRECTIONS", "dtype_code", "version"]
 
 DIRECTIONS = {"LR": 0, "RL": 1, "TB": 2, "BT": 3}
 _DT = {torch.float32: _lib.GTR_F32, torch.float16: _lib.GTR_F16, torch.bfloat16: _lib.GTR_BF16}
@@ -107,3 +108,49 @@ def gla_stack_fwd(q, k, v, log_g, z, rms_w, first_direction=0, chunk: int = 0, o
                                    dtype_code(q.dtype), _stream_ptr(dev))
     _lib.check(st)
     return out
+
+
+def gla_lowrank_fwd(q, k, v, feat, gate_w, gate_b, tau: float, z, rms_w, direction=0,
+                    chunk: int = 0, path: int = PATH_AUTO, out=None, events=None):
+    """One mixer call with the gate log g = logsigmoid(feat . gate_w + gate_b) / tau.
+
+    feat: [B, gh, gw, r] and gate_w: [r, H*dk] of the I/O dtype; gate_b: [H*dk]
+    float32; the rest as ``gla_fwd``.  ``events``: optional list of HIP event
+    handles (ints) recorded around the launches.  Returns (out, n_launches).
+    """
+    import ctypes
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    B, gh, gw, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, gh, gw, H, dv) or z.shape != v.shape:
+        raise ValueError("k must have q's shape; v, z must be [B, gh, gw, H, dv]")
+    r = feat.shape[-1]
+    if feat.shape != (B, gh, gw, r) or gate_w.shape != (r, H * dk) or gate_b.shape != (H * dk,):
+        raise ValueError("feat [B, gh, gw, r], gate_w [r, H*dk], gate_b [H*dk] expected")
+    if rms_w.shape != (dv,):
+        raise ValueError("rms_w must be [dv]")
+    if not (q.dtype == k.dtype == v.dtype == z.dtype == feat.dtype == gate_w.dtype):
+        raise TypeError("q, k, v, z, feat, gate_w must share one dtype")
+    if gate_b.dtype != torch.float32 or rms_w.dtype != torch.float32:
+        raise TypeError("gate_b and rms_w must be float32")
+    if out is None:
+        out = torch.empty_like(v)
+    _check_tensors((("q", q), ("k", k), ("v", v), ("feat", feat), ("gate_w", gate_w),
+                    ("gate_b", gate_b), ("z", z), ("rms_w", rms_w), ("out", out)), dev)
+    if out.shape != v.shape or out.dtype != v.dtype:
+        raise ValueError("out must match v")
+    n_ev = 0 if events is None else len(events)
+    ev_arr = (ctypes.c_void_p * max(1, n_ev))(*(events or []))
+    n_launch = ctypes.c_int(0)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        st = lib.gtr_gla_lowrank_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), feat.data_ptr(),
+                                     gate_w.data_ptr(), gate_b.data_ptr(), float(tau), r,
+                                     z.data_ptr(), rms_w.data_ptr(), out.data_ptr(), B, H, gh, gw,
+                                     dk, dv, _dir(direction), int(chunk), dtype_code(q.dtype),
+                                     int(path), ev_arr, n_ev, ctypes.byref(n_launch),
+                                     _stream_ptr(dev))
+    _lib.check(st)
+    return out, n_launch.value

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <map>
@@ -45,13 +46,16 @@ struct Workspace {
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// log_g written out by the low-rank gate kernel (kept apart from the states)
+std::map<std::pair<int, hipStream_t>, Workspace> g_gws;
 
-gtr_status workspace(hipStream_t stream, size_t bytes, void **out) {
+gtr_status workspace(hipStream_t stream, size_t bytes, void **out,
+                     std::map<std::pair<int, hipStream_t>, Workspace> &pool = g_ws) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_ws_mu);
-    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    Workspace &w = pool[std::make_pair(dev, stream)];
     if (w.bytes < bytes) {
         if (w.ptr) {
             e = hipStreamSynchronize(stream);
@@ -157,6 +161,8 @@ struct Marks {
         return (ev && i < n) ? hipEventRecord(ev[i], st) : hipSuccess;
     }
     hipError_t after_launch(hipStream_t st) { return record(st, ++launches); }
+    // event 0, unless an earlier launch of the call already recorded it
+    hipError_t start(hipStream_t st) { return launches == 0 ? record(st, 0) : hipSuccess; }
 };
 
 constexpr int kDefaultChunk = 64;
@@ -175,7 +181,7 @@ gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk) {
     if (s != GTR_OK) return s;
     float *U = static_cast<float *>(ws);
     float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
-    hipError_t e = mk.record(st, 0);
+    hipError_t e = mk.start(st);
     if (e == hipSuccess) e = serial_summary(a, U, G, static_cast<int>(n_chunks), st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "chunk summary launch");
@@ -201,7 +207,7 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
     if (s != GTR_OK) return s;
     float *U = static_cast<float *>(ws);
     float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
-    hipError_t e = mk.record(st, 0);
+    hipError_t e = mk.start(st);
     if (e == hipSuccess) e = sum_supported(a) ? sum_launch(a, pl, U, G, st) : mfma_summary(a, pl, U, G, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "segment summary launch");
@@ -213,6 +219,17 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
     if (e != hipSuccess) return hip_fail(e, "chunk output launch");
     return GTR_OK;
 }
+
+}  // namespace
+
+// The summary and output kernels form the gate themselves for rank-16 features
+// at their one shape (16-bit I/O, dk = dv = 64, chunk 64), without a residual.
+bool gtr::lowrank_fused_supported(const GlaArgs &a) {
+    return a.feat && a.rank == kFusedGateRank && !a.resid && a.dtype != GTR_F32 &&
+           mfma_supported(a) && sum_supported(a) && rows_supported(a) && a.dv == 64;
+}
+
+namespace {
 
 // The single-launch path: batch one, at most kFastMaxTokens tokens.
 bool fast_ok(const GlaArgs &a) {
@@ -237,7 +254,7 @@ gtr_status run_fast(const GlaArgs &a, hipStream_t st, Marks &mk) {
     if (s != GTR_OK) return s;
     float *U = static_cast<float *>(ws);
     float *G = U + T * a.dk * a.dv;
-    hipError_t e = mk.record(st, 0);
+    hipError_t e = mk.start(st);
     if (e == hipSuccess) e = fast_launch(a, U, G, static_cast<unsigned *>(ctr), st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "single-launch kernel");
@@ -276,6 +293,55 @@ int device_ok() {
         return 0;
     }
     return 1;
+}
+
+gtr_status lowrank_impl(const void *q, const void *k, const void *v, const void *feat,
+                        const void *gate_w, const float *gate_b, float tau, int rank,
+                        const void *z, const float *rms_w, void *out, int B, int H, int gh,
+                        int gw, int dk, int dv, int direction, int chunk, int dtype, int path,
+                        hipStream_t stream, Marks &mk) {
+    g_err.clear();
+    if (!feat || !gate_w || !gate_b) return fail(GTR_ERR_ARG, "null gate pointer");
+    gtr_status s = check(q, k, v, gate_b, z, rms_w, out, B, H, gh, gw, dk, dv, direction, chunk,
+                         dtype, path);
+    if (s != GTR_OK) return s;
+    if (rank < 1 || rank > 256) return fail(GTR_ERR_ARG, "rank must be 1..256, got %d", rank);
+    if (!(std::isfinite(tau) && tau > 0.f))
+        return fail(GTR_ERR_ARG, "tau must be finite and positive, got %g", static_cast<double>(tau));
+    for (const void *p : {feat, gate_w, static_cast<const void *>(gate_b)})
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(GTR_ERR_ARG, "feat, gate_w and gate_b must be 16-byte aligned");
+    const size_t tokens = static_cast<size_t>(B) * gh * gw;
+    const size_t rows = tokens * H;
+    const size_t eb = elem_bytes(dtype);
+    const size_t hd = static_cast<size_t>(H) * dk;
+    const void *ins[] = {q, k, v, feat, gate_w, gate_b, z, rms_w};
+    const size_t nb[] = {rows * dk * eb, rows * dk * eb, rows * dv * eb, tokens * rank * eb,
+                         static_cast<size_t>(rank) * hd * eb, hd * 4, rows * dv * eb,
+                         static_cast<size_t>(dv) * 4};
+    s = check_aliasing(out, rows * dv * eb, ins, nb, 8);
+    if (s != GTR_OK) return s;
+    if (!device_ok()) return GTR_ERR_HIP;
+    GlaArgs a{q, k, v, nullptr, z, rms_w, out, nullptr, B, H, gh, gw, dk, dv, direction,
+              chunk ? chunk : kDefaultChunk, dtype, static_cast<int64_t>(gh) * gw};
+    a.feat = feat;
+    a.gate_w = gate_w;
+    a.gate_b = gate_b;
+    a.inv_tau = 1.f / tau;
+    a.rank = rank;
+    const int p = path == GTR_PATH_AUTO ? auto_path(a) : path;
+    if (p == GTR_PATH_MFMA && lowrank_fused_supported(a)) return run_mfma(a, stream, mk);
+    // every other path reads log_g: write it out first
+    void *lg = nullptr;
+    s = workspace(stream, rows * dk * 4, &lg, g_gws);
+    if (s != GTR_OK) return s;
+    hipError_t e = mk.start(stream);
+    if (e == hipSuccess) e = gate_materialize(a, static_cast<float *>(lg), stream);
+    if (e == hipSuccess) e = mk.after_launch(stream);
+    if (e != hipSuccess) return hip_fail(e, "gate projection launch");
+    a.log_g = static_cast<const float *>(lg);
+    a.feat = nullptr;
+    return run(a, p, stream, mk);
 }
 
 gtr_status fwd_impl(const void *q, const void *k, const void *v, const float *log_g,
@@ -393,6 +459,25 @@ int gtr_gla_auto_path(int B, int H, int grid_h, int grid_w, int dk, int dv, int 
     return auto_path(a);
 }
 
+gtr_status gtr_gla_lowrank_fwd(const void *q, const void *k, const void *v, const void *feat,
+                               const void *gate_w, const float *gate_b, float tau, int rank,
+                               const void *z, const float *rms_w, void *out, int B, int H,
+                               int grid_h, int grid_w, int dk, int dv, int direction, int chunk,
+                               gtr_dtype dtype, int path, hipEvent_t *events, int n_events,
+                               int *n_launches, hipStream_t stream) {
+    if (n_events < 0 || (n_events > 0 && !events)) {
+        g_err.clear();
+        return fail(GTR_ERR_ARG, "events: need n_events >= 0 and a non-null array");
+    }
+    Marks mk;
+    mk.ev = events;
+    mk.n = n_events;
+    gtr_status s = lowrank_impl(q, k, v, feat, gate_w, gate_b, tau, rank, z, rms_w, out, B, H,
+                                grid_h, grid_w, dk, dv, direction, chunk, dtype, path, stream, mk);
+    if (n_launches) *n_launches = mk.launches;
+    return s;
+}
+
 const char *gtr_last_error(void) { return g_err.c_str(); }
 
 int gtr_version(void) { return GTR_VERSION; }
@@ -403,7 +488,7 @@ void gtr_release_workspace(void) {
     std::lock_guard<std::mutex> lock(g_ws_mu);
     int cur = 0;
     const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-    for (auto *m : {&g_ws, &g_ctr}) {
+    for (auto *m : {&g_ws, &g_ctr, &g_gws}) {
         for (auto &kv : *m) {
             if (!kv.second.ptr) continue;
             if (hipSetDevice(kv.first.first) == hipSuccess) {

@@ -24,7 +24,23 @@ struct GlaArgs {
     const void *resid;  // previous block's output (stack residual) or nullptr
     int B, H, gh, gw, dk, dv, direction, chunk, dtype;
     int64_t L;
+    // Low-rank gate (kernels that form log_g themselves; log_g is then unused):
+    // feat [B L][rank] and gate_w [rank][H dk] of the I/O type, gate_b [H dk]
+    // float32, log g = logsigmoid(feat . gate_w + gate_b) / tau.
+    const void *feat = nullptr;
+    const void *gate_w = nullptr;
+    const float *gate_b = nullptr;
+    float inv_tau = 1.f;
+    int rank = 0;
 };
+
+// log(sigmoid(x)) = min(x, 0) - log(1 + exp(-|x|)) with the native base-2
+// exponential and logarithm (1 + exp(-|x|) lies in [1, 2]: no overflow for
+// either sign of x).
+__device__ __forceinline__ float log_sigmoid(float x) {
+    const float u = __builtin_amdgcn_exp2f(-fabsf(x) * 1.44269504088896340736f);
+    return fminf(x, 0.f) - 0.69314718055994530942f * __builtin_amdgcn_logf(1.f + u);
+}
 
 // ------------------------------------------------------------ element I/O --
 template <int DT> struct Elem;
@@ -156,6 +172,13 @@ bool fast_supported(const GlaArgs &a);    // shape has a kernel and <= 64 chunks
 // U: [chunks][dk][dv] fp32; G: [chunks][dk]; cnt: fast_counters() words, zero before
 // the first launch (each launch leaves them zero).
 hipError_t fast_launch(const GlaArgs &a, float *U, float *G, unsigned *cnt, hipStream_t s);
+// Low-rank gate written out: log_g [B L][H dk] (float32) from a.feat, a.gate_w,
+// a.gate_b, a.inv_tau, a.rank (k_gate.hip).
+hipError_t gate_materialize(const GlaArgs &a, float *log_g, hipStream_t s);
+// The summary and output kernels that form the gate from rank-16 features
+// themselves (sum_launch / rows_output with a.feat set).
+constexpr int kFusedGateRank = 16;
+bool lowrank_fused_supported(const GlaArgs &a);
 // State scan over the segments of a plan, in place: U[k] <- state before segment k.
 hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,
                            int dv, hipStream_t s);

@@ -26,6 +26,11 @@
 // update, V for the intra product and the state update, and the state S^T
 // (hi, lo) that every wave reads for Q~ S.  Three barriers per chunk.
 //
+// Low-rank gate variant (LRG): instead of reading log_g, each wave forms its
+// tokens' gates from their rank-16 features (Method §1: a light low-rank
+// projection with a temperature) with four 16x16x16 products against the
+// segment head's projection, kept in LDS, and logsigmoid / tau.
+//
 // Value-column map.  MFMA tile dd of the output O^T (16 value columns) holds in
 // its row m the value column dcol(dd, m) = colB(dd, m / 4) + m % 4 with
 // colB(dd, k) = 32 (dd / 2) + 8 k + 4 ((dd & 1) ^ (k & 1)).  Then lane group g
@@ -58,7 +63,7 @@ __device__ __forceinline__ int colB(int dd, int k) {
 }
 __device__ __forceinline__ int dcol(int dd, int m) { return colB(dd, m >> 2) + (m & 3); }
 
-template <int DT, int DV, bool RES>
+template <int DT, int DV, bool RES, bool LRG>
 struct RowTile {
     static constexpr int C = 64, NB = 4;
     static constexpr int ND = DV / 16;  // value tiles
@@ -75,21 +80,25 @@ struct RowTile {
     static constexpr int O_TOT = O_S + 2 * DV * 64 * 2;     // float [NB][DK]
     static constexpr int O_TAB = O_TOT + NB * DK * 4;       // float [4 waves][2][DK]
     static constexpr int O_RW = O_TAB + 4 * 2 * DK * 4;     // float [DV]
-    static constexpr int BYTES = O_RW + DV * 4;
+    static constexpr int O_GATE = O_RW + DV * 4;            // low-rank gate weights (LRG)
+    static constexpr int BYTES = O_GATE + (LRG ? LowRankGate<DT>::LDS_BYTES : 0);
     static_assert(C * DK * 4 <= 2 * DV * 64 * 2, "fp32 gates must fit the state area");
     static_assert(ND * 4 * 64 * 16 <= 2 * DV * 64 * 2, "output exchange must fit the state area");
 
     GlaArgs a;
     uint16_t *sK, *sV, *sS;
     float *sTot, *sTab, *sRw;
+    char *sGate;
     int w, l, lr, g;
 
-    // this lane's token: rows (negative = past the end, ~row of the last token)
-    int64_t rowC, rowN;
+    // this lane's token: rows (negative = past the end, ~row of the last token) and
+    // token indices b L + grid position (of the row read)
+    int64_t rowC, rowN, tokC, tokN;
     // next chunk's inputs of this lane's token
     uint4 pq[2], pk[2], pv[NE], pz[NE];
     uint4 pr[RES ? NE : 1];  // previous block's output, added to v where v is consumed
-    float4 pg[4];
+    float4 pg[LRG ? 1 : 4];  // log_g (LRG: the gate features pf instead)
+    uint2 pf;
     float cs[16];
     // state tiles (S[s][ct][r] = S[16 ct + 4 g + r][dcol(NS w + s, lr)]) and the
     // output tiles of this wave's tokens (O[dd][r] = O^T[dcol(dd, 4 g + r)][token lr])
@@ -104,6 +113,7 @@ struct RowTile {
         sS = reinterpret_cast<uint16_t *>(smem + O_S);
         sTot = reinterpret_cast<float *>(smem + O_TOT);
         sRw = reinterpret_cast<float *>(smem + O_RW);
+        sGate = smem + O_GATE;
         const int tid = threadIdx.x;
         w = __builtin_amdgcn_readfirstlane(tid >> 6);
         l = tid & 63;
@@ -117,7 +127,7 @@ struct RowTile {
     // sequence bh.  A token past the end of the sequence reads the last token's
     // row (finite values that reach only masked scores, its own unstored output
     // and the state after the sequence's last chunk, which is never used).
-    __device__ __forceinline__ int64_t row_of(uint32_t b, uint32_t h, int64_t ch) const {
+    __device__ __forceinline__ int64_t row_of(uint32_t b, uint32_t h, int64_t ch, int64_t &tok) const {
         const uint32_t L32 = static_cast<uint32_t>(a.L);
         const uint32_t t0 = static_cast<uint32_t>(ch) * C + 16 * w + lr;
         uint32_t t = t0 < L32 ? t0 : L32 - 1;
@@ -128,18 +138,24 @@ struct RowTile {
             const uint32_t c = t / gh;
             pos = (t - c * gh) * static_cast<uint32_t>(a.gw) + c;
         }
-        const int64_t row = (static_cast<int64_t>(b) * a.L + pos) * a.H + h;
+        tok = static_cast<int64_t>(b) * a.L + pos;
+        const int64_t row = tok * a.H + h;
         return t0 < L32 ? row : ~row;
     }
     __device__ __forceinline__ static int64_t live(int64_t row) { return row < 0 ? ~row : row; }
 
-    __device__ __forceinline__ void prefetch_gv(int64_t rw) {
+    __device__ __forceinline__ void prefetch_gv(int64_t rw, int64_t tok) {
         const int64_t row = live(rw);
+        if constexpr (LRG) {
+            pf = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.feat) +
+                                                  tok * kFusedGateRank + 4 * g);
+        } else {
 #pragma unroll
-        for (int kap = 0; kap < 2; ++kap) {
-            const int c0 = 32 * kap + 8 * g;
-            pg[2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
-            pg[2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
+            for (int kap = 0; kap < 2; ++kap) {
+                const int c0 = 32 * kap + 8 * g;
+                pg[2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
+                pg[2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
+            }
         }
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
@@ -207,10 +223,14 @@ struct RowTile {
                 *reinterpret_cast<uint2 *>(sl + off) = make_uint2(lo[0], lo[1]);
             }
         }
+        if constexpr (LRG) {
+            LowRankGate<DT>::gates_lds(sGate, l, g, a.inv_tau, pf, cs);
+        } else {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            cs[4 * q4] = pg[q4].x; cs[4 * q4 + 1] = pg[q4].y;
-            cs[4 * q4 + 2] = pg[q4].z; cs[4 * q4 + 3] = pg[q4].w;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                cs[4 * q4] = pg[q4].x; cs[4 * q4 + 1] = pg[q4].y;
+                cs[4 * q4 + 2] = pg[q4].z; cs[4 * q4 + 3] = pg[q4].w;
+            }
         }
         row_scan(cs);
         if (lr == 15) {
@@ -532,10 +552,10 @@ struct RowTile {
     }
 };
 
-template <int DT, int DV, bool RES>
+template <int DT, int DV, bool RES, bool LRG>
 __global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const float *__restrict__ Sx,
                                                                MfmaPlan pl, MfmaPlan ps) {
-    using R = RowTile<DT, DV, RES>;
+    using R = RowTile<DT, DV, RES, LRG>;
     __shared__ __attribute__((aligned(16))) char smem[R::BYTES];
     R t;
     t.init(a, smem);
@@ -548,8 +568,8 @@ __global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const 
     const int64_t bh0 = p0 / pl.N;
     int64_t ch = p0 - bh0 * pl.N;
     uint32_t b = static_cast<uint32_t>(bh0 / a.H), h = static_cast<uint32_t>(bh0 % a.H);
-    t.rowC = t.row_of(b, h, ch);
-    t.prefetch_gv(t.rowC);
+    t.rowC = t.row_of(b, h, ch, t.tokC);
+    t.prefetch_gv(t.rowC, t.tokC);
     t.prefetch_qk(t.rowC);
     t.prefetch_z(t.rowC);
 
@@ -560,7 +580,11 @@ __global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const 
     for (int64_t p = p0; p < p1;) {
         const int64_t pe = (p - ch + pl.N < p1) ? p - ch + pl.N : p1;  // segment end
         t.load_state(Sx + seg_id(p, ps) * DK * DV);
+        LowRankGate<DT> lg;
+        if constexpr (LRG) lg.load(a, h, t.lr, t.g);  // the segment's head
         t.state_ready();
+        // (every wave is past the previous chunk's last barrier: the old copy is unused)
+        if constexpr (LRG) lg.put(t.sGate, t.l, t.g);
         for (; p < pe; ++p) {
             const bool last_in_seq = (ch == pl.N - 1);
             const bool more = p + 1 < p1;
@@ -573,8 +597,9 @@ __global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const 
                 nh = 0;
                 ++nb;
             }
-            t.rowN = more ? t.row_of(nb, nh, last_in_seq ? 0 : ch + 1) : t.rowC;
-            t.prefetch_gv(t.rowN);  // phase 1 consumed log_g and v
+            t.tokN = t.tokC;
+            t.rowN = more ? t.row_of(nb, nh, last_in_seq ? 0 : ch + 1, t.tokN) : t.rowC;
+            t.prefetch_gv(t.rowN, t.tokN);  // phase 1 consumed the gates and v
             const bool slow = t.phase2();
             t.prefetch_qk(t.rowN);  // phase 2 consumed q and k
             __syncthreads();  // B2: K^
@@ -585,6 +610,7 @@ __global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const 
             t.epilogue();
             t.prefetch_z(t.rowN);
             t.rowC = t.rowN;
+            t.tokC = t.tokN;
             __syncthreads();  // B3: LDS is rewritten by the next chunk
             ch = last_in_seq ? 0 : ch + 1;
             b = nb;
@@ -597,10 +623,18 @@ template <int DT, int DV>
 hipError_t launch_rows(const GlaArgs &a, const float *Sx, const MfmaPlan &po, const MfmaPlan &ps,
                        hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(po.n_wg));
-    if (a.resid)
-        hipLaunchKernelGGL((k_rows<DT, DV, true>), grid, dim3(NT), 0, st, a, Sx, po, ps);
-    else
-        hipLaunchKernelGGL((k_rows<DT, DV, false>), grid, dim3(NT), 0, st, a, Sx, po, ps);
+    if (a.feat) {  // gates from rank-16 features: dv = 64, no residual
+        if constexpr (DV == 64) {
+            if (a.resid || a.rank != kFusedGateRank) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((k_rows<DT, DV, false, true>), grid, dim3(NT), 0, st, a, Sx, po, ps);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (a.resid) {
+        hipLaunchKernelGGL((k_rows<DT, DV, true, false>), grid, dim3(NT), 0, st, a, Sx, po, ps);
+    } else {
+        hipLaunchKernelGGL((k_rows<DT, DV, false, false>), grid, dim3(NT), 0, st, a, Sx, po, ps);
+    }
     return hipGetLastError();
 }
 

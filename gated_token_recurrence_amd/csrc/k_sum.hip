@@ -22,6 +22,11 @@
 // 16x16x16 MFMA operands, so the only cross-wave exchange per chunk is the
 // sub-block gate totals (one barrier).  At a segment's end the four partials
 // are added through LDS.
+//
+// Low-rank gate variant (LRG): the gates come from the tokens' rank-16
+// features (Method §1: a light low-rank projection with a temperature), four
+// 16x16x16 products against the head's projection held in registers, then
+// logsigmoid / tau; log_g is not read.
 #include <type_traits>
 
 #include "mfma_common.hpp"
@@ -31,19 +36,7 @@ namespace {
 
 using namespace mf;
 
-typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
-
-// D += A B, 16x16x16, raw 16-bit operands (4 per lane)
-template <bool F16>
-__device__ __forceinline__ f32x4 mma16(s16x4 a, s16x4 b, f32x4 c) {
-    if constexpr (F16)
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-template <int DT, int DV, bool RES>
+template <int DT, int DV, bool RES, bool LRG>
 struct SumTile {
     static constexpr bool F16 = DT == DT_F16;
     static constexpr int C = 64, NB = 4;
@@ -70,7 +63,9 @@ struct SumTile {
     // inputs of the next two chunks (register sets alternate by chunk); pr: the
     // previous block's output, added to v where v is consumed
     uint4 pk[2][2], pv[2][NE], pr[2][RES ? NE : 1];
-    float4 pg[2][4];
+    float4 pg[2][LRG ? 1 : 4];  // log_g (LRG: the gate features pf instead)
+    uint2 pf[2];
+    LowRankGate<DT> lg;
     float cs[16];
     f32x4 U[4][ND];  // U[ct][dt][r] = partial U[16 ct + 4 g + r][16 dt + lr]
     float R;         // summed log2-gate of the segment's chunks after this one, channel l
@@ -93,7 +88,7 @@ struct SumTile {
     // row ((b L + grid position) H + h) of this lane's token of chunk ch of
     // sequence (b, h); a token past the end of the sequence takes the last token's
     // row (its values reach only the sequence's final state, which is never used)
-    __device__ __forceinline__ int64_t row_of(uint32_t b, uint32_t h, int64_t ch) const {
+    __device__ __forceinline__ int64_t row_of(uint32_t b, uint32_t h, int64_t ch, int64_t &tok) const {
         const uint32_t L32 = static_cast<uint32_t>(a.L);
         const uint32_t t0 = static_cast<uint32_t>(ch) * C + 16 * w + lr;
         uint32_t t = t0 < L32 ? t0 : L32 - 1;
@@ -104,16 +99,22 @@ struct SumTile {
             const uint32_t c = t / gh;
             pos = (t - c * gh) * static_cast<uint32_t>(a.gw) + c;
         }
-        return (static_cast<int64_t>(b) * a.L + pos) * a.H + h;
+        tok = static_cast<int64_t>(b) * a.L + pos;
+        return tok * a.H + h;
     }
 
     template <int S>
-    __device__ __forceinline__ void prefetch_g(int64_t row) {
+    __device__ __forceinline__ void prefetch_g(int64_t row, int64_t tok) {
+        if constexpr (LRG) {
+            pf[S] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.feat) +
+                                                     tok * kFusedGateRank + 4 * g);
+        } else {
 #pragma unroll
-        for (int kap = 0; kap < 2; ++kap) {
-            const int c0 = 32 * kap + 8 * g;
-            pg[S][2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
-            pg[S][2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
+            for (int kap = 0; kap < 2; ++kap) {
+                const int c0 = 32 * kap + 8 * g;
+                pg[S][2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
+                pg[S][2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
+            }
         }
     }
 
@@ -144,10 +145,14 @@ struct SumTile {
     // totals into buffer buf
     template <int buf>
     __device__ __forceinline__ void gates() {
+        if constexpr (LRG) {
+            lg.gates(pf[buf], cs);
+        } else {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            cs[4 * q4] = pg[buf][q4].x; cs[4 * q4 + 1] = pg[buf][q4].y;
-            cs[4 * q4 + 2] = pg[buf][q4].z; cs[4 * q4 + 3] = pg[buf][q4].w;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                cs[4 * q4] = pg[buf][q4].x; cs[4 * q4 + 1] = pg[buf][q4].y;
+                cs[4 * q4 + 2] = pg[buf][q4].z; cs[4 * q4 + 3] = pg[buf][q4].w;
+            }
         }
         row_scan(cs);
         if (lr == 15) {
@@ -269,10 +274,10 @@ struct SumTile {
     }
 };
 
-template <int DT, int DV, bool RES>
+template <int DT, int DV, bool RES, bool LRG>
 __global__ __launch_bounds__(NT, 2) void k_sum(GlaArgs a, float *__restrict__ Uo, float *__restrict__ Gs,
                                               MfmaPlan pl) {
-    using T = SumTile<DT, DV, RES>;
+    using T = SumTile<DT, DV, RES, LRG>;
     __shared__ __attribute__((aligned(16))) char smem[T::BYTES];
     T t;
     t.init(a, smem);
@@ -306,14 +311,20 @@ __global__ __launch_bounds__(NT, 2) void k_sum(GlaArgs a, float *__restrict__ Uo
         }
     };
     {
-        const int64_t row = t.row_of(far.b, far.h, far.ch);
-        t.template prefetch_g<0>(row);
+        int64_t tok, tok1;
+        const int64_t row = t.row_of(far.b, far.h, far.ch, tok);
+        t.template prefetch_g<0>(row, tok);
         t.template prefetch_kv<0>(row);
         back(far);
-        const int64_t row1 = (p1 - 2 >= p0) ? t.row_of(far.b, far.h, far.ch) : row;
-        t.template prefetch_g<1>(row1);
+        tok1 = tok;
+        const int64_t row1 = (p1 - 2 >= p0) ? t.row_of(far.b, far.h, far.ch, tok1) : row;
+        t.template prefetch_g<1>(row1, tok1);
         t.template prefetch_kv<1>(row1);
         back(far);  // now two before the current chunk
+    }
+    if constexpr (LRG) {  // weights of the last chunk's head
+        t.lg.load(a, cur.h, t.lr, t.g);
+        t.lg.ready();
     }
     t.zero();
     auto step = [&](auto S_, int64_t p) {
@@ -322,20 +333,28 @@ __global__ __launch_bounds__(NT, 2) void k_sum(GlaArgs a, float *__restrict__ Uo
         // the current chunk's rows, unused), so that the wait-count bookkeeping
         // sees the same load sequence each time and never has to drain the queue.
         const bool ahead = p - 2 >= p0;
-        const int64_t row = ahead ? t.row_of(far.b, far.h, far.ch) : t.row_of(cur.b, cur.h, cur.ch);
+        int64_t tok;
+        const int64_t row = ahead ? t.row_of(far.b, far.h, far.ch, tok) : t.row_of(cur.b, cur.h, cur.ch, tok);
         t.template gates<S>();
-        t.template prefetch_g<S>(row);  // the gates are consumed
+        t.template prefetch_g<S>(row, tok);  // the gates are consumed
         __syncthreads();  // the chunk's sub-block totals
         t.template stage<S>();
         t.template prefetch_kv<S>(row);  // k and v are consumed
         t.accumulate();
-        if (p == p0 || cur.ch == 0) {  // the segment's first chunk: its summary is complete
+        const bool seg_start = p == p0 || cur.ch == 0;
+        if (seg_start) {  // the segment's first chunk: its summary is complete
             const int64_t sid = seg_id(p, pl);
             t.finish(Uo + sid * DK * DV, Gs + sid * DK);
             t.zero();
         }
         back(cur);
         if (ahead) back(far);
+        if constexpr (LRG) {
+            if (seg_start && p > p0) {  // the next chunk belongs to the previous head
+                t.lg.load(a, cur.h, t.lr, t.g);
+                t.lg.ready();
+            }
+        }
     };
     for (int64_t p = p1 - 1; p >= p0; p -= 2) {
         step(std::integral_constant<int, 0>{}, p);
@@ -347,10 +366,14 @@ __global__ __launch_bounds__(NT, 2) void k_sum(GlaArgs a, float *__restrict__ Uo
 template <int DT, int DV>
 hipError_t launch_sum(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(ps.n_wg));
-    if (a.resid)
-        hipLaunchKernelGGL((k_sum<DT, DV, true>), grid, dim3(NT), 0, st, a, U, G, ps);
-    else
-        hipLaunchKernelGGL((k_sum<DT, DV, false>), grid, dim3(NT), 0, st, a, U, G, ps);
+    if (a.feat) {  // gates from rank-16 features, no residual
+        if (a.resid || a.rank != kFusedGateRank) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_sum<DT, DV, false, true>), grid, dim3(NT), 0, st, a, U, G, ps);
+    } else if (a.resid) {
+        hipLaunchKernelGGL((k_sum<DT, DV, true, false>), grid, dim3(NT), 0, st, a, U, G, ps);
+    } else {
+        hipLaunchKernelGGL((k_sum<DT, DV, false, false>), grid, dim3(NT), 0, st, a, U, G, ps);
+    }
     return hipGetLastError();
 }
 

@@ -178,6 +178,95 @@ __device__ __forceinline__ uint32_t half16(const uint4 &u, int s) {
     return (s & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+
+// D += A B, 16x16x16, raw 16-bit operands (4 per lane): lane i holds A[i % 16]
+// [4 (i / 16) ..], B[4 (i / 16) ..][i % 16] and D[4 (i / 16) + r][i % 16].
+template <bool F16>
+__device__ __forceinline__ f32x4 mma16(s16x4 a, s16x4 b, f32x4 c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Forget gate of one token from its rank-16 features (GTR write-up, Method §1:
+// a light low-rank projection of the input with a temperature), for the 16 key
+// channels a lane holds in the token-row layout: lane (lr, g) of a wave holds
+// token lr and cs[8 kap + s] is channel 32 kap + 8 g + s.  The projection runs
+// as four 16x16x16 products with M = 16 channels, K = the 16 ranks, N = 16
+// tokens; tile ct puts in its row m the channel
+//     chan(ct, m) = 32 (ct / 2) + 8 (m / 4) + 4 (ct % 2) + m % 4,
+// so that output element r of tile ct (row 4 g + r) is cs[4 ct + r].
+template <int DT>
+struct LowRankGate {
+    s16x4 wa[4];    // A operands: gate_w[4 g + j][h dk + chan(ct, lr)], j < 4
+    f32x4 bias[4];  // gate_b of the lane's output channels (the accumulator start)
+    float inv_tau;
+
+    __device__ __forceinline__ static int chan(int ct, int m) {
+        return 32 * (ct >> 1) + 8 * (m >> 2) + 4 * (ct & 1) + (m & 3);
+    }
+    // weights of head h (loads; the caller waits for them before the chunk loop)
+    __device__ __forceinline__ void load(const GlaArgs &a, uint32_t h, int lr, int g) {
+        const uint16_t *wp = static_cast<const uint16_t *>(a.gate_w);
+        const int64_t hd = static_cast<int64_t>(a.H) * DK;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const int64_t col = static_cast<int64_t>(h) * DK + chan(ct, lr);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wa[ct][j] = static_cast<short>(wp[(4 * g + j) * hd + col]);
+            const float4 b4 = *reinterpret_cast<const float4 *>(a.gate_b + h * DK + chan(ct, 4 * g));
+            bias[ct] = f32x4{b4.x, b4.y, b4.z, b4.w};
+        }
+        inv_tau = a.inv_tau;
+    }
+    __device__ __forceinline__ void ready() const {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) asm volatile("" ::"v"(wa[ct]), "v"(bias[ct]));
+    }
+    // cs (natural-log units) from this lane's features f = feat[token lr][4 g .. 4 g + 3]
+    __device__ __forceinline__ void gates(uint2 f, float (&cs)[16]) const {
+        const s16x4 fb = __builtin_bit_cast(s16x4, f);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const f32x4 x = mma16<DT == DT_F16>(wa[ct], fb, bias[ct]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cs[4 * ct + r] = log_sigmoid(x[r]) * inv_tau;
+        }
+    }
+
+    // LDS copy for kernels short of registers: the A operands [4][64 lanes] and
+    // the 64 biases of the head.  Every wave of a workgroup works on the same head
+    // and writes the whole copy (the same values), so a wave's own writes are all
+    // it needs before reading; callers write only after every wave is done with
+    // the previous head's copy.
+    static constexpr int LDS_BYTES = 4 * 64 * 8 + 64 * 4;
+    __device__ __forceinline__ void put(char *m, int l, int g) const {
+        s16x4 *wm = reinterpret_cast<s16x4 *>(m);
+        float *bm = reinterpret_cast<float *>(m + 4 * 64 * 8);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            wm[ct * 64 + l] = wa[ct];
+            *reinterpret_cast<f32x4 *>(bm + chan(ct, 4 * g)) = bias[ct];
+        }
+    }
+    __device__ __forceinline__ static void gates_lds(const char *m, int l, int g, float itau,
+                                                     uint2 f, float (&cs)[16]) {
+        const s16x4 *wm = reinterpret_cast<const s16x4 *>(m);
+        const float *bm = reinterpret_cast<const float *>(m + 4 * 64 * 8);
+        const s16x4 fb = __builtin_bit_cast(s16x4, f);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(bm + chan(ct, 4 * g));
+            const f32x4 x = mma16<DT == DT_F16>(wm[ct * 64 + l], fb, b);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cs[4 * ct + r] = log_sigmoid(x[r]) * itau;
+        }
+    }
+};
+
 template <int DT, int DV, int NB, bool SUM>
 struct Cfg {
     static constexpr int C = 16 * NB;

@@ -129,6 +129,38 @@ gtr_status gtr_gla_stack_fwd(const void *q, const void *k, const void *v, const 
                              int first_direction, int chunk, gtr_dtype dtype,
                              hipStream_t stream);
 
+/*
+ * One mixer call whose forget gate is formed inside the library from rank-r
+ * gate features (GTR write-up "端侧实时感知新标杆！通用线性骨干网络GTR开源",
+ * Method §1: the gate is generated from the input by a light low-rank
+ * projection with a temperature; the page's rank and temperature were lost,
+ * so both are arguments):
+ *     x[b, p, h, c]     = sum_j feat[b, p, j] * gate_w[j, h*dk + c] + gate_b[h*dk + c]
+ *     log_g[b, p, h, c] = logsigmoid(x) / tau         (g = sigmoid(x)^(1/tau))
+ * and then exactly the operation of gtr_gla_fwd with that log_g.
+ *   feat   : [B, grid_h, grid_w, rank]  I/O type; one vector per token, shared by
+ *            all heads (the input already projected to rank r)
+ *   gate_w : [rank, H*dk]               I/O type
+ *   gate_b : [H*dk]                     float32
+ *   rank   : 1 .. 256;   tau: finite and > 0 (the usual GLA choice is 16)
+ * feat, gate_w and gate_b must be 16-byte aligned.  The other tensors, dtype,
+ * direction and chunk are as for gtr_gla_fwd; path as gtr_gla_fwd_path, and
+ * AUTO picks the path gtr_gla_fwd would.  With 16-bit I/O, dk = dv = 64,
+ * chunk 64 and rank 16 the MFMA path forms the gate inside its summary and
+ * output kernels and log_g never reaches memory; every other case first
+ * writes log_g (float32) to a library workspace with one extra launch.
+ * events / n_events / n_launches as gtr_gla_fwd_events (that extra launch,
+ * when there is one, is the first); events may be NULL when n_events is 0, and
+ * n_launches may be NULL.  Errors as gtr_gla_fwd.
+ */
+gtr_status gtr_gla_lowrank_fwd(const void *q, const void *k, const void *v, const void *feat,
+                               const void *gate_w, const float *gate_b, float tau, int rank,
+                               const void *z, const float *rms_w, void *out,
+                               int B, int H, int grid_h, int grid_w, int dk, int dv,
+                               int direction, int chunk, gtr_dtype dtype, int path,
+                               hipEvent_t *events, int n_events, int *n_launches,
+                               hipStream_t stream);
+
 /* The gtr_path that GTR_PATH_AUTO selects for these arguments, or a negative
  * gtr_status if the arguments are invalid (no device access). */
 int gtr_gla_auto_path(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,

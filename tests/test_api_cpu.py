@@ -95,3 +95,62 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b|gtr_oracle|libgtr_oracle",
                                      text, flags=re.M), f
+
+
+PL = [(i + 1) << 36 for i in range(11)]  # q k v feat gate_w gate_b _ _ z rms_w out
+
+
+def _lowrank(**kw):
+    a = dict(tau=16.0, rank=16, B=1, H=2, gh=8, gw=8, dk=64, dv=64, direction=0, chunk=0,
+             dtype=1, path=0, ptrs=None)
+    a.update(kw)
+    p = a["ptrs"] or PL
+    lib = _lib.load()
+    n = ctypes.c_int(-1)
+    st = lib.gtr_gla_lowrank_fwd(p[0], p[1], p[2], p[3], p[4], p[5], a["tau"], a["rank"], p[8],
+                                 p[9], p[10], a["B"], a["H"], a["gh"], a["gw"], a["dk"], a["dv"],
+                                 a["direction"], a["chunk"], a["dtype"], a["path"], None, 0,
+                                 ctypes.byref(n), None)
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rank=0), dict(rank=257), dict(tau=0.0), dict(tau=-1.0), dict(tau=float("inf")),
+    dict(tau=float("nan")), dict(B=0), dict(direction=5), dict(path=7), dict(chunk=24),
+])
+def test_lowrank_bad_arguments_are_rejected(kw):
+    st, n = _lowrank(**kw)
+    assert st == _lib.GTR_ERR_ARG, _lib.last_error()
+    assert _lib.last_error() != "" and n == 0
+
+
+def test_lowrank_null_and_misaligned_gate_pointers():
+    for i in (3, 4, 5):
+        p = list(PL)
+        p[i] = None
+        st, _ = _lowrank(ptrs=p)
+        assert st == _lib.GTR_ERR_ARG and "null" in _lib.last_error()
+        p = list(PL)
+        p[i] = PL[i] + 8
+        st, _ = _lowrank(ptrs=p)
+        assert st == _lib.GTR_ERR_ARG and "aligned" in _lib.last_error()
+
+
+def test_lowrank_out_aliasing_is_rejected():
+    p = list(PL)
+    p[10] = PL[3]  # out on top of feat
+    st, _ = _lowrank(ptrs=p)
+    assert st == _lib.GTR_ERR_ARG and "overlaps" in _lib.last_error()
+
+
+def test_lowrank_events_need_an_array():
+    lib = _lib.load()
+    st = lib.gtr_gla_lowrank_fwd(*PL[:6], 16.0, 16, *PL[8:], 1, 2, 8, 8, 64, 64, 0, 0, 1, 0,
+                                 None, 2, None, None)
+    assert st == _lib.GTR_ERR_ARG
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device error path")
+def test_lowrank_valid_call_without_device_reports_hip_error():
+    st, n = _lowrank()
+    assert st == _lib.GTR_ERR_HIP and n == 0
