@@ -229,6 +229,51 @@ def make_lowrank_inputs(w: Workload, block: int = 0, rank: int = 16, tau: float 
                         seed=1000 * w.wid + 500 + block, rank=rank, tau=tau, scale=w.scale)
 
 
+@dataclasses.dataclass(frozen=True)
+class SSwiGLUWorkload:
+    """Shapes of the Spatial SwiGLU middle: u = [B, grid_h, grid_w, 2F] in, m = [.., F] out."""
+    wid: int
+    name: str
+    B: int
+    grid_h: int
+    grid_w: int
+    F: int
+    k: int
+    dtype: str
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.grid_h * self.grid_w
+
+    def compulsory_bytes(self) -> int:
+        """u read once, m written once, kernel taps and bias once."""
+        s = DTYPE_BYTES[self.dtype]
+        return self.tokens * 3 * self.F * s + self.F * (self.k * self.k + 1) * 4
+
+
+SSWIGLU_WORKLOADS = {
+    # 12-block backbone shapes at 1024 x 1024 (stride 16), width 768, SwiGLU hidden 2048
+    "sswiglu_1024": SSwiGLUWorkload(10, "sswiglu_1024", 8, 64, 64, 2048, 3, "bf16"),
+    # 640 x 640 input, batch one
+    "sswiglu_640": SSwiGLUWorkload(11, "sswiglu_640", 1, 40, 40, 2048, 3, "f16"),
+}
+
+
+def make_sswiglu(B: int, grid_h: int, grid_w: int, F: int, k: int, dtype: str, seed: int) -> dict:
+    """Inputs of the Spatial SwiGLU middle.  Draw order: u, w_conv, b_conv.
+    u ~ N(0, 1) rounded to the I/O type; w_conv ~ N(0, 1) / k float32 [F, k, k];
+    b_conv ~ N(0, 0.1^2) float32 [F]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {"u": cast_io(rng.standard_normal((B, grid_h, grid_w, 2 * F)), dtype)}
+    out["w_conv"] = (rng.standard_normal((F, k, k)) / k).astype(np.float32)
+    out["b_conv"] = (0.1 * rng.standard_normal(F)).astype(np.float32)
+    return out
+
+
+def make_sswiglu_inputs(w: SSwiGLUWorkload) -> dict:
+    return make_sswiglu(w.B, w.grid_h, w.grid_w, w.F, w.k, w.dtype, seed=1000 * w.wid)
+
+
 def rotation_sets(bytes_per_set: int, min_total: int = 512 << 20) -> int:
     """Number of buffer sets needed so repeated calls do not re-read the 256 MB cache."""
     return max(1, math.ceil(min_total / max(1, bytes_per_set)))

@@ -17,6 +17,13 @@ temperature are lost on the page, the library takes them as arguments):
 x = feat W + b per head channel, log g = logsigmoid(x) / tau.  ``fwd_lowrank``
 is ``fwd`` with that gate.
 
+``sswiglu_mix`` is the fused middle of the Spatial SwiGLU feed-forward block
+(Method §2: in the channel expansion the value branch is reshaped to the 2-D
+grid and mixed by a depthwise convolution; the page's kernel size was lost):
+from the expanded projection u = [gate | value], m = SiLU(gate) * (DWConv(value)
++ bias), zero padding, cross-correlation as in common deep-learning
+frameworks.
+
 ``round_io`` is this package's own IEEE round-to-nearest-even to the I/O type.
 """
 from __future__ import annotations
@@ -131,6 +138,39 @@ def fwd_lowrank(q, k, v, feat, gate_w, gate_b, tau, z, rms_w, direction: int,
     H, dk = q.shape[3], q.shape[4]
     return fwd(q, k, v, lowrank_log_g(feat, gate_w, gate_b, tau, H, dk), z, rms_w,
                direction, eps=eps, bh=bh)
+
+
+# -------------------------------------------------------------- S-SwiGLU mix --
+def depthwise_conv2d(val, w, b) -> np.ndarray:
+    """Depthwise k x k cross-correlation on the grid, zero padding, 'same' size.
+
+    val: [B, gh, gw, F] (channels last); w: [F, k, k] (k odd); b: [F].
+    out[., y, x, f] = b[f] + sum_{i, j} w[f, i, j] * val[., y + i - k//2, x + j - k//2, f]
+    """
+    val, w, b = _f64(val), _f64(w), _f64(b)
+    F, k, k2 = w.shape
+    if k != k2 or k % 2 != 1 or val.shape[-1] != F or b.shape != (F,):
+        raise ValueError("conv shapes")
+    r = k // 2
+    B, gh, gw, _ = val.shape
+    vp = np.pad(val, ((0, 0), (r, r), (r, r), (0, 0)))
+    out = np.broadcast_to(b, val.shape).copy()
+    for i in range(k):
+        for j in range(k):
+            out += w[:, i, j] * vp[:, i:i + gh, j:j + gw, :]
+    return out
+
+
+def sswiglu_mix(u, w, b) -> np.ndarray:
+    """Spatial SwiGLU middle (Method §2): u = [B, gh, gw, 2F] = [gate | value];
+    returns m = SiLU(gate) * depthwise_conv2d(value, w, b) in float64."""
+    u = _f64(u)
+    F = u.shape[-1] // 2
+    if u.shape[-1] != 2 * F:
+        raise ValueError("u must hold gate and value halves")
+    gate, val = u[..., :F], u[..., F:]
+    silu = gate / (1.0 + np.exp(-gate))
+    return silu * depthwise_conv2d(val, w, b)
 
 
 # ------------------------------------------------------------------ rounding --
