@@ -237,6 +237,42 @@ def time_lowrank(w, dev, hip, stream_ptr, steps, warmup, chunk, direction=0, ran
             "launch_us_mean": [statistics.fmean(p[j] for p in per) for j in range(n_ev - 1)]}
 
 
+def time_sswiglu(ws, dev, hip, stream_ptr, steps, warmup):
+    """Timing of gtr_sswiglu_mix on a Spatial SwiGLU workload (rotating buffer sets)."""
+    lib = _lib.load()
+    x = W.make_sswiglu_inputs(ws)
+    per_set = ws.compulsory_bytes()
+    n_sets = W.rotation_sets(per_set)
+    u0 = _io_tensor(x["u"], ws.dtype)
+    wc, bc = torch.from_numpy(x["w_conv"]).to(dev), torch.from_numpy(x["b_conv"]).to(dev)
+    sets = []
+    for _ in range(n_sets):
+        u = u0.to(dev)
+        sets.append((u, torch.empty(u.shape[:-1] + (ws.F,), dtype=u.dtype, device=dev)))
+    torch.cuda.synchronize(dev)
+
+    def run(i):
+        u, m = sets[i % n_sets]
+        _lib.check(lib.gtr_sswiglu_mix(u.data_ptr(), wc.data_ptr(), bc.data_ptr(), m.data_ptr(),
+                                       ws.B, ws.grid_h, ws.grid_w, ws.F, ws.k,
+                                       W.DTYPE_CODE[ws.dtype], stream_ptr))
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize(dev)
+    ev = hip.events(2)
+    hip.record(ev[0], stream_ptr)
+    for i in range(steps):
+        run(i)
+    hip.record(ev[1], stream_ptr)
+    us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+    torch.cuda.synchronize(dev)
+    hip.destroy(ev)
+    del sets
+    torch.cuda.empty_cache()
+    return {"us_per_call": us, "n_sets": n_sets}
+
+
 def graph_time(lib, w, sets, n_sets, dev, direction, chunk, path, steps):
     """hipGraph replay of one call per buffer set (the pages' own kernel benchmark
     used graph launch); microseconds per call."""
@@ -530,6 +566,24 @@ def main():
                 f"{['%.2f' % t for t in r['launch_us_mean']]}")
         except Exception as exc:  # report, do not hide
             lowrank = {"error": str(exc)[:300]}
+    sswiglu = {}
+    if not args.no_extra:
+        for name, ws in W.SSWIGLU_WORKLOADS.items():
+            try:
+                r = time_sswiglu(ws, dev, hip, sp, args.steps, args.warmup)
+            except Exception as exc:  # report, do not hide
+                sswiglu[name] = {"error": str(exc)[:300]}
+                continue
+            gbs = ws.compulsory_bytes() / (r["us_per_call"] * 1e-6) / 1e9
+            sswiglu[name] = {"workload": f"B={ws.B}, grid {ws.grid_h}x{ws.grid_w}, F={ws.F}, "
+                                         f"{ws.k}x{ws.k} depthwise, {ws.dtype}",
+                             "us_per_call": round(r["us_per_call"], 3),
+                             "tokens_per_s": round(ws.tokens / (r["us_per_call"] * 1e-6), 1),
+                             "algorithmic_bytes": ws.compulsory_bytes(),
+                             "achieved_GBs": round(gbs, 1),
+                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "rotating_sets": r["n_sets"]}
+            log(f"  {name}: {r['us_per_call']:.2f} us/call, {gbs:.0f} GB/s")
     cpu = None
     if not args.no_cpu:
         log("  timing the fp64 oracle on the host (bounded sample)")
@@ -566,6 +620,7 @@ def main():
         "cpu_baseline": cpu,
         "extra_1p6k": extra,
         "lowrank_gate": lowrank,
+        "sswiglu_mix": sswiglu,
     }
     print(json.dumps(line), flush=True)
 

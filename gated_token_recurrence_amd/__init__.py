@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import (GtrError, PATH_AUTO, PATH_FAST, PATH_MFMA, PATH_SERIAL)  # noqa: F401
 
-__all__ = ["gla_fwd", "gla_stack_fwd", "gla_lowrank_fwd", "GtrError", "DIRECTIONS", "dtype_code", "version"]
+__all__ = ["gla_fwd", "gla_stack_fwd", "gla_lowrank_fwd", "sswiglu_mix", "GtrError", "DIRECTIONS", "dtype_code", "version"]
 
 DIRECTIONS = {"LR": 0, "RL": 1, "TB": 2, "BT": 3}
 _DT = {torch.float32: _lib.GTR_F32, torch.float16: _lib.GTR_F16, torch.bfloat16: _lib.GTR_BF16}
@@ -154,3 +154,31 @@ def gla_lowrank_fwd(q, k, v, feat, gate_w, gate_b, tau: float, z, rms_w, directi
                                      _stream_ptr(dev))
     _lib.check(st)
     return out, n_launch.value
+
+
+def sswiglu_mix(u, w_conv, b_conv, out=None):
+    """Spatial SwiGLU middle: u [B, gh, gw, 2F] = [gate | value] (I/O dtype),
+    w_conv [F, k, k] and b_conv [F] float32.  Returns m [B, gh, gw, F] =
+    SiLU(gate) * (depthwise k x k convolution of value + b_conv)."""
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    B, gh, gw, F2 = u.shape
+    F = F2 // 2
+    if F2 != 2 * F or w_conv.dim() != 3 or w_conv.shape[0] != F or \
+            w_conv.shape[1] != w_conv.shape[2] or b_conv.shape != (F,):
+        raise ValueError("u [B, gh, gw, 2F], w_conv [F, k, k], b_conv [F] expected")
+    if w_conv.dtype != torch.float32 or b_conv.dtype != torch.float32:
+        raise TypeError("w_conv and b_conv must be float32")
+    if out is None:
+        out = torch.empty((B, gh, gw, F), dtype=u.dtype, device=dev)
+    _check_tensors((("u", u), ("w_conv", w_conv), ("b_conv", b_conv), ("out", out)), dev)
+    if out.shape != (B, gh, gw, F) or out.dtype != u.dtype:
+        raise ValueError("out must be [B, gh, gw, F] of u's dtype")
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        st = lib.gtr_sswiglu_mix(u.data_ptr(), w_conv.data_ptr(), b_conv.data_ptr(),
+                                 out.data_ptr(), B, gh, gw, F, int(w_conv.shape[1]),
+                                 dtype_code(u.dtype), _stream_ptr(dev))
+    _lib.check(st)
+    return out

@@ -478,6 +478,35 @@ gtr_status gtr_gla_lowrank_fwd(const void *q, const void *k, const void *v, cons
     return s;
 }
 
+gtr_status gtr_sswiglu_mix(const void *u, const float *w_conv, const float *b_conv, void *m,
+                           int B, int grid_h, int grid_w, int F, int k, gtr_dtype dtype,
+                           hipStream_t stream) {
+    g_err.clear();
+    if (!u || !w_conv || !b_conv || !m) return fail(GTR_ERR_ARG, "null tensor pointer");
+    if (B <= 0 || grid_h <= 0 || grid_w <= 0 || F <= 0)
+        return fail(GTR_ERR_ARG, "B, grid_h, grid_w, F must be positive (got %d, %d, %d, %d)", B,
+                    grid_h, grid_w, F);
+    if (F % 8 != 0) return fail(GTR_ERR_ARG, "F must be a multiple of 8, got %d", F);
+    if (!(k == 1 || k == 3 || k == 5 || k == 7))
+        return fail(GTR_ERR_ARG, "kernel size must be 1, 3, 5 or 7, got %d", k);
+    if (dtype < GTR_F32 || dtype > GTR_BF16) return fail(GTR_ERR_ARG, "unknown dtype %d", dtype);
+    if (reinterpret_cast<uintptr_t>(u) % 16 != 0 || reinterpret_cast<uintptr_t>(m) % 16 != 0)
+        return fail(GTR_ERR_ARG, "u and m must be 16-byte aligned");
+    const __int128 toks = static_cast<__int128>(B) * grid_h * grid_w;
+    if (toks * 2 * F * 4 > (static_cast<__int128>(1) << 62) || toks > 0x7fffffff)
+        return fail(GTR_ERR_UNSUPPORTED, "tensor sizes overflow the supported range");
+    const size_t eb = elem_bytes(dtype), nt = static_cast<size_t>(toks);
+    const void *ins[] = {u, w_conv, b_conv};
+    const size_t nb[] = {nt * 2 * F * eb, static_cast<size_t>(F) * k * k * 4,
+                         static_cast<size_t>(F) * 4};
+    gtr_status s = check_aliasing(m, nt * F * eb, ins, nb, 3);
+    if (s != GTR_OK) return s;
+    if (!device_ok()) return GTR_ERR_HIP;
+    hipError_t e = sswiglu_launch(u, w_conv, b_conv, m, B, grid_h, grid_w, F, k, dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "S-SwiGLU launch");
+    return GTR_OK;
+}
+
 const char *gtr_last_error(void) { return g_err.c_str(); }
 
 int gtr_version(void) { return GTR_VERSION; }

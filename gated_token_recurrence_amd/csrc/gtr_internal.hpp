@@ -179,6 +179,10 @@ hipError_t gate_materialize(const GlaArgs &a, float *log_g, hipStream_t s);
 // themselves (sum_launch / rows_output with a.feat set).
 constexpr int kFusedGateRank = 16;
 bool lowrank_fused_supported(const GlaArgs &a);
+// Spatial SwiGLU middle (k_sswiglu.hip): m = SiLU(gate) * (depthwise k x k conv of
+// value + bias) from u = [gate | value].
+hipError_t sswiglu_launch(const void *u, const float *w, const float *b, void *m, int B, int gh,
+                          int gw, int F, int k, int dtype, hipStream_t s);
 // State scan over the segments of a plan, in place: U[k] <- state before segment k.
 hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,
                            int dv, hipStream_t s);

@@ -161,6 +161,30 @@ gtr_status gtr_gla_lowrank_fwd(const void *q, const void *k, const void *v, cons
                                hipEvent_t *events, int n_events, int *n_launches,
                                hipStream_t stream);
 
+/*
+ * The fused middle of the Spatial SwiGLU feed-forward block (GTR write-up
+ * "端侧实时感知新标杆！通用线性骨干网络GTR开源", Method §2 "Spatial SwiGLU": in the
+ * channel expansion the value branch is reshaped to the 2-D token grid and
+ * mixed by a depthwise convolution; the page's kernel size was lost, so it is
+ * an argument):
+ *     m[b, y, x, f] = SiLU(gate[b, y, x, f]) * (b_conv[f] + sum_{i, j < k}
+ *                     w_conv[f, i, j] * value[b, y + i - k/2, x + j - k/2, f])
+ * with gate = u[..., :F] and value = u[..., F:] (one expanded projection),
+ * zero padding outside the grid (cross-correlation, as deep-learning
+ * frameworks define convolution), fp32 arithmetic, m rounded to nearest even.
+ *   u      : [B, grid_h, grid_w, 2F]  I/O type
+ *   w_conv : [F, k, k]                float32
+ *   b_conv : [F]                      float32
+ *   m      : [B, grid_h, grid_w, F]   I/O type; must not overlap any input
+ *   k      : 1, 3, 5 or 7;  F: a positive multiple of 8
+ * u and m must be 16-byte aligned.  The projections around it (x W_in before,
+ * m W_out after) are plain GEMMs left to the caller's BLAS.  Ownership,
+ * asynchrony and errors as gtr_gla_fwd.
+ */
+gtr_status gtr_sswiglu_mix(const void *u, const float *w_conv, const float *b_conv, void *m,
+                           int B, int grid_h, int grid_w, int F, int k, gtr_dtype dtype,
+                           hipStream_t stream);
+
 /* The gtr_path that GTR_PATH_AUTO selects for these arguments, or a negative
  * gtr_status if the arguments are invalid (no device access). */
 int gtr_gla_auto_path(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,

@@ -154,3 +154,30 @@ def test_lowrank_events_need_an_array():
 def test_lowrank_valid_call_without_device_reports_hip_error():
     st, n = _lowrank()
     assert st == _lib.GTR_ERR_HIP and n == 0
+
+
+def _sswiglu(**kw):
+    a = dict(B=1, gh=4, gw=4, F=16, k=3, dtype=1, ptrs=None)
+    a.update(kw)
+    p = a["ptrs"] or PL[:4]
+    return _lib.load().gtr_sswiglu_mix(p[0], p[1], p[2], p[3], a["B"], a["gh"], a["gw"], a["F"],
+                                       a["k"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(gh=-1), dict(F=0), dict(F=12), dict(k=2),
+                                dict(k=9), dict(dtype=5)])
+def test_sswiglu_bad_arguments_are_rejected(kw):
+    assert _sswiglu(**kw) == _lib.GTR_ERR_ARG
+    assert _lib.last_error() != ""
+
+
+def test_sswiglu_null_misaligned_and_aliasing():
+    p = list(PL[:4])
+    p[1] = None
+    assert _sswiglu(ptrs=p) == _lib.GTR_ERR_ARG and "null" in _lib.last_error()
+    p = list(PL[:4])
+    p[3] = PL[3] + 8
+    assert _sswiglu(ptrs=p) == _lib.GTR_ERR_ARG and "aligned" in _lib.last_error()
+    p = list(PL[:4])
+    p[3] = PL[0] + 64
+    assert _sswiglu(ptrs=p) == _lib.GTR_ERR_ARG and "overlaps" in _lib.last_error()
