@@ -273,6 +273,42 @@ def time_sswiglu(ws, dev, hip, stream_ptr, steps, warmup):
     return {"us_per_call": us, "n_sets": n_sets}
 
 
+def time_backbone(dev, steps):
+    """12-block random-weight backbone at 640 x 640, batch 1: eager and HIP-graph replay."""
+    from gated_token_recurrence_amd import backbone as bb
+    cfg = bb.BackboneConfig()
+    net = bb.Backbone(cfg, dev, seed=1)
+    image = torch.randn(cfg.batch, 3, cfg.image, cfg.image,
+                        generator=torch.Generator().manual_seed(2)).to(dev)
+    stream = torch.cuda.Stream(dev)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            net.forward(image)
+    torch.cuda.synchronize(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for _ in range(steps):
+            net.forward(image)
+        t1.record(stream)
+    torch.cuda.synchronize(dev)
+    eager_ms = t0.elapsed_time(t1) / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        net.forward(image)
+    graph.replay()
+    torch.cuda.synchronize(dev)
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        t1.record(stream)
+    torch.cuda.synchronize(dev)
+    graph_ms = t0.elapsed_time(t1) / steps
+    del graph
+    return cfg, eager_ms, graph_ms
+
+
 def graph_time(lib, w, sets, n_sets, dev, direction, chunk, path, steps):
     """hipGraph replay of one call per buffer set (the pages' own kernel benchmark
     used graph launch); microseconds per call."""
@@ -584,6 +620,19 @@ def main():
                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                              "rotating_sets": r["n_sets"]}
             log(f"  {name}: {r['us_per_call']:.2f} us/call, {gbs:.0f} GB/s")
+    backbone = None
+    if not args.no_extra:
+        try:
+            cfg, eager_ms, graph_ms = time_backbone(dev, max(10, args.steps // 4))
+            backbone = {"workload": f"{cfg.blocks}-block backbone, {cfg.image}x{cfg.image} "
+                                    f"image (grid {cfg.grid}x{cfg.grid}), width {cfg.width}, "
+                                    f"{cfg.heads} heads, S-SwiGLU hidden {cfg.hidden}, fp16, "
+                                    f"random weights",
+                        "ms_per_image_graph": round(graph_ms, 4),
+                        "ms_per_image_eager": round(eager_ms, 4)}
+            log(f"  backbone: graph {graph_ms:.3f} ms, eager {eager_ms:.3f} ms per image")
+        except Exception as exc:  # report, do not hide
+            backbone = {"error": str(exc)[:300]}
     cpu = None
     if not args.no_cpu:
         log("  timing the fp64 oracle on the host (bounded sample)")
@@ -621,6 +670,7 @@ def main():
         "extra_1p6k": extra,
         "lowrank_gate": lowrank,
         "sswiglu_mix": sswiglu,
+        "backbone_640": backbone,
     }
     print(json.dumps(line), flush=True)
 
