@@ -24,6 +24,9 @@ from the expanded projection u = [gate | value], m = SiLU(gate) * (DWConv(value)
 + bias), zero padding, cross-correlation as in common deep-learning
 frameworks.
 
+``backward.bwd`` (module ``oracle.backward``) is the fp64 backward pass of one
+mixer call, written from the chain rule.
+
 ``round_io`` is this package's own IEEE round-to-nearest-even to the I/O type.
 """
 from __future__ import annotations
