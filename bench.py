@@ -309,6 +309,54 @@ def time_backbone(dev, steps):
     return cfg, eager_ms, graph_ms
 
 
+def time_backward(w, dev, hip, stream_ptr, steps, warmup):
+    """gtr_gla_bwd on the workload's inputs (one buffer set; the call moves about twice
+    the forward's bytes, so two sets already exceed the last-level cache)."""
+    lib = _lib.load()
+    x, sets = device_sets(w, 2, dev)
+    rng = np.random.default_rng(5)
+    grads = []
+    for s_ in sets:
+        dy = torch.from_numpy(W.cast_io(rng.standard_normal(x["v"].shape), w.dtype))
+        s_["dy"] = (dy.view(torch.bfloat16) if w.dtype == "bf16" else dy).to(dev)
+        grads.append({k: torch.empty_like(s_[src]) for k, src in
+                      (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dlog_g", "log_g"), ("dz", "z"),
+                       ("drms_w", "rms_w"))})
+    torch.cuda.synchronize(dev)
+
+    def run(i, events=None, n_events=0, nl=None):
+        s_, g_ = sets[i % 2], grads[i % 2]
+        _lib.check(lib.gtr_gla_bwd(
+            s_["q"].data_ptr(), s_["k"].data_ptr(), s_["v"].data_ptr(), s_["log_g"].data_ptr(),
+            s_["z"].data_ptr(), s_["rms_w"].data_ptr(), s_["dy"].data_ptr(), g_["dq"].data_ptr(),
+            g_["dk"].data_ptr(), g_["dv"].data_ptr(), g_["dlog_g"].data_ptr(), g_["dz"].data_ptr(),
+            g_["drms_w"].data_ptr(), w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, 0, w.chunk,
+            W.DTYPE_CODE[w.dtype], events, n_events, nl, stream_ptr))
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize(dev)
+    ev = hip.events(2)
+    hip.record(ev[0], stream_ptr)
+    for i in range(steps):
+        run(i)
+    hip.record(ev[1], stream_ptr)
+    us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+    torch.cuda.synchronize(dev)
+    hip.destroy(ev)
+    evs = hip.events(10)
+    nl = ctypes.c_int(0)
+    per = []
+    for i in range(5):
+        run(i, evs, 10, ctypes.byref(nl))
+        torch.cuda.synchronize(dev)
+        per.append([hip.elapsed_ms(evs[j], evs[j + 1]) * 1e3 for j in range(nl.value)])
+    hip.destroy(evs)
+    del sets, grads
+    torch.cuda.empty_cache()
+    return us, [statistics.fmean(p[j] for p in per) for j in range(len(per[0]))]
+
+
 def graph_time(lib, w, sets, n_sets, dev, direction, chunk, path, steps):
     """hipGraph replay of one call per buffer set (the pages' own kernel benchmark
     used graph launch); microseconds per call."""
@@ -620,6 +668,25 @@ def main():
                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                              "rotating_sets": r["n_sets"]}
             log(f"  {name}: {r['us_per_call']:.2f} us/call, {gbs:.0f} GB/s")
+    backward = None
+    if not args.no_extra:
+        try:
+            bus, blaunch = time_backward(w, dev, hip, sp, max(10, args.steps // 4), 3)
+            s_io = W.DTYPE_BYTES[w.dtype]
+            bbytes = w.tokens * w.H * ((2 * w.dk + 3 * w.dv) * s_io + 4 * w.dk      # reads
+                                       + (2 * w.dk + 2 * w.dv) * s_io + 4 * w.dk)   # writes
+            names_b = ("forward_chunk_summary", "forward_state_scan", "forward_walk_dq",
+                       "reverse_chunk_summary", "reverse_state_scan", "reverse_walk_dk_dv",
+                       "gate_total_scan", "gate_offsets", "rms_w_sum")
+            backward = {"workload": f"{w.name}: backward of one call, fp32 arithmetic",
+                        "us_per_call": round(bus, 3),
+                        "tokens_per_s": round(w.tokens / (bus * 1e-6), 1),
+                        "algorithmic_bytes": bbytes,
+                        "hbm_frac": round(bbytes / (bus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "launch_us_mean": {n: round(t, 2) for n, t in zip(names_b, blaunch)}}
+            log(f"  backward: {bus:.1f} us/call, launches {['%.1f' % t for t in blaunch]}")
+        except Exception as exc:  # report, do not hide
+            backward = {"error": str(exc)[:300]}
     backbone = None
     if not args.no_extra:
         try:
@@ -671,6 +738,7 @@ def main():
         "lowrank_gate": lowrank,
         "sswiglu_mix": sswiglu,
         "backbone_640": backbone,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
 

@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import (GtrError, PATH_AUTO, PATH_FAST, PATH_MFMA, PATH_SERIAL)  # noqa: F401
 
-__all__ = ["gla_fwd", "gla_stack_fwd", "gla_lowrank_fwd", "sswiglu_mix", "GtrError", "DIRECTIONS", "dtype_code", "version"]
+__all__ = ["gla_fwd", "gla_stack_fwd", "gla_lowrank_fwd", "gla_bwd", "sswiglu_mix", "GtrError", "DIRECTIONS", "dtype_code", "version"]
 
 DIRECTIONS = {"LR": 0, "RL": 1, "TB": 2, "BT": 3}
 _DT = {torch.float32: _lib.GTR_F32, torch.float16: _lib.GTR_F16, torch.bfloat16: _lib.GTR_BF16}
@@ -182,3 +182,41 @@ def sswiglu_mix(u, w_conv, b_conv, out=None):
                                  dtype_code(u.dtype), _stream_ptr(dev))
     _lib.check(st)
     return out
+
+
+def gla_bwd(q, k, v, log_g, z, rms_w, dout, direction=0, chunk: int = 0, events=None):
+    """Backward pass of ``gla_fwd`` (same inputs, no residual) given dout = dL/dout.
+
+    Returns (grads, n_launches) with grads a dict of dq, dk, dv (I/O dtype), dlog_g
+    (float32), dz (I/O dtype) and drms_w ([dv] float32)."""
+    import ctypes
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    B, gh, gw, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or log_g.shape != q.shape or v.shape != (B, gh, gw, H, dv) or \
+            z.shape != v.shape or dout.shape != v.shape or rms_w.shape != (dv,):
+        raise ValueError("shape mismatch")
+    if not (q.dtype == k.dtype == v.dtype == z.dtype == dout.dtype):
+        raise TypeError("q, k, v, z, dout must share one dtype")
+    if log_g.dtype != torch.float32 or rms_w.dtype != torch.float32:
+        raise TypeError("log_g and rms_w must be float32")
+    _check_tensors((("q", q), ("k", k), ("v", v), ("log_g", log_g), ("z", z),
+                    ("rms_w", rms_w), ("dout", dout)), dev)
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+         "dlog_g": torch.empty_like(log_g), "dz": torch.empty_like(z),
+         "drms_w": torch.empty_like(rms_w)}
+    n_ev = 0 if events is None else len(events)
+    ev_arr = (ctypes.c_void_p * max(1, n_ev))(*(events or []))
+    n_launch = ctypes.c_int(0)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        st = lib.gtr_gla_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_g.data_ptr(),
+                             z.data_ptr(), rms_w.data_ptr(), dout.data_ptr(), g["dq"].data_ptr(),
+                             g["dk"].data_ptr(), g["dv"].data_ptr(), g["dlog_g"].data_ptr(),
+                             g["dz"].data_ptr(), g["drms_w"].data_ptr(), B, H, gh, gw, dk, dv,
+                             _dir(direction), int(chunk), dtype_code(q.dtype), ev_arr, n_ev,
+                             ctypes.byref(n_launch), _stream_ptr(dev))
+    _lib.check(st)
+    return g, n_launch.value

@@ -478,6 +478,65 @@ gtr_status gtr_gla_lowrank_fwd(const void *q, const void *k, const void *v, cons
     return s;
 }
 
+static hipError_t mark_after(void *ctx, hipStream_t st) {
+    return static_cast<Marks *>(ctx)->after_launch(st);
+}
+
+gtr_status gtr_gla_bwd(const void *q, const void *k, const void *v, const float *log_g,
+                       const void *z, const float *rms_w, const void *dout, void *dq, void *dk,
+                       void *dv, float *dlog_g, void *dz, float *drms_w, int B, int H,
+                       int grid_h, int grid_w, int dk_, int dv_, int direction, int chunk,
+                       gtr_dtype dtype, hipEvent_t *events, int n_events, int *n_launches,
+                       hipStream_t stream) {
+    g_err.clear();
+    if (n_launches) *n_launches = 0;
+    if (n_events < 0 || (n_events > 0 && !events))
+        return fail(GTR_ERR_ARG, "events: need n_events >= 0 and a non-null array");
+    if (!dout || !dq || !dk || !dv || !dlog_g || !dz || !drms_w)
+        return fail(GTR_ERR_ARG, "null gradient pointer");
+    gtr_status s = check(q, k, v, log_g, z, rms_w, dq, B, H, grid_h, grid_w, dk_, dv_, direction,
+                         chunk, dtype, GTR_PATH_AUTO);
+    if (s != GTR_OK) return s;
+    const size_t rows = static_cast<size_t>(B) * grid_h * grid_w * H;
+    const size_t eb = elem_bytes(dtype);
+    const void *bufs[] = {q, k, v, log_g, z, rms_w, dout, dq, dk, dv, dlog_g, dz, drms_w};
+    const size_t nb[] = {rows * dk_ * eb, rows * dk_ * eb, rows * dv_ * eb, rows * dk_ * 4,
+                         rows * dv_ * eb, static_cast<size_t>(dv_) * 4, rows * dv_ * eb,
+                         rows * dk_ * eb, rows * dk_ * eb, rows * dv_ * eb, rows * dk_ * 4,
+                         rows * dv_ * eb, static_cast<size_t>(dv_) * 4};
+    for (int o = 7; o < 13; ++o) {  // every gradient against every other buffer
+        for (int i = 0; i < 13; ++i) {
+            if (i == o) continue;
+            const char *a0 = static_cast<const char *>(bufs[i]), *a1 = a0 + nb[i];
+            const char *o0 = static_cast<const char *>(bufs[o]), *o1 = o0 + nb[o];
+            if (a0 < o1 && o0 < a1) return fail(GTR_ERR_ARG, "gradient %d overlaps buffer %d", o - 7, i);
+        }
+    }
+    if (!device_ok()) return GTR_ERR_HIP;
+    GlaArgs a{q, k, v, log_g, z, rms_w, nullptr, nullptr, B, H, grid_h, grid_w, dk_, dv_,
+              direction, chunk ? chunk : kDefaultChunk, dtype,
+              static_cast<int64_t>(grid_h) * grid_w};
+    const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
+    if (static_cast<int64_t>(B) * H * n_chunks > 0x7fffffff)
+        return fail(GTR_ERR_UNSUPPORTED, "too many chunks");
+    void *ws = nullptr;
+    s = workspace(stream, bwd_workspace_bytes(a, static_cast<int>(n_chunks)), &ws);
+    if (s != GTR_OK) return s;
+    Marks mk;
+    mk.ev = events;
+    mk.n = n_events;
+    BwdLaunchHooks hooks;
+    hooks.fn = mark_after;
+    hooks.ctx = &mk;
+    hipError_t e = mk.start(stream);
+    if (e == hipSuccess)
+        e = bwd_launch(a, dout, dq, dk, dv, dlog_g, dz, drms_w, ws, static_cast<int>(n_chunks),
+                       stream, hooks);
+    if (n_launches) *n_launches = mk.launches;
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return GTR_OK;
+}
+
 gtr_status gtr_sswiglu_mix(const void *u, const float *w_conv, const float *b_conv, void *m,
                            int B, int grid_h, int grid_w, int F, int k, gtr_dtype dtype,
                            hipStream_t stream) {

@@ -183,6 +183,17 @@ bool lowrank_fused_supported(const GlaArgs &a);
 // value + bias) from u = [gate | value].
 hipError_t sswiglu_launch(const void *u, const float *w, const float *b, void *m, int B, int gh,
                           int gw, int F, int k, int dtype, hipStream_t s);
+// Backward pass (k_bwd.hip), fp32 chunk-parallel.  hooks.after() runs after every
+// launch (event recording).  ws: bwd_workspace_bytes(a, n_chunks) bytes.
+struct BwdLaunchHooks {
+    hipError_t (*fn)(void *ctx, hipStream_t st) = nullptr;
+    void *ctx = nullptr;
+    hipError_t after(hipStream_t st) const { return fn ? fn(ctx, st) : hipSuccess; }
+};
+size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks);
+hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
+                      float *dlog_g, void *dz, float *drms_w, void *ws, int n_chunks,
+                      hipStream_t st, const BwdLaunchHooks &hooks);
 // State scan over the segments of a plan, in place: U[k] <- state before segment k.
 hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,
                            int dv, hipStream_t s);

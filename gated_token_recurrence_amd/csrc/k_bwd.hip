@@ -1,0 +1,620 @@
+// k_bwd.hip -- backward pass of one mixer call, fp32, chunk-parallel.
+//
+// GTR write-up ("端侧实时感知新标杆！通用线性骨干网络GTR开源"), Method §1 gives the
+// forward: S_t = Diag(g_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, then RMSNorm,
+// the rms_w weight and the SiLU(z) gate; Method §4 its chunkwise evaluation
+// (chunk summaries, a boundary-state scan, per-chunk outputs), which the
+// backward mirrors in both directions.  With dy the gradient of the output:
+//   epilogue   r = (mean(o^2) + eps)^-1/2, n = r o:  dn = dy w silu(z),
+//              do = r (dn - n mean(dn n)),  dz = dy n w silu'(z),  drms_w = sum dy n silu(z)
+//   forward    dq_t = S_t do_t                         (S_t from the chunk's incoming state)
+//   reverse    dS_t = q_t do_t^T + Diag(g_{t+1}) dS_{t+1},  dk_t = dS_t v_t,  dv_t = dS_t^T k_t
+//   gate       dlog_g_t = sum_{s >= t} (q_s dq_s - k_s dk_s)   (reverse cumulative sum; the
+//              derivative of the loss with respect to the cumulative log-gate at step s is
+//              q_s dq_s - k_s dk_s, and log g_t enters every cumulative sum from t on)
+// The reverse recurrence has the same form as the forward one read backwards:
+// a chunk's dS summary from zero, E = Diag(g_first) dS_first, chains across chunks
+// as E_{n-1} = Diag(exp(Gamma_n)) E_n + (summary of chunk n), so the forward scan
+// kernel runs it over the chunks in reversed order.
+//
+// Every kernel is token-serial inside a chunk, one workgroup per (b, h, chunk),
+// with the dk x dv state (or its gradient) in registers.  Two thread->state maps:
+//   A: column j = tid % DV, channels c0 + CSTEP m (c0 = tid / DV): sums over
+//      channels (o_t, dv_t) are per-thread partials added across CSTEP groups;
+//   B: channel c = tid % DK, columns j0 + JSTEP m (j0 = tid / DK): sums over columns
+//      (dq_t, dk_t) likewise.
+// Where a chunk needs sums along both axes it is walked twice, once per map.
+#include "gtr_internal.hpp"
+
+namespace gtr {
+namespace {
+
+constexpr int NT = 256;
+
+template <int DK, int DV> struct BwdShape {
+    static constexpr int PER = DK * DV / NT;      // state elements per thread
+    static constexpr int CSTEP = NT / DV;         // map A: channel stride
+    static constexpr int JSTEP = NT / DK;         // map B: column stride
+    static constexpr int TILE = (DK + DV > 128) ? 8 : 16;
+    static constexpr int RG = CSTEP > JSTEP ? CSTEP : JSTEP;
+    static constexpr int RW = DK > DV ? DK : DV;
+};
+
+struct BwdArgs {
+    GlaArgs a;
+    const void *dy;      // gradient of out, I/O type
+    const float *Sx;     // forward incoming state per chunk [bh N + n][DK][DV]
+    const float *Er;     // reverse incoming gradient state per chunk, reversed order
+    float *dO;           // [rows][DV]
+    float *qdq;          // [rows][DK]
+    float *Ur, *Gr;      // reverse summaries and chunk gates, reversed chunk order
+    float *Tn;           // [bh N + n][DK] chunk totals of q dq - k dk
+    float *dWp;          // [bh N + n][DV] drms_w partials
+    void *dq, *dk, *dv, *dz;
+    float *dlog_g, *drms_w;
+    int n_chunks;
+};
+
+// Chunk of this workgroup and its token range
+struct ChunkPos {
+    int n, bh, b, h;
+    int64_t t0, t1;
+    __device__ ChunkPos(const GlaArgs &a, int n_chunks) {
+        n = blockIdx.x % n_chunks;
+        bh = blockIdx.x / n_chunks;
+        b = bh / a.H;
+        h = bh % a.H;
+        t0 = static_cast<int64_t>(n) * a.chunk;
+        t1 = (t0 + a.chunk < a.L) ? t0 + a.chunk : a.L;
+    }
+    __device__ size_t cid() const { return static_cast<size_t>(blockIdx.x); }
+};
+
+// ---- B1: forward walk.  Pass 1 (map A): o_t, epilogue backward -> do_t (global),
+// dz_t, drms_w partials.  Pass 2 (map B): dq_t = S_t do_t, q dq (fp32, global).
+template <int DT, int DK, int DV>
+__global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
+    using Sh = BwdShape<DK, DV>;
+    constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, JSTEP = Sh::JSTEP, TILE = Sh::TILE;
+    const GlaArgs &a = p.a;
+    __shared__ float sq[TILE][DK], sk[TILE][DK], sg[TILE][DK];
+    __shared__ float sv[TILE][DV], sz[TILE][DV], sdy[TILE][DV], so[TILE][DV], sdn[TILE][DV];
+    __shared__ float red[TILE][Sh::RG][Sh::RW];
+    __shared__ float swp[NT];
+    __shared__ float sinv[TILE], smdn[TILE];  // per token: RMSNorm factor, mean(dn n)
+    __shared__ int64_t srow[TILE];
+    const int tid = threadIdx.x;
+    const ChunkPos cp(a, p.n_chunks);
+    const size_t soff = cp.cid() * DK * DV;
+
+    // ---- pass 1, map A
+    {
+        const int j = tid % DV, c0 = tid / DV;
+        float s[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) s[m] = p.Sx[soff + static_cast<size_t>(c0 + CSTEP * m) * DV + j];
+        float wacc = 0.f;  // drms_w partial of column tid % DV
+        for (int64_t tb = cp.t0; tb < cp.t1; tb += TILE) {
+            const int nt = static_cast<int>((cp.t1 - tb < TILE) ? cp.t1 - tb : TILE);
+            __syncthreads();
+            if (tid < TILE) srow[tid] = tid < nt ? scan_row(a, cp.b, cp.h, tb + tid) : 0;
+            __syncthreads();
+            for (int i = tid; i < TILE * DK; i += NT) {
+                const int tt = i / DK, c = i % DK;
+                float kk = 0.f, lg = 0.f, qq = 0.f;
+                if (tt < nt) {
+                    const int64_t r = srow[tt] * DK + c;
+                    kk = ld<DT>(a.k, r);
+                    lg = a.log_g[r];
+                    qq = ld<DT>(a.q, r);
+                }
+                sk[tt][c] = kk;
+                sg[tt][c] = expf(lg);
+                sq[tt][c] = qq;
+            }
+            for (int i = tid; i < TILE * DV; i += NT) {
+                const int tt = i / DV, jj = i % DV;
+                float vv = 0.f, zz = 0.f, gy = 0.f;
+                if (tt < nt) {
+                    const int64_t r = srow[tt] * DV + jj;
+                    vv = ld<DT>(a.v, r);
+                    zz = ld<DT>(a.z, r);
+                    gy = ld<DT>(p.dy, r);
+                }
+                sv[tt][jj] = vv;
+                sz[tt][jj] = zz;
+                sdy[tt][jj] = gy;
+            }
+            __syncthreads();
+            for (int tt = 0; tt < nt; ++tt) {
+                const float vj = sv[tt][j];
+                float part = 0.f;
+#pragma unroll
+                for (int m = 0; m < PER; ++m) {
+                    const int c = c0 + CSTEP * m;
+                    s[m] = sg[tt][c] * s[m] + sk[tt][c] * vj;
+                    part += s[m] * sq[tt][c];
+                }
+                red[tt][c0][j] = part;
+            }
+            __syncthreads();
+            for (int i = tid; i < TILE * DV; i += NT) {
+                const int tt = i / DV, jj = i % DV;
+                float o = 0.f;
+#pragma unroll
+                for (int r = 0; r < CSTEP; ++r) o += red[tt][r][jj];
+                so[tt][jj] = o;
+            }
+            __syncthreads();
+            if (tid < nt) {  // one thread per token: the RMSNorm factor
+                float ss = 0.f;
+                for (int x = 0; x < DV; ++x) ss += so[tid][x] * so[tid][x];
+                sinv[tid] = 1.0f / sqrtf(ss / DV + GTR_RMS_EPS);
+            }
+            __syncthreads();
+            // epilogue backward, element (tt, jj) = (i / DV, i % DV), i = tid + u NT; jj is
+            // tid % DV for every u (NT is a multiple of DV)
+            constexpr int ITER = TILE * DV / NT;
+            float nn[ITER], inv_t[ITER];
+#pragma unroll
+            for (int u = 0; u < ITER; ++u) {
+                const int i = tid + u * NT;
+                nn[u] = inv_t[u] = 0.f;
+                if (i < nt * DV) {
+                    const int tt = i / DV, jj = i % DV;
+                    const float inv = sinv[tt];
+                    const float n = so[tt][jj] * inv;
+                    const float zz = sz[tt][jj];
+                    const float sig = 1.0f / (1.0f + expf(-zz));
+                    const float silu = zz * sig;
+                    const float gy = sdy[tt][jj];
+                    const float w = a.rms_w[jj];
+                    sdn[tt][jj] = gy * w * silu * n;  // dn * n, for the projection term
+                    wacc += gy * n * silu;
+                    st<DT>(p.dz, srow[tt] * DV + jj, gy * n * w * sig * (1.0f + zz * (1.0f - sig)));
+                    nn[u] = n;
+                    inv_t[u] = inv;
+                }
+            }
+            __syncthreads();
+            if (tid < nt) {
+                float mdn = 0.f;
+                for (int x = 0; x < DV; ++x) mdn += sdn[tid][x];
+                smdn[tid] = mdn * (1.0f / DV);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < ITER; ++u) {
+                const int i = tid + u * NT;
+                if (i < nt * DV) {
+                    const int tt = i / DV, jj = i % DV;
+                    const float mdn = smdn[tt];
+                    const float zz = sz[tt][jj];
+                    const float silu = zz / (1.0f + expf(-zz));
+                    const float dn = sdy[tt][jj] * a.rms_w[jj] * silu;
+                    p.dO[srow[tt] * DV + jj] = inv_t[u] * (dn - nn[u] * mdn);
+                }
+            }
+        }
+        swp[tid] = wacc;
+        __syncthreads();
+        if (tid < DV) {
+            float w = 0.f;
+            for (int r = tid; r < NT; r += DV) w += swp[r];
+            p.dWp[cp.cid() * DV + tid] = w;
+        }
+    }
+    __syncthreads();  // this workgroup's do_t writes are visible to its own reads below
+
+    // ---- pass 2, map B: dq_t = S_t do_t
+    {
+        const int c = tid % DK, j0 = tid / DK;
+        float s[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) s[m] = p.Sx[soff + static_cast<size_t>(c) * DV + j0 + JSTEP * m];
+        for (int64_t tb = cp.t0; tb < cp.t1; tb += TILE) {
+            const int nt = static_cast<int>((cp.t1 - tb < TILE) ? cp.t1 - tb : TILE);
+            __syncthreads();
+            if (tid < TILE) srow[tid] = tid < nt ? scan_row(a, cp.b, cp.h, tb + tid) : 0;
+            __syncthreads();
+            for (int i = tid; i < TILE * DK; i += NT) {
+                const int tt = i / DK, cc = i % DK;
+                float kk = 0.f, lg = 0.f, qq = 0.f;
+                if (tt < nt) {
+                    const int64_t r = srow[tt] * DK + cc;
+                    kk = ld<DT>(a.k, r);
+                    lg = a.log_g[r];
+                    qq = ld<DT>(a.q, r);
+                }
+                sk[tt][cc] = kk;
+                sg[tt][cc] = expf(lg);
+                sq[tt][cc] = qq;
+            }
+            for (int i = tid; i < TILE * DV; i += NT) {
+                const int tt = i / DV, jj = i % DV;
+                float vv = 0.f, dd = 0.f;
+                if (tt < nt) {
+                    const int64_t r = srow[tt] * DV + jj;
+                    vv = ld<DT>(a.v, r);
+                    dd = p.dO[r];
+                }
+                sv[tt][jj] = vv;
+                so[tt][jj] = dd;  // do_t
+            }
+            __syncthreads();
+            for (int tt = 0; tt < nt; ++tt) {
+                const float g = sg[tt][c], kc = sk[tt][c];
+                float part = 0.f;
+#pragma unroll
+                for (int m = 0; m < PER; ++m) {
+                    const int j = j0 + JSTEP * m;
+                    s[m] = g * s[m] + kc * sv[tt][j];
+                    part += s[m] * so[tt][j];
+                }
+                red[tt][j0][c] = part;
+            }
+            __syncthreads();
+            for (int i = tid; i < nt * DK; i += NT) {
+                const int tt = i / DK, cc = i % DK;
+                float d = 0.f;
+#pragma unroll
+                for (int r = 0; r < JSTEP; ++r) d += red[tt][r][cc];
+                const int64_t r = srow[tt] * DK + cc;
+                st<DT>(p.dq, r, d);
+                p.qdq[r] = sq[tt][cc] * d;
+            }
+        }
+    }
+}
+
+// ---- B2: reverse summary of each chunk (map A; no sums): dS walked from the
+// chunk's last token to its first from zero, then Diag(g_first) dS; written with
+// the chunk's summed log-gate at the reversed chunk index.
+template <int DT, int DK, int DV>
+__global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
+    using Sh = BwdShape<DK, DV>;
+    constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, TILE = Sh::TILE;
+    const GlaArgs &a = p.a;
+    __shared__ float sq[TILE][DK], sg[TILE][DK], sdo[TILE][DV];
+    __shared__ float gpart[NT];
+    __shared__ int64_t srow[TILE];
+    const int tid = threadIdx.x;
+    const ChunkPos cp(a, p.n_chunks);
+    const int j = tid % DV, c0 = tid / DV;
+    float s[PER], gnext[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) s[m] = 0.f, gnext[m] = 0.f;  // no decay before the last token
+    float gacc = 0.f;
+    const int64_t len = cp.t1 - cp.t0;
+    const int64_t ntiles = (len + TILE - 1) / TILE;
+    for (int64_t ti = ntiles - 1; ti >= 0; --ti) {
+        const int64_t tb = cp.t0 + ti * TILE;
+        const int nt = static_cast<int>((cp.t1 - tb < TILE) ? cp.t1 - tb : TILE);
+        __syncthreads();
+        if (tid < TILE) srow[tid] = tid < nt ? scan_row(a, cp.b, cp.h, tb + tid) : 0;
+        __syncthreads();
+        for (int i = tid; i < TILE * DK; i += NT) {
+            const int tt = i / DK, c = i % DK;
+            float lg = 0.f, qq = 0.f;
+            if (tt < nt) {
+                const int64_t r = srow[tt] * DK + c;
+                lg = a.log_g[r];
+                qq = ld<DT>(a.q, r);
+            }
+            sg[tt][c] = expf(lg);
+            sq[tt][c] = qq;
+            gacc += lg;
+        }
+        for (int i = tid; i < TILE * DV; i += NT) {
+            const int tt = i / DV, jj = i % DV;
+            sdo[tt][jj] = tt < nt ? p.dO[srow[tt] * DV + jj] : 0.f;
+        }
+        __syncthreads();
+        for (int tt = nt - 1; tt >= 0; --tt) {
+            const float dj = sdo[tt][j];
+#pragma unroll
+            for (int m = 0; m < PER; ++m) {
+                const int c = c0 + CSTEP * m;
+                s[m] = gnext[m] * s[m] + sq[tt][c] * dj;
+                gnext[m] = sg[tt][c];
+            }
+        }
+    }
+    // E contribution: Diag(g of the chunk's first token) dS_first
+    const size_t ridx = static_cast<size_t>(cp.bh) * p.n_chunks + (p.n_chunks - 1 - cp.n);
+#pragma unroll
+    for (int m = 0; m < PER; ++m)
+        p.Ur[ridx * DK * DV + static_cast<size_t>(c0 + CSTEP * m) * DV + j] = gnext[m] * s[m];
+    gpart[tid] = gacc;
+    __syncthreads();
+    if (tid < DK) {
+        float gsum = 0.f;
+        for (int r = tid; r < NT; r += DK) gsum += gpart[r];
+        p.Gr[ridx * DK + tid] = gsum;
+    }
+}
+
+// ---- B3: reverse walk from the incoming gradient state E.  Pass A (map B):
+// dk_t = dS_t v_t, then q dq - k dk, its reverse cumulative sum inside the chunk
+// (written as dlog_g, completed by B4) and the chunk total.  Pass B (map A):
+// dv_t = dS_t^T k_t.
+template <int DT, int DK, int DV>
+__global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
+    using Sh = BwdShape<DK, DV>;
+    constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, JSTEP = Sh::JSTEP, TILE = Sh::TILE;
+    const GlaArgs &a = p.a;
+    __shared__ float sq[TILE][DK], sk[TILE][DK], sg[TILE][DK];
+    __shared__ float sv[TILE][DV], sdo[TILE][DV];
+    __shared__ float red[TILE][Sh::RG][Sh::RW];
+    __shared__ float sacc[DK];
+    __shared__ int64_t srow[TILE];
+    const int tid = threadIdx.x;
+    const ChunkPos cp(a, p.n_chunks);
+    const size_t eoff = (static_cast<size_t>(cp.bh) * p.n_chunks + (p.n_chunks - 1 - cp.n)) * DK * DV;
+    const int64_t len = cp.t1 - cp.t0;
+    const int64_t ntiles = (len + TILE - 1) / TILE;
+
+    auto load_tile = [&](int64_t tb, int nt) {
+        __syncthreads();
+        if (tid < TILE) srow[tid] = tid < nt ? scan_row(a, cp.b, cp.h, tb + tid) : 0;
+        __syncthreads();
+        for (int i = tid; i < TILE * DK; i += NT) {
+            const int tt = i / DK, c = i % DK;
+            float kk = 0.f, lg = 0.f, qq = 0.f;
+            if (tt < nt) {
+                const int64_t r = srow[tt] * DK + c;
+                kk = ld<DT>(a.k, r);
+                lg = a.log_g[r];
+                qq = ld<DT>(a.q, r);
+            }
+            sk[tt][c] = kk;
+            sg[tt][c] = expf(lg);
+            sq[tt][c] = qq;
+        }
+        for (int i = tid; i < TILE * DV; i += NT) {
+            const int tt = i / DV, jj = i % DV;
+            float vv = 0.f, dd = 0.f;
+            if (tt < nt) {
+                const int64_t r = srow[tt] * DV + jj;
+                vv = ld<DT>(a.v, r);
+                dd = p.dO[r];
+            }
+            sv[tt][jj] = vv;
+            sdo[tt][jj] = dd;
+        }
+        __syncthreads();
+    };
+
+    // ---- pass A, map B
+    {
+        const int c = tid % DK, j0 = tid / DK;
+        float s[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) s[m] = p.Er[eoff + static_cast<size_t>(c) * DV + j0 + JSTEP * m];
+        float gnext = 1.f;  // E already carries the next chunk's first gate
+        if (tid < DK) sacc[tid] = 0.f;
+        for (int64_t ti = ntiles - 1; ti >= 0; --ti) {
+            const int64_t tb = cp.t0 + ti * TILE;
+            const int nt = static_cast<int>((cp.t1 - tb < TILE) ? cp.t1 - tb : TILE);
+            load_tile(tb, nt);
+            for (int tt = nt - 1; tt >= 0; --tt) {
+                const float qc = sq[tt][c];
+                float part = 0.f;
+#pragma unroll
+                for (int m = 0; m < PER; ++m) {
+                    const int j = j0 + JSTEP * m;
+                    s[m] = gnext * s[m] + qc * sdo[tt][j];
+                    part += s[m] * sv[tt][j];
+                }
+                gnext = sg[tt][c];
+                red[tt][j0][c] = part;
+            }
+            __syncthreads();
+            // dk, then the in-chunk reverse cumulative sum of q dq - k dk (thread c < DK
+            // walks the tile's tokens last to first)
+            for (int i = tid; i < nt * DK; i += NT) {
+                const int tt = i / DK, cc = i % DK;
+                float d = 0.f;
+#pragma unroll
+                for (int r = 0; r < JSTEP; ++r) d += red[tt][r][cc];
+                st<DT>(p.dk, srow[tt] * DK + cc, d);
+                red[tt][0][cc] = d;  // reuse: dk of (tt, cc)
+            }
+            __syncthreads();
+            if (tid < DK) {
+                float acc = sacc[tid];
+                for (int tt = nt - 1; tt >= 0; --tt) {
+                    const int64_t r = srow[tt] * DK + tid;
+                    acc += p.qdq[r] - sk[tt][tid] * red[tt][0][tid];
+                    p.dlog_g[r] = acc;
+                }
+                sacc[tid] = acc;
+            }
+        }
+        __syncthreads();
+        if (tid < DK) p.Tn[cp.cid() * DK + tid] = sacc[tid];
+    }
+
+    // ---- pass B, map A: dv_t = dS_t^T k_t
+    {
+        const int j = tid % DV, c0 = tid / DV;
+        float s[PER], gnext[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            s[m] = p.Er[eoff + static_cast<size_t>(c0 + CSTEP * m) * DV + j];
+            gnext[m] = 1.f;
+        }
+        for (int64_t ti = ntiles - 1; ti >= 0; --ti) {
+            const int64_t tb = cp.t0 + ti * TILE;
+            const int nt = static_cast<int>((cp.t1 - tb < TILE) ? cp.t1 - tb : TILE);
+            load_tile(tb, nt);
+            for (int tt = nt - 1; tt >= 0; --tt) {
+                const float dj = sdo[tt][j];
+                float part = 0.f;
+#pragma unroll
+                for (int m = 0; m < PER; ++m) {
+                    const int c = c0 + CSTEP * m;
+                    s[m] = gnext[m] * s[m] + sq[tt][c] * dj;
+                    gnext[m] = sg[tt][c];
+                    part += s[m] * sk[tt][c];
+                }
+                red[tt][c0][j] = part;
+            }
+            __syncthreads();
+            for (int i = tid; i < nt * DV; i += NT) {
+                const int tt = i / DV, jj = i % DV;
+                float d = 0.f;
+#pragma unroll
+                for (int r = 0; r < CSTEP; ++r) d += red[tt][r][jj];
+                st<DT>(p.dv, srow[tt] * DV + jj, d);
+            }
+        }
+    }
+}
+
+// ---- B4a: Tn[n] <- sum of the totals of the sequence's later chunks (exclusive
+// reverse scan, in place).  Thread = (sequence, channel); the loads of 16 chunks
+// are issued before their sums.
+__global__ __launch_bounds__(NT) void k_bwd_gatescan(float *__restrict__ Tn, int n_seq,
+                                                     int n_chunks, int dk) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+    if (i >= static_cast<int64_t>(n_seq) * dk) return;
+    const int64_t seq = i / dk;
+    const int c = static_cast<int>(i % dk);
+    float *t = Tn + seq * n_chunks * dk + c;
+    float acc = 0.f;
+    for (int n1 = n_chunks; n1 > 0; n1 -= 16) {
+        const int n0 = n1 - 16 > 0 ? n1 - 16 : 0;
+        float x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x[u] = (n0 + u < n1) ? t[static_cast<int64_t>(n0 + u) * dk] : 0.f;
+#pragma unroll
+        for (int u = 15; u >= 0; --u) {
+            if (n0 + u < n1) {
+                t[static_cast<int64_t>(n0 + u) * dk] = acc;
+                acc += x[u];
+            }
+        }
+    }
+}
+
+// ---- B4b: dlog_g of chunk n += the scanned totals of the later chunks.
+template <int DK>
+__global__ __launch_bounds__(NT) void k_bwd_gateoff(BwdArgs p) {
+    const GlaArgs &a = p.a;
+    __shared__ float soff[DK];
+    const int tid = threadIdx.x;
+    const ChunkPos cp(a, p.n_chunks);
+    if (tid < DK) soff[tid] = p.Tn[cp.cid() * DK + tid];
+    __syncthreads();
+    const int64_t len = cp.t1 - cp.t0;
+    for (int64_t i = tid; i < len * DK; i += NT) {
+        const int64_t tt = i / DK;
+        const int c = static_cast<int>(i % DK);
+        const int64_t r = scan_row(a, cp.b, cp.h, cp.t0 + tt) * DK + c;
+        p.dlog_g[r] += soff[c];
+    }
+}
+
+// ---- B5: drms_w = sum of the per-chunk partials (fixed order): 1024 threads, each
+// column summed by 1024 / DV threads over strided rows (8 loads in flight each),
+// then their partials in order.
+constexpr int WS_THREADS = 1024;
+template <int DV>
+__global__ __launch_bounds__(WS_THREADS) void k_bwd_wsum(BwdArgs p, int64_t n_parts) {
+    __shared__ float part[WS_THREADS];
+    const int tid = threadIdx.x;
+    const int j = tid % DV, g = tid / DV;
+    constexpr int GS = WS_THREADS / DV;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int64_t r0 = g; r0 < n_parts; r0 += 8 * GS) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t r = r0 + static_cast<int64_t>(u) * GS;
+            acc[u] += (r < n_parts) ? p.dWp[r * DV + j] : 0.f;
+        }
+    }
+    part[tid] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    __syncthreads();
+    if (tid < DV) {
+        float w = 0.f;
+        for (int r = 0; r < GS; ++r) w += part[r * DV + tid];
+        p.drms_w[tid] = w;
+    }
+}
+
+template <int DT, int DK, int DV>
+hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hooks) {
+    const int64_t ncb = static_cast<int64_t>(p.a.B) * p.a.H * p.n_chunks;
+    const dim3 grid(static_cast<unsigned>(ncb));
+    auto done = [&]() {
+        const hipError_t e = hipGetLastError();
+        return e != hipSuccess ? e : hooks.after(st);
+    };
+    hipError_t e;
+    hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV>), grid, dim3(NT), 0, st, p);
+    if ((e = done()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_revsum<DT, DK, DV>), grid, dim3(NT), 0, st, p);
+    if ((e = done()) != hipSuccess) return e;
+    e = state_scan(p.Ur, p.Gr, static_cast<int>(p.a.B * p.a.H), p.n_chunks, DK, DV, st);
+    if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+    BwdArgs q = p;
+    q.Er = p.Ur;  // scanned in place
+    hipLaunchKernelGGL((k_bwd_revwalk<DT, DK, DV>), grid, dim3(NT), 0, st, q);
+    if ((e = done()) != hipSuccess) return e;
+    const int64_t nsc = static_cast<int64_t>(p.a.B) * p.a.H * DK;
+    hipLaunchKernelGGL(k_bwd_gatescan, dim3(static_cast<unsigned>((nsc + NT - 1) / NT)), dim3(NT), 0,
+                       st, p.Tn, static_cast<int>(p.a.B * p.a.H), p.n_chunks, DK);
+    if ((e = done()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_gateoff<DK>), grid, dim3(NT), 0, st, q);
+    if ((e = done()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_wsum<DV>), dim3(1), dim3(WS_THREADS), 0, st, q, ncb);
+    return done();
+}
+
+template <int DT>
+hipError_t run_dt(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hooks) {
+#define GTR_BWD_CASE(DK_, DV_) \
+    if (p.a.dk == DK_ && p.a.dv == DV_) return run_shape<DT, DK_, DV_>(p, st, hooks);
+    GTR_BWD_CASE(32, 32) GTR_BWD_CASE(32, 64) GTR_BWD_CASE(32, 128)
+    GTR_BWD_CASE(64, 32) GTR_BWD_CASE(64, 64) GTR_BWD_CASE(64, 128)
+    GTR_BWD_CASE(128, 32) GTR_BWD_CASE(128, 64) GTR_BWD_CASE(128, 128)
+#undef GTR_BWD_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks) {
+    const size_t ncb = static_cast<size_t>(a.B) * a.H * n_chunks;
+    const size_t rows = static_cast<size_t>(a.B) * a.L * a.H;
+    return 4 * (2 * ncb * (static_cast<size_t>(a.dk) * a.dv + a.dk)  // forward and reverse states
+                + rows * (a.dv + a.dk)                                // do, q dq
+                + ncb * (a.dk + a.dv));                               // chunk totals, drms_w parts
+}
+
+hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
+                      float *dlog_g, void *dz, float *drms_w, void *ws, int n_chunks,
+                      hipStream_t st, const BwdLaunchHooks &hooks) {
+    const size_t ncb = static_cast<size_t>(a.B) * a.H * n_chunks;
+    const size_t rows = static_cast<size_t>(a.B) * a.L * a.H;
+    const size_t dd = static_cast<size_t>(a.dk) * a.dv;
+    float *f = static_cast<float *>(ws);
+    float *Uf = f, *Gf = Uf + ncb * dd, *Ur = Gf + ncb * a.dk, *Gr = Ur + ncb * dd;
+    float *dO = Gr + ncb * a.dk, *qdq = dO + rows * a.dv, *Tn = qdq + rows * a.dk;
+    float *dWp = Tn + ncb * a.dk;
+    // forward incoming states: the forward path's chunk summaries and scan
+    hipError_t e = serial_summary(a, Uf, Gf, n_chunks, st);
+    if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+    e = state_scan(Uf, Gf, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st);
+    if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+    BwdArgs p{a, dy, Uf, nullptr, dO, qdq, Ur, Gr, Tn, dWp, dq, dk, dv, dz, dlog_g, drms_w, n_chunks};
+    switch (a.dtype) {
+    case DT_F32: return run_dt<DT_F32>(p, st, hooks);
+    case DT_F16: return run_dt<DT_F16>(p, st, hooks);
+    case DT_BF16: return run_dt<DT_BF16>(p, st, hooks);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gtr

@@ -160,6 +160,55 @@ __global__ __launch_bounds__(NT) void k_scan_rows(float *__restrict__ U,
     }
 }
 
+// The same four-part fold for plain sequences of n_units units each (unit k of
+// sequence seq at index seq n_units + k), any dv: each lane takes its own key
+// channel.  Workgroup = (sequence, 64 consecutive state elements).
+template <int M>
+__global__ __launch_bounds__(NT) void k_scan_rows_seq(float *__restrict__ U,
+                                                      const float *__restrict__ G, int n_units,
+                                                      int dk, int dv) {
+    __shared__ float sA[4][64], sB[4][64];
+    const int64_t dd = static_cast<int64_t>(dk) * dv;
+    const uint32_t slices = static_cast<uint32_t>(dk * dv / 64);
+    const uint32_t seq32 = blockIdx.x / slices;
+    const int64_t seq = seq32;
+    const int lane = threadIdx.x & 63;
+    const int part = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t el = static_cast<int64_t>(blockIdx.x - seq32 * slices) * 64 + lane;
+    const int c = static_cast<int>(el / dv);
+    const int64_t s0 = seq * n_units, s1 = s0 + n_units;
+    const int64_t len = (n_units + 3) / 4;  // <= M (checked by the host)
+    const int64_t kb = s0 + part * len;
+    const int n = static_cast<int>(kb < s1 ? (kb + len < s1 ? len : s1 - kb) : 0);
+    float x[M], e[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int64_t k = (i < n) ? kb + i : s1 - 1;  // in bounds; unused past n
+        const float xv = U[k * dd + el];
+        const float gv = G[k * dk + c];
+        x[i] = (i < n) ? xv : 0.f;
+        e[i] = (i < n) ? expf(gv) : 1.f;
+    }
+    float A = 1.f, B = 0.f;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        B = e[i] * B + x[i];
+        A *= e[i];
+    }
+    sA[part][lane] = A;
+    sB[part][lane] = B;
+    __syncthreads();
+    float st = 0.f;
+    for (int q = 0; q < part; ++q) st = sA[q][lane] * st + sB[q][lane];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        if (i < n) {
+            U[(kb + i) * dd + el] = st;
+            st = e[i] * st + x[i];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,
@@ -183,6 +232,17 @@ hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_s
 hipError_t state_scan(float *U, const float *G, int n_seq, int n_units, int dk, int dv,
                       hipStream_t s) {
     const int64_t n_elem = static_cast<int64_t>(n_seq) * dk * dv;
+    if ((static_cast<int64_t>(dk) * dv) % 64 == 0 && n_units <= 4 * 64) {
+        // the four-part fold: memory latency paid about once per sequence
+        const dim3 grid(static_cast<unsigned>(n_elem / 64));
+        if (n_units <= 4 * 16)
+            hipLaunchKernelGGL((k_scan_rows_seq<16>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+        else if (n_units <= 4 * 32)
+            hipLaunchKernelGGL((k_scan_rows_seq<32>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+        else
+            hipLaunchKernelGGL((k_scan_rows_seq<64>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+        return hipGetLastError();
+    }
     const dim3 grid(static_cast<unsigned>((n_elem + NT - 1) / NT));
     hipLaunchKernelGGL(k_state_scan, grid, dim3(NT), 0, s, U, G, n_elem, n_units, dk, dv);
     return hipGetLastError();

@@ -162,6 +162,28 @@ gtr_status gtr_gla_lowrank_fwd(const void *q, const void *k, const void *v, cons
                                hipStream_t stream);
 
 /*
+ * Backward pass of one mixer call (gtr_gla_fwd's operation, Method §1 of the
+ * GTR write-up "端侧实时感知新标杆！通用线性骨干网络GTR开源", evaluated chunkwise as
+ * in Method §4 in both scan directions): given dout = dL/dout, writes
+ *   dq, dk : [B, grid_h, grid_w, H, dk]  I/O type
+ *   dv, dz : [B, grid_h, grid_w, H, dv]  I/O type
+ *   dlog_g : [B, grid_h, grid_w, H, dk]  float32
+ *   drms_w : [dv]                        float32 (summed over every token and head)
+ * Inputs q, k, v, log_g, z, rms_w, dims, direction and chunk as gtr_gla_fwd
+ * (no stack residual); dout has out's shape and type.  Arithmetic is fp32
+ * (the forward states are recomputed, not stored); gradients of 16-bit I/O are
+ * rounded to nearest even.  No gradient buffer may overlap another buffer.
+ * events / n_events / n_launches as gtr_gla_fwd_events (NULL / 0 allowed).
+ * Errors, ownership and asynchrony as gtr_gla_fwd.
+ */
+gtr_status gtr_gla_bwd(const void *q, const void *k, const void *v, const float *log_g,
+                       const void *z, const float *rms_w, const void *dout, void *dq, void *dk,
+                       void *dv, float *dlog_g, void *dz, float *drms_w,
+                       int B, int H, int grid_h, int grid_w, int dk_, int dv_, int direction,
+                       int chunk, gtr_dtype dtype, hipEvent_t *events, int n_events,
+                       int *n_launches, hipStream_t stream);
+
+/*
  * The fused middle of the Spatial SwiGLU feed-forward block (GTR write-up
  * "端侧实时感知新标杆！通用线性骨干网络GTR开源", Method §2 "Spatial SwiGLU": in the
  * channel expansion the value branch is reshaped to the 2-D token grid and

@@ -181,3 +181,24 @@ def test_sswiglu_null_misaligned_and_aliasing():
     p = list(PL[:4])
     p[3] = PL[0] + 64
     assert _sswiglu(ptrs=p) == _lib.GTR_ERR_ARG and "overlaps" in _lib.last_error()
+
+
+def test_bwd_argument_errors():
+    lib = _lib.load()
+    P13 = [(i + 1) << 36 for i in range(13)]
+    n = ctypes.c_int(-1)
+    # null gradient
+    args = list(P13)
+    args[9] = None
+    st = lib.gtr_gla_bwd(*args, 1, 2, 8, 8, 64, 64, 0, 0, 1, None, 0, ctypes.byref(n), None)
+    assert st == _lib.GTR_ERR_ARG and "null" in _lib.last_error() and n.value == 0
+    # a gradient on top of an input
+    args = list(P13)
+    args[7] = P13[0]
+    st = lib.gtr_gla_bwd(*args, 1, 2, 8, 8, 64, 64, 0, 0, 1, None, 0, None, None)
+    assert st == _lib.GTR_ERR_ARG and "overlaps" in _lib.last_error()
+    # bad sizes and enums go through the forward's checks
+    st = lib.gtr_gla_bwd(*P13, 1, 2, 8, 8, 48, 64, 0, 0, 1, None, 0, None, None)
+    assert st == _lib.GTR_ERR_UNSUPPORTED
+    st = lib.gtr_gla_bwd(*P13, 1, 2, 8, 8, 64, 64, 7, 0, 1, None, 0, None, None)
+    assert st == _lib.GTR_ERR_ARG

@@ -1,0 +1,127 @@
+"""GPU parity of the backward pass (gtr_gla_bwd) against the fp64 backward oracle.
+
+The kernels compute in fp32 from the same (rounded) inputs the oracle gets, so:
+float32 gradients (every gradient for float32 I/O; dlog_g and drms_w always)
+within rel-L2 1e-4 of the oracle; 16-bit gradients (dq, dk, dv, dz) within
+rel-L2 1e-3 of the oracle rounded to the I/O type.  An absolute allowance is
+added: 1e-10 per element, and for dlog_g the fp32 bound of a cancelling sum,
+64 2^-24 sqrt(L) || |q dq| + |k dk| ||: the kernels form the gate gradient as
+a reverse cumulative sum of q dq - k dk, whose terms cancel (exactly, for a
+scan's first token, where the gradient is zero), so its error scales with
+those terms rather than with the result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_token_recurrence_amd as g
+from gated_token_recurrence_amd import workloads as W
+
+from _helpers import inputs_f64, inputs_to_dev, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+IO_GRADS = ("dq", "dk", "dv", "dz")
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+def _run_case(oracle_mod, x, dtype, direction, chunk=0, bh=None, seed=0):
+    from oracle import backward as ob
+    shape_v = x["v"].shape
+    dy = W.cast_io(np.random.default_rng(seed).standard_normal(shape_v), dtype)
+    t = inputs_to_dev(x, dtype)
+    grads, n = g.gla_bwd(t["q"], t["k"], t["v"], t["log_g"], t["z"], t["rms_w"],
+                         to_dev(dy, dtype), direction, chunk=chunk)
+    torch.cuda.synchronize()
+    assert n == 9
+    f = inputs_f64(x, dtype)
+    ref = ob.bwd(f["q"], f["k"], f["v"], f["log_g"], f["z"], f["rms_w"],
+                 W.io_to_f64(dy, dtype), direction, bh=bh)
+    H = x["q"].shape[3]
+    L = x["q"].shape[1] * x["q"].shape[2]
+    gate_terms = np.abs(f["q"] * ref["dq"]) + np.abs(f["k"] * ref["dk"])
+    worst = {}
+    for name, got_t in grads.items():
+        got = to_f64(got_t)
+        r = ref[name]
+        terms = gate_terms
+        if bh is not None and name != "drms_w":
+            sel = [(s // H, s % H) for s in bh]
+            got = np.stack([got[b, :, :, h] for b, h in sel])
+            r = np.stack([r[b, :, :, h] for b, h in sel])
+            terms = np.stack([gate_terms[b, :, :, h] for b, h in sel])
+        if name == "drms_w" and bh is not None:
+            continue  # summed over the chosen sequences only
+        assert np.isfinite(got).all(), f"{name}: non-finite"
+        if dtype != "f32" and name in IO_GRADS:
+            r = oracle_mod.round_io(r, dtype)
+            tol = 1e-3
+        else:
+            tol = 1e-4
+        allow = 1e-10 * np.sqrt(r.size)
+        if name == "dlog_g":
+            allow += 64 * 2.0 ** -24 * np.sqrt(L) * np.linalg.norm(terms)
+        err = np.linalg.norm(got - r)
+        rel = err / (np.linalg.norm(r) + allow / tol)
+        worst[name] = rel
+        assert err <= tol * np.linalg.norm(r) + allow, (
+            f"{name}: error {err:.2e}, rel-L2 {err / max(np.linalg.norm(r), 1e-300):.2e} > {tol:.0e}")
+    _note("  " + " ".join(f"{k} {v:.1e}" for k, v in worst.items()))
+
+
+SHAPES = [
+    # B, gh, gw, H, dk, dv, dtype, chunk
+    (1, 7, 9, 2, 32, 32, "f32", 16),
+    (2, 5, 13, 3, 64, 64, "f32", 32),
+    (1, 9, 7, 2, 128, 64, "f32", 64),
+    (1, 6, 11, 1, 32, 128, "f32", 128),
+    (1, 17, 15, 2, 64, 64, "f16", 64),
+    (2, 12, 12, 2, 64, 128, "bf16", 64),
+    (1, 1, 1, 2, 64, 64, "f16", 64),
+    (1, 1, 70, 1, 64, 64, "bf16", 32),
+    (1, 70, 1, 1, 64, 64, "f16", 16),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_shapes(oracle_mod, shape):
+    B, gh, gw, H, dk, dv, dtype, chunk = shape
+    x = W.make_custom(B, gh, gw, H, dk, dv, dtype, seed=B * 100 + gh + dk)
+    _note(f"bwd {shape}")
+    _run_case(oracle_mod, x, dtype, direction=1, chunk=chunk, seed=3)
+
+
+@pytest.mark.parametrize("direction", [0, 1, 2, 3])
+def test_bwd_directions(oracle_mod, direction):
+    x = W.make_custom(1, 9, 11, 2, 64, 64, "f32", seed=40 + direction)
+    _note(f"bwd direction {direction}")
+    _run_case(oracle_mod, x, "f32", direction, chunk=16, seed=direction)
+
+
+@pytest.mark.parametrize("log_g", [0.0, -1e-4, -3.0])
+def test_bwd_extreme_gates(oracle_mod, log_g):
+    x = W.make_custom(1, 8, 12, 2, 64, 64, "f32", seed=7, log_g_const=log_g)
+    _note(f"bwd constant log_g {log_g}")
+    _run_case(oracle_mod, x, "f32", 2, chunk=32, seed=1)
+
+
+def test_bwd_mixer_640_sampled(oracle_mod):
+    """The 1.6K-token workload (H = 6, fp16), three sequences checked."""
+    w = W.WORKLOADS["mixer_640"]
+    x = W.make_inputs(w)
+    _note("bwd mixer_640")
+    _run_case(oracle_mod, x, w.dtype, 0, chunk=w.chunk, bh=[0, 3, 5], seed=11)
+
+
+def test_bwd_is_deterministic():
+    x = W.make_custom(1, 10, 10, 2, 64, 64, "bf16", seed=5)
+    t = inputs_to_dev(x, "bf16")
+    dy = to_dev(W.cast_io(np.random.default_rng(2).standard_normal(x["v"].shape), "bf16"), "bf16")
+    a, _ = g.gla_bwd(t["q"], t["k"], t["v"], t["log_g"], t["z"], t["rms_w"], dy, 3)
+    b, _ = g.gla_bwd(t["q"], t["k"], t["v"], t["log_g"], t["z"], t["rms_w"], dy, 3)
+    torch.cuda.synchronize()
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
