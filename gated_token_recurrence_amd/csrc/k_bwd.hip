@@ -38,7 +38,22 @@ template <int DK, int DV> struct BwdShape {
     static constexpr int TILE = (DK + DV > 128) ? 8 : 16;
     static constexpr int RG = CSTEP > JSTEP ? CSTEP : JSTEP;
     static constexpr int RW = DK > DV ? DK : DV;
+    // LDS order of the per-token channel and column vectors: the PER channels a
+    // map-A thread walks (c0 + CSTEP m) and the PER columns a map-B thread walks
+    // (j0 + JSTEP m) are contiguous, so each thread reads them as 16-byte pieces
+    __device__ static int pc(int c) { return (c % CSTEP) * PER + c / CSTEP; }
+    __device__ static int pj(int j) { return (j % JSTEP) * PER + j / JSTEP; }
 };
+
+// PER floats of an LDS row starting at a 16-byte aligned offset
+template <int PER>
+__device__ __forceinline__ void lds_vec(const float *src, float (&dst)[PER]) {
+#pragma unroll
+    for (int i = 0; i < PER / 4; ++i) {
+        const float4 x = reinterpret_cast<const float4 *>(src)[i];
+        dst[4 * i] = x.x; dst[4 * i + 1] = x.y; dst[4 * i + 2] = x.z; dst[4 * i + 3] = x.w;
+    }
+}
 
 struct BwdArgs {
     GlaArgs a;
@@ -77,11 +92,11 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
     using Sh = BwdShape<DK, DV>;
     constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, JSTEP = Sh::JSTEP, TILE = Sh::TILE;
     const GlaArgs &a = p.a;
-    __shared__ float sq[TILE][DK], sk[TILE][DK], sg[TILE][DK];
-    __shared__ float sv[TILE][DV], sz[TILE][DV], sdy[TILE][DV], so[TILE][DV], sdn[TILE][DV];
-    __shared__ float red[TILE][Sh::RG][Sh::RW];
-    __shared__ float swp[NT];
-    __shared__ float sinv[TILE], smdn[TILE];  // per token: RMSNorm factor, mean(dn n)
+    __shared__ __attribute__((aligned(16))) float sq[TILE][DK], sk[TILE][DK], sg[TILE][DK];
+    __shared__ __attribute__((aligned(16))) float sv[TILE][DV], sz[TILE][DV], sdy[TILE][DV], so[TILE][DV], sdn[TILE][DV];
+    __shared__ __attribute__((aligned(16))) float red[TILE][Sh::RG][Sh::RW];
+    __shared__ __attribute__((aligned(16))) float swp[NT];
+    __shared__ __attribute__((aligned(16))) float sinv[TILE], smdn[TILE];  // per token: RMSNorm factor, mean(dn n)
     __shared__ int64_t srow[TILE];
     const int tid = threadIdx.x;
     const ChunkPos cp(a, p.n_chunks);
@@ -108,9 +123,9 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
                     lg = a.log_g[r];
                     qq = ld<DT>(a.q, r);
                 }
-                sk[tt][c] = kk;
-                sg[tt][c] = expf(lg);
-                sq[tt][c] = qq;
+                sk[tt][Sh::pc(c)] = kk;
+                sg[tt][Sh::pc(c)] = expf(lg);
+                sq[tt][Sh::pc(c)] = qq;
             }
             for (int i = tid; i < TILE * DV; i += NT) {
                 const int tt = i / DV, jj = i % DV;
@@ -128,12 +143,15 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
             __syncthreads();
             for (int tt = 0; tt < nt; ++tt) {
                 const float vj = sv[tt][j];
+                float gg[PER], kk[PER], qq[PER];
+                lds_vec<PER>(&sg[tt][c0 * PER], gg);
+                lds_vec<PER>(&sk[tt][c0 * PER], kk);
+                lds_vec<PER>(&sq[tt][c0 * PER], qq);
                 float part = 0.f;
 #pragma unroll
                 for (int m = 0; m < PER; ++m) {
-                    const int c = c0 + CSTEP * m;
-                    s[m] = sg[tt][c] * s[m] + sk[tt][c] * vj;
-                    part += s[m] * sq[tt][c];
+                    s[m] = gg[m] * s[m] + kk[m] * vj;
+                    part += s[m] * qq[m];
                 }
                 red[tt][c0][j] = part;
             }
@@ -226,9 +244,9 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
                     lg = a.log_g[r];
                     qq = ld<DT>(a.q, r);
                 }
-                sk[tt][cc] = kk;
-                sg[tt][cc] = expf(lg);
-                sq[tt][cc] = qq;
+                sk[tt][Sh::pc(cc)] = kk;
+                sg[tt][Sh::pc(cc)] = expf(lg);
+                sq[tt][Sh::pc(cc)] = qq;
             }
             for (int i = tid; i < TILE * DV; i += NT) {
                 const int tt = i / DV, jj = i % DV;
@@ -238,18 +256,20 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
                     vv = ld<DT>(a.v, r);
                     dd = p.dO[r];
                 }
-                sv[tt][jj] = vv;
-                so[tt][jj] = dd;  // do_t
+                sv[tt][Sh::pj(jj)] = vv;
+                so[tt][Sh::pj(jj)] = dd;  // do_t
             }
             __syncthreads();
             for (int tt = 0; tt < nt; ++tt) {
-                const float g = sg[tt][c], kc = sk[tt][c];
+                const float g = sg[tt][Sh::pc(c)], kc = sk[tt][Sh::pc(c)];
+                float vv[PER], dd[PER];
+                lds_vec<PER>(&sv[tt][j0 * PER], vv);
+                lds_vec<PER>(&so[tt][j0 * PER], dd);
                 float part = 0.f;
 #pragma unroll
                 for (int m = 0; m < PER; ++m) {
-                    const int j = j0 + JSTEP * m;
-                    s[m] = g * s[m] + kc * sv[tt][j];
-                    part += s[m] * so[tt][j];
+                    s[m] = g * s[m] + kc * vv[m];
+                    part += s[m] * dd[m];
                 }
                 red[tt][j0][c] = part;
             }
@@ -261,7 +281,7 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
                 for (int r = 0; r < JSTEP; ++r) d += red[tt][r][cc];
                 const int64_t r = srow[tt] * DK + cc;
                 st<DT>(p.dq, r, d);
-                p.qdq[r] = sq[tt][cc] * d;
+                p.qdq[r] = sq[tt][Sh::pc(cc)] * d;
             }
         }
     }
@@ -275,8 +295,8 @@ __global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
     using Sh = BwdShape<DK, DV>;
     constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, TILE = Sh::TILE;
     const GlaArgs &a = p.a;
-    __shared__ float sq[TILE][DK], sg[TILE][DK], sdo[TILE][DV];
-    __shared__ float gpart[NT];
+    __shared__ __attribute__((aligned(16))) float sq[TILE][DK], sg[TILE][DK], sdo[TILE][DV];
+    __shared__ __attribute__((aligned(16))) float gpart[NT];
     __shared__ int64_t srow[TILE];
     const int tid = threadIdx.x;
     const ChunkPos cp(a, p.n_chunks);
@@ -301,8 +321,8 @@ __global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
                 lg = a.log_g[r];
                 qq = ld<DT>(a.q, r);
             }
-            sg[tt][c] = expf(lg);
-            sq[tt][c] = qq;
+            sg[tt][Sh::pc(c)] = expf(lg);
+            sq[tt][Sh::pc(c)] = qq;
             gacc += lg;
         }
         for (int i = tid; i < TILE * DV; i += NT) {
@@ -312,12 +332,11 @@ __global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
         __syncthreads();
         for (int tt = nt - 1; tt >= 0; --tt) {
             const float dj = sdo[tt][j];
+            float qq[PER];
+            lds_vec<PER>(&sq[tt][c0 * PER], qq);
 #pragma unroll
-            for (int m = 0; m < PER; ++m) {
-                const int c = c0 + CSTEP * m;
-                s[m] = gnext[m] * s[m] + sq[tt][c] * dj;
-                gnext[m] = sg[tt][c];
-            }
+            for (int m = 0; m < PER; ++m) s[m] = gnext[m] * s[m] + qq[m] * dj;
+            lds_vec<PER>(&sg[tt][c0 * PER], gnext);
         }
     }
     // E contribution: Diag(g of the chunk's first token) dS_first
@@ -343,10 +362,10 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
     using Sh = BwdShape<DK, DV>;
     constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, JSTEP = Sh::JSTEP, TILE = Sh::TILE;
     const GlaArgs &a = p.a;
-    __shared__ float sq[TILE][DK], sk[TILE][DK], sg[TILE][DK];
-    __shared__ float sv[TILE][DV], sdo[TILE][DV];
-    __shared__ float red[TILE][Sh::RG][Sh::RW];
-    __shared__ float sacc[DK];
+    __shared__ __attribute__((aligned(16))) float sq[TILE][DK], sk[TILE][DK], sg[TILE][DK];
+    __shared__ __attribute__((aligned(16))) float sv[TILE][DV], sdo[TILE][DV];
+    __shared__ __attribute__((aligned(16))) float red[TILE][Sh::RG][Sh::RW];
+    __shared__ __attribute__((aligned(16))) float sacc[DK];
     __shared__ int64_t srow[TILE];
     const int tid = threadIdx.x;
     const ChunkPos cp(a, p.n_chunks);
@@ -367,9 +386,9 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
                 lg = a.log_g[r];
                 qq = ld<DT>(a.q, r);
             }
-            sk[tt][c] = kk;
-            sg[tt][c] = expf(lg);
-            sq[tt][c] = qq;
+            sk[tt][Sh::pc(c)] = kk;
+            sg[tt][Sh::pc(c)] = expf(lg);
+            sq[tt][Sh::pc(c)] = qq;
         }
         for (int i = tid; i < TILE * DV; i += NT) {
             const int tt = i / DV, jj = i % DV;
@@ -379,8 +398,8 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
                 vv = ld<DT>(a.v, r);
                 dd = p.dO[r];
             }
-            sv[tt][jj] = vv;
-            sdo[tt][jj] = dd;
+            sv[tt][Sh::pj(jj)] = vv;
+            sdo[tt][Sh::pj(jj)] = dd;
         }
         __syncthreads();
     };
@@ -398,15 +417,17 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
             const int nt = static_cast<int>((cp.t1 - tb < TILE) ? cp.t1 - tb : TILE);
             load_tile(tb, nt);
             for (int tt = nt - 1; tt >= 0; --tt) {
-                const float qc = sq[tt][c];
+                const float qc = sq[tt][Sh::pc(c)];
+                float dd[PER], vv[PER];
+                lds_vec<PER>(&sdo[tt][j0 * PER], dd);
+                lds_vec<PER>(&sv[tt][j0 * PER], vv);
                 float part = 0.f;
 #pragma unroll
                 for (int m = 0; m < PER; ++m) {
-                    const int j = j0 + JSTEP * m;
-                    s[m] = gnext * s[m] + qc * sdo[tt][j];
-                    part += s[m] * sv[tt][j];
+                    s[m] = gnext * s[m] + qc * dd[m];
+                    part += s[m] * vv[m];
                 }
-                gnext = sg[tt][c];
+                gnext = sg[tt][Sh::pc(c)];
                 red[tt][j0][c] = part;
             }
             __syncthreads();
@@ -425,7 +446,7 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
                 float acc = sacc[tid];
                 for (int tt = nt - 1; tt >= 0; --tt) {
                     const int64_t r = srow[tt] * DK + tid;
-                    acc += p.qdq[r] - sk[tt][tid] * red[tt][0][tid];
+                    acc += p.qdq[r] - sk[tt][Sh::pc(tid)] * red[tt][0][tid];
                     p.dlog_g[r] = acc;
                 }
                 sacc[tid] = acc;
@@ -449,15 +470,17 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
             const int nt = static_cast<int>((cp.t1 - tb < TILE) ? cp.t1 - tb : TILE);
             load_tile(tb, nt);
             for (int tt = nt - 1; tt >= 0; --tt) {
-                const float dj = sdo[tt][j];
+                const float dj = sdo[tt][Sh::pj(j)];
+                float qq[PER], kk[PER];
+                lds_vec<PER>(&sq[tt][c0 * PER], qq);
+                lds_vec<PER>(&sk[tt][c0 * PER], kk);
                 float part = 0.f;
 #pragma unroll
                 for (int m = 0; m < PER; ++m) {
-                    const int c = c0 + CSTEP * m;
-                    s[m] = gnext[m] * s[m] + sq[tt][c] * dj;
-                    gnext[m] = sg[tt][c];
-                    part += s[m] * sk[tt][c];
+                    s[m] = gnext[m] * s[m] + qq[m] * dj;
+                    part += s[m] * kk[m];
                 }
+                lds_vec<PER>(&sg[tt][c0 * PER], gnext);
                 red[tt][c0][j] = part;
             }
             __syncthreads();
@@ -502,7 +525,7 @@ __global__ __launch_bounds__(NT) void k_bwd_gatescan(float *__restrict__ Tn, int
 template <int DK>
 __global__ __launch_bounds__(NT) void k_bwd_gateoff(BwdArgs p) {
     const GlaArgs &a = p.a;
-    __shared__ float soff[DK];
+    __shared__ __attribute__((aligned(16))) float soff[DK];
     const int tid = threadIdx.x;
     const ChunkPos cp(a, p.n_chunks);
     if (tid < DK) soff[tid] = p.Tn[cp.cid() * DK + tid];
@@ -522,7 +545,7 @@ __global__ __launch_bounds__(NT) void k_bwd_gateoff(BwdArgs p) {
 constexpr int WS_THREADS = 1024;
 template <int DV>
 __global__ __launch_bounds__(WS_THREADS) void k_bwd_wsum(BwdArgs p, int64_t n_parts) {
-    __shared__ float part[WS_THREADS];
+    __shared__ __attribute__((aligned(16))) float part[WS_THREADS];
     const int tid = threadIdx.x;
     const int j = tid % DV, g = tid / DV;
     constexpr int GS = WS_THREADS / DV;
