@@ -344,13 +344,13 @@ def time_backward(w, dev, hip, stream_ptr, steps, warmup):
     us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
     torch.cuda.synchronize(dev)
     hip.destroy(ev)
-    evs = hip.events(10)
+    evs = hip.events(16)
     nl = ctypes.c_int(0)
     per = []
     for i in range(5):
-        run(i, evs, 10, ctypes.byref(nl))
+        run(i, evs, 16, ctypes.byref(nl))
         torch.cuda.synchronize(dev)
-        per.append([hip.elapsed_ms(evs[j], evs[j + 1]) * 1e3 for j in range(nl.value)])
+        per.append([hip.elapsed_ms(evs[j], evs[j + 1]) * 1e3 for j in range(min(nl.value, 15))])
     hip.destroy(evs)
     del sets, grads
     torch.cuda.empty_cache()
@@ -675,9 +675,14 @@ def main():
             s_io = W.DTYPE_BYTES[w.dtype]
             bbytes = w.tokens * w.H * ((2 * w.dk + 3 * w.dv) * s_io + 4 * w.dk      # reads
                                        + (2 * w.dk + 2 * w.dv) * s_io + 4 * w.dk)   # writes
-            names_b = ("forward_chunk_summary", "forward_state_scan", "forward_walk_dq",
-                       "reverse_chunk_summary", "reverse_state_scan", "reverse_walk_dk_dv",
-                       "gate_total_scan", "gate_offsets", "rms_w_sum")
+            if w.dtype != "f32" and w.dk == 64 and w.dv == 64 and w.chunk <= 64:  # matrix-core gradients
+                names_b = ("forward_chunk_summary", "forward_state_scan", "forward_walk_do",
+                           "reverse_chunk_summary", "reverse_state_scan", "chunk_gradients_mfma",
+                           "fallback_dq", "fallback_dk_dv_dlog_g", "rms_w_sum")
+            else:
+                names_b = ("forward_chunk_summary", "forward_state_scan", "forward_walk_dq",
+                           "reverse_chunk_summary", "reverse_state_scan", "reverse_walk_dk_dv",
+                           "gate_total_scan", "gate_offsets", "rms_w_sum")
             backward = {"workload": f"{w.name}: backward of one call, fp32 arithmetic",
                         "us_per_call": round(bus, 3),
                         "tokens_per_s": round(w.tokens / (bus * 1e-6), 1),

@@ -191,6 +191,13 @@ struct BwdLaunchHooks {
     hipError_t after(hipStream_t st) const { return fn ? fn(ctx, st) : hipSuccess; }
 };
 size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks);
+// Matrix-core gradients of q, k, v per chunk (k_bgrad.hip): 16-bit I/O, dk = dv = 64,
+// chunk <= 64.  Chunks whose decay span is out of range are flagged (flags[chunk] = 1)
+// and left to the token-serial kernels.
+bool bgrad_supported(const GlaArgs &a);
+hipError_t bgrad_launch(const GlaArgs &a, const float *dO, const float *Sx, const float *Er,
+                        void *dq, void *dk, void *dv, float *dlog_g, int *flags, int n_chunks,
+                        hipStream_t s);
 hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
                       float *dlog_g, void *dz, float *drms_w, void *ws, int n_chunks,
                       hipStream_t st, const BwdLaunchHooks &hooks);

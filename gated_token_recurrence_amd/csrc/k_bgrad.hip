@@ -1,0 +1,499 @@
+// k_bgrad.hip -- matrix-core gradients of q, k and v for one chunk (backward pass,
+// 16-bit I/O, dk = dv = 64, chunk <= 64).
+//
+// GTR write-up ("端侧实时感知新标杆！通用线性骨干网络GTR开源"): Method §1 gives the
+// recurrence S_t = Diag(g_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t; Method §4 its
+// chunkwise evaluation.  Differentiating the chunkwise form of a chunk with
+// incoming state S (from the earlier chunks), incoming gradient state E (from the
+// later chunks, already carrying the next chunk's first gate), a the in-chunk
+// inclusive cumulative log2-gate and G = a at the chunk's last token:
+//   Q~ = q 2^a,  K^ = k 2^-a,  K~ = k 2^(G - a),  M = [j <= i]
+//   D = (dO V^T) . M            (gradient of the scores, no gate on the v . do sum)
+//   P = (Q~ K^^T) . M           (the forward scores)
+//   dQ = 2^a . (dO S^T + D K^)
+//   dK = 2^-a . (D^T Q~) + 2^(G - a) . (V E^T)
+//   dV = P^T dO + K~ E
+// The gate gradient's per-token term q . dq - k . dk is summed in reverse over
+// the chunk and offset by the sum over all later tokens of the sequence, which
+// equals sum_d E[c][d] S_out[c][d] (the gate gradient at the next chunk's first
+// token, g S_prev . dS there: E carries that token's gate, S_out = 2^G . (S + K^^T V)
+// is the state after this chunk's last token), so dlog_g is complete here.
+// 2^-a grows with the chunk's decay span: a chunk whose span exceeds kSpanMax
+// (log2 units) in any channel is only flagged here, and the fp32 token-serial
+// kernels produce its gradients.
+//
+// Persistent workgroups of four waves, one chunk at a time; the next chunk's
+// inputs are requested while the current chunk is computed.  Every product is a
+// 64 x 64 x 64 product on v_mfma_f32_16x16x32_bf16 with each operand split into
+// bf16 hi + lo (three products per pair), wave w computing output rows
+// [16 w, 16 w + 16).  Operands are split once, when written to LDS, into hi and
+// lo planes of 64 x 64 16-bit elements (rows XOR-swizzled by 16-byte piece); a
+// product reads rows of a plane (16- or 8-byte pieces) or columns of it (the
+// transposing ds_read_b64_tr_b16).  D and P are stored transposed, so that a
+// lane's four results per tile are one 8-byte piece.  E enters pre-scaled by
+// 2^G (E' = 2^G . E), which merges dK's two terms under one factor 2^-a and
+// makes dV = P^T dO + K^ E'.  dq, dk and dv pass through an fp32 staging
+// matrix on their way out (16-byte global stores), where the gate gradient's
+// per-token term q dq - k dk is formed from the exact q and k.
+#include "mfma_common.hpp"
+
+namespace gtr {
+namespace {
+
+using namespace mf;
+
+constexpr int BC = 64;         // chunk tokens (rows of every matrix) and channels
+constexpr int LS = BC + 4;     // fp32 LDS row stride
+constexpr int MAT = BC * BC;   // elements of one 16-bit plane
+constexpr int64_t kPersistent = 256;  // workgroups: one per CU (LDS allows no second)
+
+struct BgArgs {
+    GlaArgs a;
+    const float *dO;    // [rows][64]
+    const float *Sx;    // forward incoming state per chunk [bh N + n][64][64]
+    const float *Er;    // reverse incoming gradient state per chunk, reversed chunk order
+    void *dq, *dk, *dv;
+    float *dlog_g;      // complete gate gradient
+    int *flags;         // per chunk: 1 = left to the token-serial kernels
+    int n_chunks;
+};
+
+__device__ __forceinline__ void st4(float *dst, float4 x) { *reinterpret_cast<float4 *>(dst) = x; }
+__device__ __forceinline__ float4 ld4(const float *src) { return *reinterpret_cast<const float4 *>(src); }
+
+// hi and lo planes (X, X + MAT) of N consecutive elements of row `row` from `col`
+template <int N>
+__device__ __forceinline__ void put(uint16_t *X, int row, int col, const float (&x)[N]) {
+    uint32_t h[N / 2], l[N / 2];
+    split_pk<false>(x, h, l);
+    const int off = swn(row, col);
+    if constexpr (N == 8) {
+        *reinterpret_cast<uint4 *>(X + off) = u4(h);
+        *reinterpret_cast<uint4 *>(X + MAT + off) = u4(l);
+    } else {
+        static_assert(N == 4, "4 or 8 elements");
+        *reinterpret_cast<uint2 *>(X + off) = make_uint2(h[0], h[1]);
+        *reinterpret_cast<uint2 *>(X + MAT + off) = make_uint2(l[0], l[1]);
+    }
+}
+
+// Operand fetch of lane (lr, g), k block kap.  NAT: row m, k slots
+// 32 kap + 8 g + s.  PERM: row m, k slots 32 kap + 16 (s / 4) + 4 g + s % 4.
+// TRN: column m (= a multiple of 16 + lr), the same k slots as PERM, which are
+// what the transposing read delivers (lane lr's slot j of one read comes from
+// the 8-byte piece of lane 4 j + lr / 4).  Both operands of a product use NAT,
+// or both use PERM / TRN.
+enum { NAT = 0, PERM = 1, TRN = 2 };
+template <int MODE>
+__device__ __forceinline__ void fetch(const uint16_t *X, int m, int lr, int g, int kap, s16x8 &hi,
+                                      s16x8 &lo) {
+    if constexpr (MODE == NAT) {
+        const int off = swn(m, 32 * kap + 8 * g);
+        hi = *reinterpret_cast<const s16x8 *>(X + off);
+        lo = *reinterpret_cast<const s16x8 *>(X + MAT + off);
+    } else if constexpr (MODE == PERM) {
+        const int o0 = swn(m, 32 * kap + 4 * g), o1 = swn(m, 32 * kap + 16 + 4 * g);
+        const s16x4 h0 = *reinterpret_cast<const s16x4 *>(X + o0);
+        const s16x4 h1 = *reinterpret_cast<const s16x4 *>(X + o1);
+        const s16x4 l0 = *reinterpret_cast<const s16x4 *>(X + MAT + o0);
+        const s16x4 l1 = *reinterpret_cast<const s16x4 *>(X + MAT + o1);
+        hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+        lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        const int r = 32 * kap + 4 * g + (lr >> 2), c = (m & ~15) + 4 * (lr & 3);
+        const int o0 = swn(r, c), o1 = swn(r + 16, c);
+        const s16x4 h0 = ld_tr(X + o0), h1 = ld_tr(X + o1);
+        const s16x4 l0 = ld_tr(X + MAT + o0), l1 = ld_tr(X + MAT + o1);
+        hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+        lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+// acc[t] += A[16 w + .., :] B[:, 16 t + ..], t = 0..3.  Row modes: A stored
+// [m][k], B stored [n][k]; TRN: A stored [k][m], B stored [k][n].  Lane l:
+// output rows 16 w + 4 (l / 16) + r, column 16 t + l % 16 (acc[t][r]).
+template <int MA, int MB>
+__device__ __forceinline__ void gemm(f32x4 (&acc)[4], const uint16_t *A, const uint16_t *B, int w,
+                                     int lr, int g) {
+    static_assert((MA == NAT) == (MB == NAT), "both operands must use one k slot order");
+#pragma unroll
+    for (int kap = 0; kap < 2; ++kap) {
+        s16x8 ah, al;
+        fetch<MA>(A, 16 * w + lr, lr, g, kap, ah, al);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            s16x8 bh, bl;
+            fetch<MB>(B, 16 * t + lr, lr, g, kap, bh, bl);
+            acc[t] = mma<false>(ah, bh, acc[t]);
+            acc[t] = mma<false>(ah, bl, acc[t]);
+            acc[t] = mma<false>(al, bh, acc[t]);
+        }
+    }
+}
+
+__device__ __forceinline__ void zero4(f32x4 (&acc)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Position of chunk c (of B H N, sequence-major) and its token count
+struct ChunkAt {
+    int n, bh, b, h, nt;
+    int64_t t0;
+    size_t cidx, ridx;
+    __device__ ChunkAt(const BgArgs &p, int64_t c) {
+        const GlaArgs &a = p.a;
+        n = static_cast<int>(c % p.n_chunks);
+        bh = static_cast<int>(c / p.n_chunks);
+        b = bh / a.H;
+        h = bh % a.H;
+        t0 = static_cast<int64_t>(n) * a.chunk;
+        nt = static_cast<int>((t0 + a.chunk < a.L) ? a.chunk : a.L - t0);
+        cidx = static_cast<size_t>(c);
+        ridx = static_cast<size_t>(bh) * p.n_chunks + (p.n_chunks - 1 - n);
+    }
+    // global row of token t; rows past the chunk's end repeat its last row
+    __device__ int64_t row(const GlaArgs &a, int t) const {
+        return scan_row(a, b, h, t0 + (t < nt ? t : nt - 1));
+    }
+};
+
+// Global inputs of one chunk, held in registers from their request until they
+// are used.  Thread tid takes 16-byte pieces i = tid + 256 u: fp32 rows
+// t = i / 16, columns 4 (i % 16); 16-bit rows t = i / 8, columns 8 (i % 8).
+struct TokIn {   // per-token inputs, requested first
+    float4 g[4], dO[4];
+    uint4 q[2], k[2], v[2];
+};
+struct StateIn {  // the chunk's two boundary states, requested once the last are used
+    float4 S[4], E[4];
+};
+
+__device__ __forceinline__ void request_tok(TokIn &in, const BgArgs &p, const int64_t *rows, int tid) {
+    const GlaArgs &a = p.a;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+        in.g[u] = ld4(a.log_g + rows[t] * DK + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
+        in.q[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + rows[t] * DK + c);
+        in.k[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + rows[t] * DK + c);
+        in.v[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + rows[t] * BC + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+        in.dO[u] = ld4(p.dO + rows[t] * BC + c);
+    }
+}
+
+__device__ __forceinline__ void request_state(StateIn &in, const BgArgs &p, const ChunkAt &at, int tid) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+        in.S[u] = ld4(p.Sx + at.cidx * MAT + t * BC + c);  // S[c'][d]: row c' = t, column d = c
+        in.E[u] = ld4(p.Er + at.ridx * MAT + t * BC + c);  // E[c'][d]
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 pack8(const float *x) {
+    uint32_t u[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = f2h<DT>(x[2 * e]) | (f2h<DT>(x[2 * e + 1]) << 16);
+    return u4(u);
+}
+
+template <int DT>
+__global__ __launch_bounds__(NT, 1) void k_bgrad(BgArgs p) {
+    const GlaArgs &a = p.a;
+    // hi + lo planes; SE holds S, then E'
+    __shared__ __attribute__((aligned(16))) uint16_t sDO[2 * MAT], sQT[2 * MAT], sKH[2 * MAT], sV[2 * MAT];
+    __shared__ __attribute__((aligned(16))) uint16_t sSE[2 * MAT], sDT[2 * MAT], sPT[2 * MAT];
+    __shared__ __attribute__((aligned(16))) float sA2[BC][LS];  // 2^a, later q dq - k dk
+    __shared__ __attribute__((aligned(16))) float sX[BC][LS];   // fp32 staging: T, dq, dk, dv
+    __shared__ float sG[BC], sOff[BC], sTot[4][BC];
+    __shared__ int64_t srow[2][BC];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
+    const int64_t total = static_cast<int64_t>(a.B) * a.H * p.n_chunks;
+
+    int64_t ch = blockIdx.x;
+    int buf = 0;
+    if (tid < BC) srow[0][tid] = ChunkAt(p, ch).row(a, tid);
+    __syncthreads();
+    TokIn in;
+    StateIn st_in;
+    request_tok(in, p, srow[0], tid);
+    request_state(st_in, p, ChunkAt(p, ch), tid);
+
+    for (; ch < total; ch += gridDim.x, buf ^= 1) {
+        const ChunkAt at(p, ch);
+        const int64_t *rows = srow[buf];
+        const int nt = at.nt;
+        const int64_t cn = ch + gridDim.x;  // next chunk of this workgroup
+
+        // ---- cumulative gates (log2 units): raw values, then a 4-segment scan per channel
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+            const bool ok = t < nt;
+            const float4 x = in.g[u];
+            st4(&sA2[t][c], make_float4(ok ? x.x * kLog2e : 0.f, ok ? x.y * kLog2e : 0.f,
+                                        ok ? x.z * kLog2e : 0.f, ok ? x.w * kLog2e : 0.f));
+        }
+        __syncthreads();
+        float cum[16];
+        {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                acc += sA2[16 * w + s][l];
+                cum[s] = acc;
+            }
+            sTot[w][l] = acc;
+        }
+        __syncthreads();
+        float off = 0.f, tot = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float x = sTot[u][l];
+            off += (u < w) ? x : 0.f;
+            tot += x;
+        }
+#pragma unroll
+        for (int s = 0; s < 16; ++s) sA2[16 * w + s][l] = fexp2(cum[s] + off);
+        if (w == 0) sG[l] = fexp2(tot);
+        const bool slow = __syncthreads_or(-tot > kSpanMax);  // uniform over the workgroup
+        if (tid == 0) p.flags[at.cidx] = slow ? 1 : 0;
+
+        // ---- operands (rows past the chunk's end are zero); exact q and k kept
+        uint4 qk[2][2];
+        if (!slow) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
+                const bool ok = t < nt;
+                float q8[8], k8[8], v8[8];
+                unpack8<DT>(in.q[u], q8);
+                unpack8<DT>(in.k[u], k8);
+                unpack8<DT>(in.v[u], v8);
+                qk[u][0] = in.q[u];
+                qk[u][1] = in.k[u];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float e = sA2[t][c + s];
+                    q8[s] = ok ? q8[s] * e : 0.f;
+                    k8[s] = ok ? k8[s] * frcp(e) : 0.f;
+                    v8[s] = ok ? v8[s] : 0.f;
+                }
+                put<8>(sQT, t, c, q8);
+                put<8>(sKH, t, c, k8);
+                put<8>(sV, t, c, v8);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+                const float4 d = in.dO[u], sv = st_in.S[u];
+                const bool ok = t < nt;
+                const float dd[4] = {ok ? d.x : 0.f, ok ? d.y : 0.f, ok ? d.z : 0.f, ok ? d.w : 0.f};
+                const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
+                put<4>(sDO, t, c, dd);
+                put<4>(sSE, t, c, ss);
+            }
+        }
+        // ---- the next chunk's rows, then its per-token inputs (those registers are free)
+        if (cn < total && tid < BC) srow[buf ^ 1][tid] = ChunkAt(p, cn).row(a, tid);
+        __syncthreads();
+        if (cn < total) request_tok(in, p, srow[buf ^ 1], tid);
+        if (slow) {  // the whole workgroup; its gradients come from the token-serial kernels
+            if (cn < total) request_state(st_in, p, ChunkAt(p, cn), tid);
+            continue;
+        }
+
+        f32x4 acc[4];
+        // ---- D = (dO V^T) . M and P = (Q~ K^^T) . M, rows i of wave w, stored transposed
+        zero4(acc);
+        gemm<NAT, NAT>(acc, sDO, sV, w, lr, g);      // B(k=d, n=j) = V[j][d]
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * w + 4 * g + r) ? acc[t][r] : 0.f;
+            put<4>(sDT, 16 * t + lr, 16 * w + 4 * g, x);
+        }
+        zero4(acc);
+        gemm<NAT, NAT>(acc, sQT, sKH, w, lr, g);     // B(k=c, n=j) = K^[j][c]
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * w + 4 * g + r) ? acc[t][r] : 0.f;
+            put<4>(sPT, 16 * t + lr, 16 * w + 4 * g, x);
+        }
+        // ---- T = K^^T V (rows c of wave w), staged
+        zero4(acc);
+        gemm<TRN, TRN>(acc, sKH, sV, w, lr, g);      // A(m=c, k=j) = K^[j][c], B(k=j, n=d) = V[j][d]
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[16 * w + 4 * g + r][16 * t + lr] = acc[t][r];
+        __syncthreads();
+
+        // ---- offset of the gate gradient: sum_d E[c][d] S_out[c][d] with
+        // S_out = 2^G . (S + T); the 16 lanes of a channel row reduce together
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+            const float4 sv = st_in.S[u], ev = st_in.E[u], tv = ld4(&sX[t][c]);
+            float x = ev.x * (sv.x + tv.x) + ev.y * (sv.y + tv.y) + ev.z * (sv.z + tv.z) +
+                      ev.w * (sv.w + tv.w);
+            x += __shfl_xor(x, 1);
+            x += __shfl_xor(x, 2);
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+            if ((tid & 15) == 0) sOff[t] = sG[t] * x;
+        }
+
+        // ---- dQ = 2^a . (dO S^T + D K^), rows i of wave w
+        zero4(acc);
+        gemm<NAT, NAT>(acc, sDO, sSE, w, lr, g);     // B(k=d, n=c) = S[c][d]
+        gemm<TRN, TRN>(acc, sDT, sKH, w, lr, g);     // A(m=i, k=j) = D[i][j], B(k=j, n=c) = K^[j][c]
+        __syncthreads();  // S and T are read
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * g + r, c = 16 * t + lr;
+                sX[i][c] = sA2[i][c] * acc[t][r];
+            }
+        // E' = 2^G . E (rows c scaled), then the next chunk's states
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+            const float4 ev = st_in.E[u];
+            const float gt = sG[t];
+            const float ee[4] = {gt * ev.x, gt * ev.y, gt * ev.z, gt * ev.w};
+            put<4>(sSE, t, c, ee);
+        }
+        if (cn < total) request_state(st_in, p, ChunkAt(p, cn), tid);
+        __syncthreads();
+        // dq out; q . dq of this thread's pieces
+        float qdq[2][8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
+            float x[8], q8[8];
+            const float4 x0 = ld4(&sX[t][c]), x1 = ld4(&sX[t][c + 4]);
+            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+            unpack8<DT>(qk[u][0], q8);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) qdq[u][s] = q8[s] * x[s];
+            if (t < nt)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dq) + rows[t] * DK + c) = pack8<DT>(x);
+        }
+
+        // ---- dK = 2^-a . (D^T Q~ + V E'^T), rows j of wave w
+        zero4(acc);
+        gemm<PERM, TRN>(acc, sDT, sQT, w, lr, g);    // A(m=j, k=i) = D[i][j], B(k=i, n=c) = Q~[i][c]
+        gemm<NAT, NAT>(acc, sV, sSE, w, lr, g);      // B(k=d, n=c) = E'[c][d]
+        __syncthreads();  // dq is read
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * w + 4 * g + r, c = 16 * t + lr;
+                sX[j][c] = acc[t][r] * frcp(sA2[j][c]);
+            }
+        __syncthreads();
+        // dk out; the gate gradient's terms q dq - k dk replace 2^a
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
+            float x[8], k8[8], y[8];
+            const float4 x0 = ld4(&sX[t][c]), x1 = ld4(&sX[t][c + 4]);
+            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+            unpack8<DT>(qk[u][1], k8);
+            const bool ok = t < nt;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) y[s] = ok ? qdq[u][s] - k8[s] * x[s] : 0.f;
+            st4(&sA2[t][c], make_float4(y[0], y[1], y[2], y[3]));
+            st4(&sA2[t][c + 4], make_float4(y[4], y[5], y[6], y[7]));
+            if (ok)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dk) + rows[t] * DK + c) = pack8<DT>(x);
+        }
+
+        // ---- dV = P^T dO + K^ E', rows j of wave w
+        zero4(acc);
+        gemm<PERM, TRN>(acc, sPT, sDO, w, lr, g);    // A(m=j, k=i) = P[i][j], B(k=i, n=d) = dO[i][d]
+        gemm<PERM, TRN>(acc, sKH, sSE, w, lr, g);    // A(m=j, k=c) = K^[j][c], B(k=c, n=d) = E'[c][d]
+        __syncthreads();  // dk and the gate terms are through LDS
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[16 * w + 4 * g + r][16 * t + lr] = acc[t][r];
+        // dlog_g, part 1: wave w takes tokens [16 w, 16 w + 16) of channel l
+        float x16[16];
+        {
+            float s = 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                x16[u] = sA2[16 * w + u][l];
+                s += x16[u];
+            }
+            sTot[w][l] = s;
+        }
+        __syncthreads();
+        // dv out
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
+            float x[8];
+            const float4 x0 = ld4(&sX[t][c]), x1 = ld4(&sX[t][c + 4]);
+            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+            if (t < nt)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dv) + rows[t] * BC + c) = pack8<DT>(x);
+        }
+        // dlog_g, part 2: reverse cumulative sum from the offset and the later segments
+        float s = sOff[l];
+#pragma unroll
+        for (int u = 3; u > 0; --u) s += (u > w) ? sTot[u][l] : 0.f;
+#pragma unroll
+        for (int u = 15; u >= 0; --u) {
+            const int t = 16 * w + u;
+            s += x16[u];
+            if (t < nt) p.dlog_g[rows[t] * DK + l] = s;
+        }
+        __syncthreads();  // LDS is rewritten by the next chunk
+    }
+}
+
+}  // namespace
+
+bool bgrad_supported(const GlaArgs &a) {
+    auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
+    return (a.dtype == DT_F16 || a.dtype == DT_BF16) && a.dk == 64 && a.dv == 64 && a.chunk <= 64 &&
+           !a.resid && al16(a.q) && al16(a.k) && al16(a.v) && al16(a.log_g);
+}
+
+hipError_t bgrad_launch(const GlaArgs &a, const float *dO, const float *Sx, const float *Er,
+                        void *dq, void *dk, void *dv, float *dlog_g, int *flags, int n_chunks,
+                        hipStream_t s) {
+    const BgArgs p{a, dO, Sx, Er, dq, dk, dv, dlog_g, flags, n_chunks};
+    const int64_t total = static_cast<int64_t>(a.B) * a.H * n_chunks;
+    const dim3 grid(static_cast<unsigned>(total < kPersistent ? total : kPersistent));
+    if (a.dtype == DT_F16)
+        hipLaunchKernelGGL((k_bgrad<DT_F16>), grid, dim3(NT), 0, s, p);
+    else if (a.dtype == DT_BF16)
+        hipLaunchKernelGGL((k_bgrad<DT_BF16>), grid, dim3(NT), 0, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace gtr

@@ -67,6 +67,7 @@ struct BwdArgs {
     float *dWp;          // [bh N + n][DV] drms_w partials
     void *dq, *dk, *dv, *dz;
     float *dlog_g, *drms_w;
+    const int *flags;    // chunks left to the token-serial gradients (matrix-core path)
     int n_chunks;
 };
 
@@ -87,7 +88,8 @@ struct ChunkPos {
 
 // ---- B1: forward walk.  Pass 1 (map A): o_t, epilogue backward -> do_t (global),
 // dz_t, drms_w partials.  Pass 2 (map B): dq_t = S_t do_t, q dq (fp32, global).
-template <int DT, int DK, int DV>
+// MODE 0: both passes; 1: pass 1 only; 2: pass 2 only, for the flagged chunks.
+template <int DT, int DK, int DV, int MODE>
 __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
     using Sh = BwdShape<DK, DV>;
     constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, JSTEP = Sh::JSTEP, TILE = Sh::TILE;
@@ -101,9 +103,10 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
     const int tid = threadIdx.x;
     const ChunkPos cp(a, p.n_chunks);
     const size_t soff = cp.cid() * DK * DV;
+    if (MODE == 2 && p.flags[cp.cid()] == 0) return;  // the whole workgroup
 
     // ---- pass 1, map A
-    {
+    if constexpr (MODE != 2) {
         const int j = tid % DV, c0 = tid / DV;
         float s[PER];
 #pragma unroll
@@ -222,6 +225,7 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
             p.dWp[cp.cid() * DV + tid] = w;
         }
     }
+    if constexpr (MODE == 1) return;
     __syncthreads();  // this workgroup's do_t writes are visible to its own reads below
 
     // ---- pass 2, map B: dq_t = S_t do_t
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
 // dk_t = dS_t v_t, then q dq - k dk, its reverse cumulative sum inside the chunk
 // (written as dlog_g, completed by B4) and the chunk total.  Pass B (map A):
 // dv_t = dS_t^T k_t.
-template <int DT, int DK, int DV>
+template <int DT, int DK, int DV, bool FLAGGED>
 __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
     using Sh = BwdShape<DK, DV>;
     constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, JSTEP = Sh::JSTEP, TILE = Sh::TILE;
@@ -369,6 +373,7 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
     __shared__ int64_t srow[TILE];
     const int tid = threadIdx.x;
     const ChunkPos cp(a, p.n_chunks);
+    if (FLAGGED && p.flags[cp.cid()] == 0) return;  // the whole workgroup
     const size_t eoff = (static_cast<size_t>(cp.bh) * p.n_chunks + (p.n_chunks - 1 - cp.n)) * DK * DV;
     const int64_t len = cp.t1 - cp.t0;
     const int64_t ntiles = (len + TILE - 1) / TILE;
@@ -411,7 +416,20 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
 #pragma unroll
         for (int m = 0; m < PER; ++m) s[m] = p.Er[eoff + static_cast<size_t>(c) * DV + j0 + JSTEP * m];
         float gnext = 1.f;  // E already carries the next chunk's first gate
-        if (tid < DK) sacc[tid] = 0.f;
+        if (tid < DK) {
+            // complete dlog_g for a flagged chunk (the matrix-core path has no offset
+            // pass): the sum over the later tokens of the sequence is the gate
+            // gradient at the next chunk's first token, sum_d E[c][d] S_out[c][d],
+            // with S_out the next chunk's incoming state (none after the last chunk)
+            float o = 0.f;
+            if (FLAGGED && cp.n + 1 < p.n_chunks) {
+                const float *sn = p.Sx + (cp.cid() + 1) * DK * DV + static_cast<size_t>(tid) * DV;
+                const float *en = p.Er + eoff + static_cast<size_t>(tid) * DV;
+#pragma unroll 16
+                for (int d = 0; d < DV; ++d) o += en[d] * sn[d];
+            }
+            sacc[tid] = o;
+        }
         for (int64_t ti = ntiles - 1; ti >= 0; --ti) {
             const int64_t tb = cp.t0 + ti * TILE;
             const int nt = static_cast<int>((cp.t1 - tb < TILE) ? cp.t1 - tb : TILE);
@@ -567,15 +585,22 @@ __global__ __launch_bounds__(WS_THREADS) void k_bwd_wsum(BwdArgs p, int64_t n_pa
 }
 
 template <int DT, int DK, int DV>
-hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hooks) {
+hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hooks, int *flags) {
     const int64_t ncb = static_cast<int64_t>(p.a.B) * p.a.H * p.n_chunks;
     const dim3 grid(static_cast<unsigned>(ncb));
     auto done = [&]() {
         const hipError_t e = hipGetLastError();
         return e != hipSuccess ? e : hooks.after(st);
     };
+    // matrix-core gradients where the shape allows (16-bit I/O, dk = dv = 64)
+    auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
+    const bool mfma = DT != DT_F32 && DK == 64 && DV == 64 && bgrad_supported(p.a) && al16(p.dq) &&
+                      al16(p.dk) && al16(p.dv);
     hipError_t e;
-    hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV>), grid, dim3(NT), 0, st, p);
+    if (mfma)
+        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 1>), grid, dim3(NT), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 0>), grid, dim3(NT), 0, st, p);
     if ((e = done()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_bwd_revsum<DT, DK, DV>), grid, dim3(NT), 0, st, p);
     if ((e = done()) != hipSuccess) return e;
@@ -583,22 +608,34 @@ hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hoo
     if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
     BwdArgs q = p;
     q.Er = p.Ur;  // scanned in place
-    hipLaunchKernelGGL((k_bwd_revwalk<DT, DK, DV>), grid, dim3(NT), 0, st, q);
+    q.flags = flags;
+    if (mfma) {
+        e = bgrad_launch(p.a, p.dO, p.Sx, q.Er, p.dq, p.dk, p.dv, p.dlog_g, flags, p.n_chunks, st);
+        if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+        // chunks out of the matrix path's exponent range: token-serial gradients
+        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 2>), grid, dim3(NT), 0, st, q);
+        if ((e = done()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_bwd_revwalk<DT, DK, DV, true>), grid, dim3(NT), 0, st, q);
+    } else {
+        hipLaunchKernelGGL((k_bwd_revwalk<DT, DK, DV, false>), grid, dim3(NT), 0, st, q);
+    }
     if ((e = done()) != hipSuccess) return e;
-    const int64_t nsc = static_cast<int64_t>(p.a.B) * p.a.H * DK;
-    hipLaunchKernelGGL(k_bwd_gatescan, dim3(static_cast<unsigned>((nsc + NT - 1) / NT)), dim3(NT), 0,
-                       st, p.Tn, static_cast<int>(p.a.B * p.a.H), p.n_chunks, DK);
-    if ((e = done()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_gateoff<DK>), grid, dim3(NT), 0, st, q);
-    if ((e = done()) != hipSuccess) return e;
+    if (!mfma) {  // the matrix-core path writes complete gate gradients
+        const int64_t nsc = static_cast<int64_t>(p.a.B) * p.a.H * DK;
+        hipLaunchKernelGGL(k_bwd_gatescan, dim3(static_cast<unsigned>((nsc + NT - 1) / NT)), dim3(NT),
+                           0, st, p.Tn, static_cast<int>(p.a.B * p.a.H), p.n_chunks, DK);
+        if ((e = done()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_bwd_gateoff<DK>), grid, dim3(NT), 0, st, q);
+        if ((e = done()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((k_bwd_wsum<DV>), dim3(1), dim3(WS_THREADS), 0, st, q, ncb);
     return done();
 }
 
 template <int DT>
-hipError_t run_dt(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hooks) {
+hipError_t run_dt(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hooks, int *flags) {
 #define GTR_BWD_CASE(DK_, DV_) \
-    if (p.a.dk == DK_ && p.a.dv == DV_) return run_shape<DT, DK_, DV_>(p, st, hooks);
+    if (p.a.dk == DK_ && p.a.dv == DV_) return run_shape<DT, DK_, DV_>(p, st, hooks, flags);
     GTR_BWD_CASE(32, 32) GTR_BWD_CASE(32, 64) GTR_BWD_CASE(32, 128)
     GTR_BWD_CASE(64, 32) GTR_BWD_CASE(64, 64) GTR_BWD_CASE(64, 128)
     GTR_BWD_CASE(128, 32) GTR_BWD_CASE(128, 64) GTR_BWD_CASE(128, 128)
@@ -613,7 +650,8 @@ size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks) {
     const size_t rows = static_cast<size_t>(a.B) * a.L * a.H;
     return 4 * (2 * ncb * (static_cast<size_t>(a.dk) * a.dv + a.dk)  // forward and reverse states
                 + rows * (a.dv + a.dk)                                // do, q dq
-                + ncb * (a.dk + a.dv));                               // chunk totals, drms_w parts
+                + ncb * (a.dk + a.dv)                                 // chunk totals, drms_w parts
+                + ncb);                                               // chunk flags
 }
 
 hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
@@ -626,16 +664,18 @@ hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void
     float *Uf = f, *Gf = Uf + ncb * dd, *Ur = Gf + ncb * a.dk, *Gr = Ur + ncb * dd;
     float *dO = Gr + ncb * a.dk, *qdq = dO + rows * a.dv, *Tn = qdq + rows * a.dk;
     float *dWp = Tn + ncb * a.dk;
+    int *flags = reinterpret_cast<int *>(dWp + ncb * a.dv);
     // forward incoming states: the forward path's chunk summaries and scan
     hipError_t e = serial_summary(a, Uf, Gf, n_chunks, st);
     if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
     e = state_scan(Uf, Gf, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st);
     if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
-    BwdArgs p{a, dy, Uf, nullptr, dO, qdq, Ur, Gr, Tn, dWp, dq, dk, dv, dz, dlog_g, drms_w, n_chunks};
+    BwdArgs p{a, dy, Uf, nullptr, dO, qdq, Ur, Gr, Tn, dWp, dq, dk, dv, dz, dlog_g, drms_w,
+              nullptr, n_chunks};
     switch (a.dtype) {
-    case DT_F32: return run_dt<DT_F32>(p, st, hooks);
-    case DT_F16: return run_dt<DT_F16>(p, st, hooks);
-    case DT_BF16: return run_dt<DT_BF16>(p, st, hooks);
+    case DT_F32: return run_dt<DT_F32>(p, st, hooks, flags);
+    case DT_F16: return run_dt<DT_F16>(p, st, hooks, flags);
+    case DT_BF16: return run_dt<DT_BF16>(p, st, hooks, flags);
     default: return hipErrorInvalidValue;
     }
 }

@@ -36,7 +36,10 @@ def _run_case(oracle_mod, x, dtype, direction, chunk=0, bh=None, seed=0):
     grads, n = g.gla_bwd(t["q"], t["k"], t["v"], t["log_g"], t["z"], t["rms_w"],
                          to_dev(dy, dtype), direction, chunk=chunk)
     torch.cuda.synchronize()
-    assert n == 9
+    # 9 launches on either path: the matrix-core gradients (16-bit I/O, dk = dv = 64,
+    # chunk <= 64) with their token-serial fallback for flagged chunks replace the
+    # reverse walk and the two gate-offset passes
+    assert n == 9, n
     f = inputs_f64(x, dtype)
     ref = ob.bwd(f["q"], f["k"], f["v"], f["log_g"], f["z"], f["rms_w"],
                  W.io_to_f64(dy, dtype), direction, bh=bh)
@@ -106,6 +109,27 @@ def test_bwd_extreme_gates(oracle_mod, log_g):
     x = W.make_custom(1, 8, 12, 2, 64, 64, "f32", seed=7, log_g_const=log_g)
     _note(f"bwd constant log_g {log_g}")
     _run_case(oracle_mod, x, "f32", 2, chunk=32, seed=1)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("log_g", [0.0, -1e-4, -0.5, -3.0])
+def test_bwd_matrix_path_gates(oracle_mod, dtype, log_g):
+    """16-bit I/O on the matrix-core gradients; -3.0 per token spans far more than
+    64 log2 units per chunk, so every chunk falls back to the token-serial kernels."""
+    x = W.make_custom(1, 11, 13, 2, 64, 64, dtype, seed=17, log_g_const=log_g)
+    _note(f"bwd matrix path {dtype} constant log_g {log_g}")
+    _run_case(oracle_mod, x, dtype, 1, chunk=64, seed=5)
+
+
+def test_bwd_matrix_path_mixed_spans(oracle_mod):
+    """Some chunks in range, others flagged (one channel decays fast in the second
+    half of the scan only)."""
+    x = W.make_custom(1, 16, 16, 2, 64, 64, "f16", seed=23)
+    lg = x["log_g"].reshape(1, 256, 2, 64)
+    lg[:, 128:, 1, 5] = -3.0
+    x["log_g"] = np.ascontiguousarray(lg.reshape(x["log_g"].shape))
+    _note("bwd matrix path mixed spans")
+    _run_case(oracle_mod, x, "f16", 0, chunk=64, seed=6)
 
 
 def test_bwd_mixer_640_sampled(oracle_mod):
