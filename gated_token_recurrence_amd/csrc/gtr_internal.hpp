@@ -120,8 +120,9 @@ __device__ __forceinline__ int64_t scan_row(const GlaArgs &a, int b, int h, int6
 hipError_t serial_summary(const GlaArgs &a, float *U, float *G, int n_chunks, hipStream_t s);
 hipError_t serial_output(const GlaArgs &a, const float *Sx, int n_chunks, hipStream_t s);
 // Inter-chunk (or inter-segment) state scan, in place: U[n] <- S before unit n.
+// G: summed gates of each unit, natural log (log2_gates: log2 units).
 hipError_t state_scan(float *U, const float *G, int n_seq, int n_units, int dk, int dv,
-                      hipStream_t s);
+                      hipStream_t s, bool log2_gates = false);
 // MFMA chunk path.  The B*H*N chunks (N per sequence, sequence-major) are cut
 // into ranges of Q chunks, one per workgroup; segments are the pieces of those
 // ranges within one sequence.  Segment k starts at the k-th element of the

@@ -665,10 +665,21 @@ hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void
     float *dO = Gr + ncb * a.dk, *qdq = dO + rows * a.dv, *Tn = qdq + rows * a.dk;
     float *dWp = Tn + ncb * a.dk;
     int *flags = reinterpret_cast<int *>(dWp + ncb * a.dv);
-    // forward incoming states: the forward path's chunk summaries and scan
-    hipError_t e = serial_summary(a, Uf, Gf, n_chunks, st);
+    // forward incoming states: the forward path's chunk summaries (the matrix-core
+    // kernel with one chunk per segment where it applies; log2 gate totals) and scan
+    auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
+    const bool msum = sum_supported(a) && !a.feat && !a.resid && al16(a.k) && al16(a.v) &&
+                      al16(a.log_g);
+    hipError_t e;
+    if (msum) {
+        MfmaPlan ps, po;
+        mfma_plans(a, 1, &ps, &po);
+        e = sum_launch(a, ps, Uf, Gf, st);
+    } else {
+        e = serial_summary(a, Uf, Gf, n_chunks, st);
+    }
     if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
-    e = state_scan(Uf, Gf, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st);
+    e = state_scan(Uf, Gf, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st, msum);
     if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
     BwdArgs p{a, dy, Uf, nullptr, dO, qdq, Ur, Gr, Tn, dWp, dq, dk, dv, dz, dlog_g, drms_w,
               nullptr, n_chunks};

@@ -18,7 +18,7 @@ constexpr int PF = 8;  // units fetched ahead of the dependent chain
 
 __global__ __launch_bounds__(NT) void k_state_scan(float *__restrict__ U,
                                                    const float *__restrict__ G, int64_t n_elem,
-                                                   int n_units, int dk, int dv) {
+                                                   int n_units, int dk, int dv, bool log2_gates) {
     const int64_t e = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
     if (e >= n_elem) return;
     const int64_t dd = static_cast<int64_t>(dk) * dv;
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(NT) void k_state_scan(float *__restrict__ U,
         for (int i = 0; i < PF; ++i) {
             if (n0 + i < n_units) {
                 u[static_cast<int64_t>(n0 + i) * dd] = s;
-                s = expf(gg[i]) * s + x[i];
+                s = (log2_gates ? __builtin_amdgcn_exp2f(gg[i]) : expf(gg[i])) * s + x[i];
             }
         }
     }
@@ -162,8 +162,9 @@ __global__ __launch_bounds__(NT) void k_scan_rows(float *__restrict__ U,
 
 // The same four-part fold for plain sequences of n_units units each (unit k of
 // sequence seq at index seq n_units + k), any dv: each lane takes its own key
-// channel.  Workgroup = (sequence, 64 consecutive state elements).
-template <int M>
+// channel.  Workgroup = (sequence, 64 consecutive state elements).  LOG2: the
+// unit gate totals G are in log2 units (else natural).
+template <int M, bool LOG2>
 __global__ __launch_bounds__(NT) void k_scan_rows_seq(float *__restrict__ U,
                                                       const float *__restrict__ G, int n_units,
                                                       int dk, int dv) {
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(NT) void k_scan_rows_seq(float *__restrict__ U,
         const float xv = U[k * dd + el];
         const float gv = G[k * dk + c];
         x[i] = (i < n) ? xv : 0.f;
-        e[i] = (i < n) ? expf(gv) : 1.f;
+        e[i] = (i < n) ? (LOG2 ? __builtin_amdgcn_exp2f(gv) : expf(gv)) : 1.f;
     }
     float A = 1.f, B = 0.f;
 #pragma unroll
@@ -229,22 +230,33 @@ hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_s
     return hipGetLastError();
 }
 
+namespace {
+template <int M>
+void launch_rows_seq(float *U, const float *G, int n_units, int dk, int dv, bool log2_gates,
+                     dim3 grid, hipStream_t s) {
+    if (log2_gates)
+        hipLaunchKernelGGL((k_scan_rows_seq<M, true>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+    else
+        hipLaunchKernelGGL((k_scan_rows_seq<M, false>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+}
+}  // namespace
+
 hipError_t state_scan(float *U, const float *G, int n_seq, int n_units, int dk, int dv,
-                      hipStream_t s) {
+                      hipStream_t s, bool log2_gates) {
     const int64_t n_elem = static_cast<int64_t>(n_seq) * dk * dv;
     if ((static_cast<int64_t>(dk) * dv) % 64 == 0 && n_units <= 4 * 64) {
         // the four-part fold: memory latency paid about once per sequence
         const dim3 grid(static_cast<unsigned>(n_elem / 64));
         if (n_units <= 4 * 16)
-            hipLaunchKernelGGL((k_scan_rows_seq<16>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+            launch_rows_seq<16>(U, G, n_units, dk, dv, log2_gates, grid, s);
         else if (n_units <= 4 * 32)
-            hipLaunchKernelGGL((k_scan_rows_seq<32>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+            launch_rows_seq<32>(U, G, n_units, dk, dv, log2_gates, grid, s);
         else
-            hipLaunchKernelGGL((k_scan_rows_seq<64>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+            launch_rows_seq<64>(U, G, n_units, dk, dv, log2_gates, grid, s);
         return hipGetLastError();
     }
     const dim3 grid(static_cast<unsigned>((n_elem + NT - 1) / NT));
-    hipLaunchKernelGGL(k_state_scan, grid, dim3(NT), 0, s, U, G, n_elem, n_units, dk, dv);
+    hipLaunchKernelGGL(k_state_scan, grid, dim3(NT), 0, s, U, G, n_elem, n_units, dk, dv, log2_gates);
     return hipGetLastError();
 }
 
