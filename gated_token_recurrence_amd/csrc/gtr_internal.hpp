@@ -196,6 +196,10 @@ size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks);
 // chunk <= 64.  Chunks whose decay span is out of range are flagged (flags[chunk] = 1)
 // and left to the token-serial kernels.
 bool bgrad_supported(const GlaArgs &a);
+// Matrix-core epilogue backward and reverse chunk summaries (same support):
+// dO, dz, drms_w partials, Ur and Gr (log2) per chunk; flags as bgrad_launch.
+hipError_t bdo_launch(const GlaArgs &a, const void *dy, const float *Sx, float *dO, void *dz,
+                      float *dWp, float *Ur, float *Gr, int *flags, int n_chunks, hipStream_t s);
 hipError_t bgrad_launch(const GlaArgs &a, const float *dO, const float *Sx, const float *Er,
                         void *dq, void *dk, void *dv, float *dlog_g, int *flags, int n_chunks,
                         hipStream_t s);

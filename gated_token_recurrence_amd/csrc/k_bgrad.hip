@@ -141,16 +141,15 @@ struct ChunkAt {
     int n, bh, b, h, nt;
     int64_t t0;
     size_t cidx, ridx;
-    __device__ ChunkAt(const BgArgs &p, int64_t c) {
-        const GlaArgs &a = p.a;
-        n = static_cast<int>(c % p.n_chunks);
-        bh = static_cast<int>(c / p.n_chunks);
+    __device__ ChunkAt(const GlaArgs &a, int n_chunks, int64_t c) {
+        n = static_cast<int>(c % n_chunks);
+        bh = static_cast<int>(c / n_chunks);
         b = bh / a.H;
         h = bh % a.H;
         t0 = static_cast<int64_t>(n) * a.chunk;
         nt = static_cast<int>((t0 + a.chunk < a.L) ? a.chunk : a.L - t0);
         cidx = static_cast<size_t>(c);
-        ridx = static_cast<size_t>(bh) * p.n_chunks + (p.n_chunks - 1 - n);
+        ridx = static_cast<size_t>(bh) * n_chunks + (n_chunks - 1 - n);
     }
     // global row of token t; rows past the chunk's end repeat its last row
     __device__ int64_t row(const GlaArgs &a, int t) const {
@@ -199,6 +198,46 @@ __device__ __forceinline__ void request_state(StateIn &in, const BgArgs &p, cons
     }
 }
 
+// Cumulative gates of a chunk from its log_g pieces (fp32 layout): A2[t][c] =
+// 2^a (a: in-chunk inclusive cumulative log2-gate, rows past nt add nothing),
+// G2[c] = 2^G; returns G of channel tid % 64 (log2).  A 4-segment scan: wave w
+// takes tokens [16 w, 16 w + 16).  Ends before a barrier the caller places.
+__device__ __forceinline__ float chunk_gates(const float4 (&xg)[4], float (*A2)[LS], float *G2,
+                                             float (*tot4)[BC], int nt, int tid) {
+    const int w = tid >> 6, l = tid & 63;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+        const bool ok = t < nt;
+        const float4 x = xg[u];
+        st4(&A2[t][c], make_float4(ok ? x.x * kLog2e : 0.f, ok ? x.y * kLog2e : 0.f,
+                                   ok ? x.z * kLog2e : 0.f, ok ? x.w * kLog2e : 0.f));
+    }
+    __syncthreads();
+    float cum[16];
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            acc += A2[16 * w + s][l];
+            cum[s] = acc;
+        }
+        tot4[w][l] = acc;
+    }
+    __syncthreads();
+    float off = 0.f, tot = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float x = tot4[u][l];
+        off += (u < w) ? x : 0.f;
+        tot += x;
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) A2[16 * w + s][l] = fexp2(cum[s] + off);
+    if (w == 0) G2[l] = fexp2(tot);
+    return tot;
+}
+
 template <int DT>
 __device__ __forceinline__ uint4 pack8(const float *x) {
     uint32_t u[4];
@@ -222,50 +261,20 @@ __global__ __launch_bounds__(NT, 1) void k_bgrad(BgArgs p) {
 
     int64_t ch = blockIdx.x;
     int buf = 0;
-    if (tid < BC) srow[0][tid] = ChunkAt(p, ch).row(a, tid);
+    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, ch).row(a, tid);
     __syncthreads();
     TokIn in;
     StateIn st_in;
     request_tok(in, p, srow[0], tid);
-    request_state(st_in, p, ChunkAt(p, ch), tid);
+    request_state(st_in, p, ChunkAt(a, p.n_chunks, ch), tid);
 
     for (; ch < total; ch += gridDim.x, buf ^= 1) {
-        const ChunkAt at(p, ch);
+        const ChunkAt at(a, p.n_chunks, ch);
         const int64_t *rows = srow[buf];
         const int nt = at.nt;
         const int64_t cn = ch + gridDim.x;  // next chunk of this workgroup
 
-        // ---- cumulative gates (log2 units): raw values, then a 4-segment scan per channel
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
-            const bool ok = t < nt;
-            const float4 x = in.g[u];
-            st4(&sA2[t][c], make_float4(ok ? x.x * kLog2e : 0.f, ok ? x.y * kLog2e : 0.f,
-                                        ok ? x.z * kLog2e : 0.f, ok ? x.w * kLog2e : 0.f));
-        }
-        __syncthreads();
-        float cum[16];
-        {
-            float acc = 0.f;
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                acc += sA2[16 * w + s][l];
-                cum[s] = acc;
-            }
-            sTot[w][l] = acc;
-        }
-        __syncthreads();
-        float off = 0.f, tot = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float x = sTot[u][l];
-            off += (u < w) ? x : 0.f;
-            tot += x;
-        }
-#pragma unroll
-        for (int s = 0; s < 16; ++s) sA2[16 * w + s][l] = fexp2(cum[s] + off);
-        if (w == 0) sG[l] = fexp2(tot);
+        const float tot = chunk_gates(in.g, sA2, sG, sTot, nt, tid);
         const bool slow = __syncthreads_or(-tot > kSpanMax);  // uniform over the workgroup
         if (tid == 0) p.flags[at.cidx] = slow ? 1 : 0;
 
@@ -305,11 +314,11 @@ __global__ __launch_bounds__(NT, 1) void k_bgrad(BgArgs p) {
             }
         }
         // ---- the next chunk's rows, then its per-token inputs (those registers are free)
-        if (cn < total && tid < BC) srow[buf ^ 1][tid] = ChunkAt(p, cn).row(a, tid);
+        if (cn < total && tid < BC) srow[buf ^ 1][tid] = ChunkAt(a, p.n_chunks, cn).row(a, tid);
         __syncthreads();
         if (cn < total) request_tok(in, p, srow[buf ^ 1], tid);
         if (slow) {  // the whole workgroup; its gradients come from the token-serial kernels
-            if (cn < total) request_state(st_in, p, ChunkAt(p, cn), tid);
+            if (cn < total) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
             continue;
         }
 
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(NT, 1) void k_bgrad(BgArgs p) {
             const float ee[4] = {gt * ev.x, gt * ev.y, gt * ev.z, gt * ev.w};
             put<4>(sSE, t, c, ee);
         }
-        if (cn < total) request_state(st_in, p, ChunkAt(p, cn), tid);
+        if (cn < total) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
         __syncthreads();
         // dq out; q . dq of this thread's pieces
         float qdq[2][8];
@@ -473,12 +482,257 @@ __global__ __launch_bounds__(NT, 1) void k_bgrad(BgArgs p) {
     }
 }
 
+// ---- The epilogue backward and the reverse chunk summary (they precede the
+// gradients): per chunk, with S the forward incoming state,
+//   O = Q~ S + P V                      (the forward outputs before RMSNorm)
+//   r = (mean(o^2) + eps)^-1/2, n = r o, dn = dy w silu(z)
+//   dO = r (dn - n mean(dn n)),  dz = dy n w silu'(z),  drms_w partial = sum dy n silu(z)
+//   Ur = Q~^T dO = sum_i 2^(a_i) q_i dO_i^T   (the chunk's gradient state from zero,
+//                                              times its first gate), with G (log2)
+// Same workgroup layout as the gradient kernel; the epilogue runs in the load
+// layout (a thread holds 8 columns of a row; the 8 lanes of a row reduce together)
+// through an fp32 staging matrix.
+struct BdArgs {
+    GlaArgs a;
+    const void *dy;     // gradient of out, I/O type
+    const float *Sx;    // forward incoming state per chunk [bh N + n][64][64]
+    float *dO;          // [rows][64]
+    void *dz;
+    float *dWp;         // [bh N + n][64] drms_w partials
+    float *Ur, *Gr;     // reverse summaries and chunk gates (log2), reversed chunk order
+    int *flags;         // per chunk: 1 = left to the token-serial kernels
+    int n_chunks;
+};
+
+struct DoIn {
+    float4 g[4], S[4];
+    uint4 q[2], k[2], v[2], z[2], dy[2];
+};
+
+__device__ __forceinline__ void request_do(DoIn &in, const BdArgs &p, const ChunkAt &at,
+                                           const int64_t *rows, int tid) {
+    const GlaArgs &a = p.a;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+        in.g[u] = ld4(a.log_g + rows[t] * DK + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
+        const int64_t rk = rows[t] * DK + c, rv = rows[t] * BC + c;
+        in.q[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + rk);
+        in.k[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + rk);
+        in.v[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + rv);
+        in.z[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.z) + rv);
+        in.dy[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.dy) + rv);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+        in.S[u] = ld4(p.Sx + at.cidx * MAT + t * BC + c);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(NT, 1) void k_bdo(BdArgs p) {
+    const GlaArgs &a = p.a;
+    // hi + lo planes: Q~; K^, then P^T; V; S, then dO
+    __shared__ __attribute__((aligned(16))) uint16_t sQT[2 * MAT], sKP[2 * MAT], sV[2 * MAT], sSD[2 * MAT];
+    __shared__ __attribute__((aligned(16))) float sX[BC][LS];  // 2^a, then O, then Ur (staging)
+    __shared__ float sG[BC], sTot[4][BC], sW[4][BC];
+    __shared__ int64_t srow[2][BC];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
+    const int64_t total = static_cast<int64_t>(a.B) * a.H * p.n_chunks;
+    // rms_w of this thread's eight load-layout columns
+    float rw[8];
+    {
+        const int c = (tid & 7) * 8;
+        const float4 w0 = ld4(a.rms_w + c), w1 = ld4(a.rms_w + c + 4);
+        rw[0] = w0.x; rw[1] = w0.y; rw[2] = w0.z; rw[3] = w0.w;
+        rw[4] = w1.x; rw[5] = w1.y; rw[6] = w1.z; rw[7] = w1.w;
+    }
+
+    int64_t ch = blockIdx.x;
+    int buf = 0;
+    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, ch).row(a, tid);
+    __syncthreads();
+    DoIn in;
+    request_do(in, p, ChunkAt(a, p.n_chunks, ch), srow[0], tid);
+
+    for (; ch < total; ch += gridDim.x, buf ^= 1) {
+        const ChunkAt at(a, p.n_chunks, ch);
+        const int64_t *rows = srow[buf];
+        const int nt = at.nt;
+        const int64_t cn = ch + gridDim.x;
+
+        const float tot = chunk_gates(in.g, sX, sG, sTot, nt, tid);
+        const bool slow = __syncthreads_or(-tot > kSpanMax);
+        if (tid == 0) p.flags[at.cidx] = slow ? 1 : 0;
+
+        uint4 zy[2][2];  // z and dy pieces, kept for the epilogue
+        if (!slow) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
+                const bool ok = t < nt;
+                float q8[8], k8[8], v8[8];
+                unpack8<DT>(in.q[u], q8);
+                unpack8<DT>(in.k[u], k8);
+                unpack8<DT>(in.v[u], v8);
+                zy[u][0] = in.z[u];
+                zy[u][1] = in.dy[u];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float e = sX[t][c + s];
+                    q8[s] = ok ? q8[s] * e : 0.f;
+                    k8[s] = ok ? k8[s] * frcp(e) : 0.f;
+                    v8[s] = ok ? v8[s] : 0.f;
+                }
+                put<8>(sQT, t, c, q8);
+                put<8>(sKP, t, c, k8);
+                put<8>(sV, t, c, v8);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+                const float4 sv = in.S[u];
+                const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
+                put<4>(sSD, t, c, ss);
+            }
+        }
+        if (cn < total && tid < BC) srow[buf ^ 1][tid] = ChunkAt(a, p.n_chunks, cn).row(a, tid);
+        __syncthreads();
+        if (cn < total) request_do(in, p, ChunkAt(a, p.n_chunks, cn), srow[buf ^ 1], tid);
+        if (slow) continue;  // the whole workgroup; the token-serial kernels take the chunk
+
+        f32x4 acc[4];
+        // ---- P = (Q~ K^^T) . M, rows i of wave w; P^T replaces K^
+        zero4(acc);
+        gemm<NAT, NAT>(acc, sQT, sKP, w, lr, g);     // B(k=c, n=j) = K^[j][c]
+        __syncthreads();  // K^ is read
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * w + 4 * g + r) ? acc[t][r] : 0.f;
+            put<4>(sKP, 16 * t + lr, 16 * w + 4 * g, x);
+        }
+        __syncthreads();
+        // ---- O = Q~ S + P V, rows i of wave w, staged
+        zero4(acc);
+        gemm<PERM, TRN>(acc, sQT, sSD, w, lr, g);    // A = Q~[i][c], B(k=c, n=d) = S[c][d]
+        gemm<TRN, TRN>(acc, sKP, sV, w, lr, g);      // A(m=i, k=j) = P[i][j], B(k=j, n=d) = V[j][d]
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[16 * w + 4 * g + r][16 * t + lr] = acc[t][r];
+        __syncthreads();  // O staged; S is read
+
+        // ---- epilogue backward in the load layout: rows t, columns c .. c + 7
+        float wp[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) wp[s] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
+            const bool ok = t < nt;
+            float o[8], z8[8], dy8[8];
+            const float4 o0 = ld4(&sX[t][c]), o1 = ld4(&sX[t][c + 4]);
+            o[0] = o0.x; o[1] = o0.y; o[2] = o0.z; o[3] = o0.w;
+            o[4] = o1.x; o[5] = o1.y; o[6] = o1.z; o[7] = o1.w;
+            unpack8<DT>(zy[u][0], z8);
+            unpack8<DT>(zy[u][1], dy8);
+            float ss = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) ss += o[s] * o[s];
+            ss += __shfl_xor(ss, 1);
+            ss += __shfl_xor(ss, 2);
+            ss += __shfl_xor(ss, 4);
+            const float r = 1.0f / sqrtf(ss / BC + GTR_RMS_EPS);
+            float nn[8], dn[8], sg[8], md = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                nn[s] = o[s] * r;
+                sg[s] = 1.0f / (1.0f + expf(-z8[s]));
+                dn[s] = dy8[s] * rw[s] * (z8[s] * sg[s]);
+                md += dn[s] * nn[s];
+            }
+            md += __shfl_xor(md, 1);
+            md += __shfl_xor(md, 2);
+            md += __shfl_xor(md, 4);
+            md *= 1.0f / BC;
+            float dov[8], dzv[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                dov[s] = ok ? r * (dn[s] - nn[s] * md) : 0.f;
+                dzv[s] = dy8[s] * nn[s] * rw[s] * sg[s] * (1.0f + z8[s] * (1.0f - sg[s]));
+                wp[s] += ok ? dy8[s] * nn[s] * (z8[s] * sg[s]) : 0.f;
+            }
+            put<8>(sSD, t, c, dov);
+            if (ok) {
+                float *dst = p.dO + rows[t] * BC + c;
+                st4(dst, make_float4(dov[0], dov[1], dov[2], dov[3]));
+                st4(dst + 4, make_float4(dov[4], dov[5], dov[6], dov[7]));
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dz) + rows[t] * BC + c) = pack8<DT>(dzv);
+            }
+        }
+        // drms_w partial: the 8 rows of this wave that share the columns, then the waves
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            float x = wp[s];
+            x += __shfl_xor(x, 8);
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            wp[s] = x;
+        }
+        if (l < 8) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) sW[w][8 * l + s] = wp[s];
+        }
+        __syncthreads();  // dO in LDS; O is read
+
+        // ---- Ur = Q~^T dO, rows c of wave w, staged; G and the drms_w partial
+        zero4(acc);
+        gemm<TRN, TRN>(acc, sQT, sSD, w, lr, g);     // A(m=c, k=i) = Q~[i][c], B(k=i, n=d) = dO[i][d]
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[16 * w + 4 * g + r][16 * t + lr] = acc[t][r];
+        if (w == 0) {
+            p.Gr[at.ridx * BC + l] = tot;
+            p.dWp[at.cidx * BC + l] = (sW[0][l] + sW[1][l]) + (sW[2][l] + sW[3][l]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+            st4(p.Ur + at.ridx * MAT + t * BC + c, ld4(&sX[t][c]));
+        }
+        __syncthreads();  // LDS is rewritten by the next chunk
+    }
+}
+
 }  // namespace
 
 bool bgrad_supported(const GlaArgs &a) {
     auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
     return (a.dtype == DT_F16 || a.dtype == DT_BF16) && a.dk == 64 && a.dv == 64 && a.chunk <= 64 &&
            !a.resid && al16(a.q) && al16(a.k) && al16(a.v) && al16(a.log_g);
+}
+
+hipError_t bdo_launch(const GlaArgs &a, const void *dy, const float *Sx, float *dO, void *dz,
+                      float *dWp, float *Ur, float *Gr, int *flags, int n_chunks, hipStream_t s) {
+    const BdArgs p{a, dy, Sx, dO, dz, dWp, Ur, Gr, flags, n_chunks};
+    const int64_t total = static_cast<int64_t>(a.B) * a.H * n_chunks;
+    const dim3 grid(static_cast<unsigned>(total < kPersistent ? total : kPersistent));
+    if (a.dtype == DT_F16)
+        hipLaunchKernelGGL((k_bdo<DT_F16>), grid, dim3(NT), 0, s, p);
+    else if (a.dtype == DT_BF16)
+        hipLaunchKernelGGL((k_bdo<DT_BF16>), grid, dim3(NT), 0, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t bgrad_launch(const GlaArgs &a, const float *dO, const float *Sx, const float *Er,

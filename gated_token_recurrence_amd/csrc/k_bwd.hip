@@ -30,6 +30,7 @@ namespace gtr {
 namespace {
 
 constexpr int NT = 256;
+constexpr float kLog2e = 1.44269504088896340736f;
 
 template <int DK, int DV> struct BwdShape {
     static constexpr int PER = DK * DV / NT;      // state elements per thread
@@ -88,7 +89,8 @@ struct ChunkPos {
 
 // ---- B1: forward walk.  Pass 1 (map A): o_t, epilogue backward -> do_t (global),
 // dz_t, drms_w partials.  Pass 2 (map B): dq_t = S_t do_t, q dq (fp32, global).
-// MODE 0: both passes; 1: pass 1 only; 2: pass 2 only, for the flagged chunks.
+// MODE 0: both passes; 1: pass 1 only; 2: pass 2 only, for the flagged chunks;
+// 3: pass 1 only, for the flagged chunks.
 template <int DT, int DK, int DV, int MODE>
 __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
     using Sh = BwdShape<DK, DV>;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
     const int tid = threadIdx.x;
     const ChunkPos cp(a, p.n_chunks);
     const size_t soff = cp.cid() * DK * DV;
-    if (MODE == 2 && p.flags[cp.cid()] == 0) return;  // the whole workgroup
+    if ((MODE == 2 || MODE == 3) && p.flags[cp.cid()] == 0) return;  // the whole workgroup
 
     // ---- pass 1, map A
     if constexpr (MODE != 2) {
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
             p.dWp[cp.cid() * DV + tid] = w;
         }
     }
-    if constexpr (MODE == 1) return;
+    if constexpr (MODE == 1 || MODE == 3) return;
     __syncthreads();  // this workgroup's do_t writes are visible to its own reads below
 
     // ---- pass 2, map B: dq_t = S_t do_t
@@ -293,8 +295,9 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
 
 // ---- B2: reverse summary of each chunk (map A; no sums): dS walked from the
 // chunk's last token to its first from zero, then Diag(g_first) dS; written with
-// the chunk's summed log-gate at the reversed chunk index.
-template <int DT, int DK, int DV>
+// the chunk's summed gate (log2 units) at the reversed chunk index.  FLAGGED:
+// only the chunks left to the token-serial kernels.
+template <int DT, int DK, int DV, bool FLAGGED>
 __global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
     using Sh = BwdShape<DK, DV>;
     constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, TILE = Sh::TILE;
@@ -304,6 +307,7 @@ __global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
     __shared__ int64_t srow[TILE];
     const int tid = threadIdx.x;
     const ChunkPos cp(a, p.n_chunks);
+    if (FLAGGED && p.flags[cp.cid()] == 0) return;  // the whole workgroup
     const int j = tid % DV, c0 = tid / DV;
     float s[PER], gnext[PER];
 #pragma unroll
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
     if (tid < DK) {
         float gsum = 0.f;
         for (int r = tid; r < NT; r += DK) gsum += gpart[r];
-        p.Gr[ridx * DK + tid] = gsum;
+        p.Gr[ridx * DK + tid] = gsum * kLog2e;
     }
 }
 
@@ -595,20 +599,27 @@ hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hoo
     // matrix-core gradients where the shape allows (16-bit I/O, dk = dv = 64)
     auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
     const bool mfma = DT != DT_F32 && DK == 64 && DV == 64 && bgrad_supported(p.a) && al16(p.dq) &&
-                      al16(p.dk) && al16(p.dv);
-    hipError_t e;
-    if (mfma)
-        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 1>), grid, dim3(NT), 0, st, p);
-    else
-        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 0>), grid, dim3(NT), 0, st, p);
-    if ((e = done()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_revsum<DT, DK, DV>), grid, dim3(NT), 0, st, p);
-    if ((e = done()) != hipSuccess) return e;
-    e = state_scan(p.Ur, p.Gr, static_cast<int>(p.a.B * p.a.H), p.n_chunks, DK, DV, st);
-    if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+                      al16(p.dk) && al16(p.dv) && al16(p.dz) && al16(p.dy) && al16(p.a.z) &&
+                      al16(p.a.rms_w);
     BwdArgs q = p;
-    q.Er = p.Ur;  // scanned in place
     q.flags = flags;
+    hipError_t e;
+    if (mfma) {
+        e = bdo_launch(p.a, p.dy, p.Sx, p.dO, p.dz, p.dWp, p.Ur, p.Gr, flags, p.n_chunks, st);
+        if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+        // chunks out of the matrix path's exponent range: token-serial dO and summaries
+        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 3>), grid, dim3(NT), 0, st, q);
+        if ((e = done()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_bwd_revsum<DT, DK, DV, true>), grid, dim3(NT), 0, st, q);
+    } else {
+        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 0>), grid, dim3(NT), 0, st, p);
+        if ((e = done()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_bwd_revsum<DT, DK, DV, false>), grid, dim3(NT), 0, st, p);
+    }
+    if ((e = done()) != hipSuccess) return e;
+    e = state_scan(p.Ur, p.Gr, static_cast<int>(p.a.B * p.a.H), p.n_chunks, DK, DV, st, true);
+    if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+    q.Er = p.Ur;  // scanned in place
     if (mfma) {
         e = bgrad_launch(p.a, p.dO, p.Sx, q.Er, p.dq, p.dk, p.dv, p.dlog_g, flags, p.n_chunks, st);
         if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
