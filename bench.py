@@ -677,8 +677,8 @@ def main():
                                        + (2 * w.dk + 2 * w.dv) * s_io + 4 * w.dk)   # writes
             if w.dtype != "f32" and w.dk == 64 and w.dv == 64 and w.chunk <= 64:  # matrix-core gradients
                 names_b = ("forward_chunk_summary", "forward_state_scan", "chunk_do_and_summary_mfma",
-                           "fallback_do", "fallback_reverse_summary", "reverse_state_scan",
-                           "chunk_gradients_mfma", "fallback_dq", "fallback_dk_dv_dlog_g", "rms_w_sum")
+                           "fallback_do_and_summary", "reverse_state_scan", "chunk_gradients_mfma",
+                           "fallback_gradients", "rms_w_sum")
             else:
                 names_b = ("forward_chunk_summary", "forward_state_scan", "forward_walk_dq",
                            "reverse_chunk_summary", "reverse_state_scan", "reverse_walk_dk_dv",

@@ -522,6 +522,9 @@ gtr_status gtr_gla_bwd(const void *q, const void *k, const void *v, const float 
     void *ws = nullptr;
     s = workspace(stream, bwd_workspace_bytes(a, static_cast<int>(n_chunks)), &ws);
     if (s != GTR_OK) return s;
+    void *ctr = nullptr;  // the drms_w reduction's block counter (left zero)
+    s = counters(stream, 1, &ctr);
+    if (s != GTR_OK) return s;
     Marks mk;
     mk.ev = events;
     mk.n = n_events;
@@ -530,8 +533,8 @@ gtr_status gtr_gla_bwd(const void *q, const void *k, const void *v, const float 
     hooks.ctx = &mk;
     hipError_t e = mk.start(stream);
     if (e == hipSuccess)
-        e = bwd_launch(a, dout, dq, dk, dv, dlog_g, dz, drms_w, ws, static_cast<int>(n_chunks),
-                       stream, hooks);
+        e = bwd_launch(a, dout, dq, dk, dv, dlog_g, dz, drms_w, ws, static_cast<unsigned *>(ctr),
+                       static_cast<int>(n_chunks), stream, hooks);
     if (n_launches) *n_launches = mk.launches;
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return GTR_OK;

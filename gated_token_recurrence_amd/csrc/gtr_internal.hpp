@@ -204,7 +204,7 @@ hipError_t bgrad_launch(const GlaArgs &a, const float *dO, const float *Sx, cons
                         void *dq, void *dk, void *dv, float *dlog_g, int *flags, int n_chunks,
                         hipStream_t s);
 hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
-                      float *dlog_g, void *dz, float *drms_w, void *ws, int n_chunks,
+                      float *dlog_g, void *dz, float *drms_w, void *ws, unsigned *ctr, int n_chunks,
                       hipStream_t st, const BwdLaunchHooks &hooks);
 // State scan over the segments of a plan, in place: U[k] <- state before segment k.
 hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,

@@ -504,98 +504,164 @@ struct BdArgs {
     int n_chunks;
 };
 
+// Eight waves (two per SIMD, so that one wave's LDS, matrix-unit and memory
+// waits overlap the other's work): wave w computes rows [16 (w % 4), + 16) and
+// columns [32 (w / 4), + 32) of every product.
+constexpr int NW = 8;
+constexpr int NTB = 64 * NW;
+
+// acc[tt] += A[16 rs + .., :] B[:, 16 (2 ch + tt) + ..], tt = 0, 1 (modes as gemm)
+template <int MA, int MB>
+__device__ __forceinline__ void gemm2(f32x4 (&acc)[2], const uint16_t *A, const uint16_t *B, int rs,
+                                      int ch, int lr, int g) {
+    static_assert((MA == NAT) == (MB == NAT), "both operands must use one k slot order");
+#pragma unroll
+    for (int kap = 0; kap < 2; ++kap) {
+        s16x8 ah, al;
+        fetch<MA>(A, 16 * rs + lr, lr, g, kap, ah, al);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            s16x8 bh, bl;
+            fetch<MB>(B, 16 * (2 * ch + tt) + lr, lr, g, kap, bh, bl);
+            acc[tt] = mma<false>(ah, bh, acc[tt]);
+            acc[tt] = mma<false>(ah, bl, acc[tt]);
+            acc[tt] = mma<false>(al, bh, acc[tt]);
+        }
+    }
+}
+
+__device__ __forceinline__ void zero2(f32x4 (&acc)[2]) {
+    acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// chunk_gates for eight waves: fp32 pieces i = tid + 512 u (u < 2); wave w scans
+// tokens [8 w, 8 w + 8)
+__device__ __forceinline__ float chunk_gates8(const float4 (&xg)[2], float (*A2)[LS], float *G2,
+                                              float (*tot8)[BC], int nt, int tid) {
+    const int w = tid >> 6, l = tid & 63;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
+        const bool ok = t < nt;
+        const float4 x = xg[u];
+        st4(&A2[t][c], make_float4(ok ? x.x * kLog2e : 0.f, ok ? x.y * kLog2e : 0.f,
+                                   ok ? x.z * kLog2e : 0.f, ok ? x.w * kLog2e : 0.f));
+    }
+    __syncthreads();
+    float cum[8];
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            acc += A2[8 * w + s][l];
+            cum[s] = acc;
+        }
+        tot8[w][l] = acc;
+    }
+    __syncthreads();
+    float off = 0.f, tot = 0.f;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+        const float x = tot8[u][l];
+        off += (u < w) ? x : 0.f;
+        tot += x;
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) A2[8 * w + s][l] = fexp2(cum[s] + off);
+    if (w == 0) G2[l] = fexp2(tot);
+    return tot;
+}
+
+// Per-chunk inputs of the epilogue kernel: fp32 pieces i = tid + 512 u (u < 2),
+// rows i / 16, columns 4 (i % 16); 16-bit pieces: row tid / 8, columns 8 (tid % 8).
 struct DoIn {
-    float4 g[4], S[4];
-    uint4 q[2], k[2], v[2], z[2], dy[2];
+    float4 g[2], S[2];
+    uint4 q, k, v, z, dy;
 };
 
 __device__ __forceinline__ void request_do(DoIn &in, const BdArgs &p, const ChunkAt &at,
                                            const int64_t *rows, int tid) {
     const GlaArgs &a = p.a;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
         in.g[u] = ld4(a.log_g + rows[t] * DK + c);
+    }
+    {
+        const int t = tid >> 3, c = (tid & 7) * 8;
+        const int64_t rk = rows[t] * DK + c, rv = rows[t] * BC + c;
+        in.q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + rk);
+        in.k = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + rk);
+        in.v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + rv);
+        in.z = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.z) + rv);
+        in.dy = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.dy) + rv);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
-        const int64_t rk = rows[t] * DK + c, rv = rows[t] * BC + c;
-        in.q[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + rk);
-        in.k[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + rk);
-        in.v[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + rv);
-        in.z[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.z) + rv);
-        in.dy[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.dy) + rv);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+        const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
         in.S[u] = ld4(p.Sx + at.cidx * MAT + t * BC + c);
     }
 }
 
 template <int DT>
-__global__ __launch_bounds__(NT, 1) void k_bdo(BdArgs p) {
+__global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
     const GlaArgs &a = p.a;
     // hi + lo planes: Q~; K^, then P^T; V; S, then dO
     __shared__ __attribute__((aligned(16))) uint16_t sQT[2 * MAT], sKP[2 * MAT], sV[2 * MAT], sSD[2 * MAT];
     __shared__ __attribute__((aligned(16))) float sX[BC][LS];  // 2^a, then O, then Ur (staging)
-    __shared__ float sG[BC], sTot[4][BC], sW[4][BC];
+    __shared__ float sG[BC], sTot[NW][BC], sW[NW][BC];
     __shared__ int64_t srow[2][BC];
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
+    const int rs = w & 3, ch2 = w >> 2;  // row stripe, column half
     const int64_t total = static_cast<int64_t>(a.B) * a.H * p.n_chunks;
-    // rms_w of this thread's eight load-layout columns
-    float rw[8];
+    const int et = tid >> 3, ec = (tid & 7) * 8;  // load-layout row and columns of this thread
+    float rw[8];                                  // rms_w of those columns
     {
-        const int c = (tid & 7) * 8;
-        const float4 w0 = ld4(a.rms_w + c), w1 = ld4(a.rms_w + c + 4);
+        const float4 w0 = ld4(a.rms_w + ec), w1 = ld4(a.rms_w + ec + 4);
         rw[0] = w0.x; rw[1] = w0.y; rw[2] = w0.z; rw[3] = w0.w;
         rw[4] = w1.x; rw[5] = w1.y; rw[6] = w1.z; rw[7] = w1.w;
     }
 
-    int64_t ch = blockIdx.x;
+    int64_t chk = blockIdx.x;
     int buf = 0;
-    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, ch).row(a, tid);
+    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, chk).row(a, tid);
     __syncthreads();
     DoIn in;
-    request_do(in, p, ChunkAt(a, p.n_chunks, ch), srow[0], tid);
+    request_do(in, p, ChunkAt(a, p.n_chunks, chk), srow[0], tid);
 
-    for (; ch < total; ch += gridDim.x, buf ^= 1) {
-        const ChunkAt at(a, p.n_chunks, ch);
+    for (; chk < total; chk += gridDim.x, buf ^= 1) {
+        const ChunkAt at(a, p.n_chunks, chk);
         const int64_t *rows = srow[buf];
         const int nt = at.nt;
-        const int64_t cn = ch + gridDim.x;
+        const int64_t cn = chk + gridDim.x;
 
-        const float tot = chunk_gates(in.g, sX, sG, sTot, nt, tid);
+        const float tot = chunk_gates8(in.g, sX, sG, sTot, nt, tid);
         const bool slow = __syncthreads_or(-tot > kSpanMax);
         if (tid == 0) p.flags[at.cidx] = slow ? 1 : 0;
 
-        uint4 zy[2][2];  // z and dy pieces, kept for the epilogue
+        uint4 zk, yk;  // z and dy, kept for the epilogue
         if (!slow) {
+            const bool ok = et < nt;
+            float q8[8], k8[8], v8[8];
+            unpack8<DT>(in.q, q8);
+            unpack8<DT>(in.k, k8);
+            unpack8<DT>(in.v, v8);
+            zk = in.z;
+            yk = in.dy;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const float e = sX[et][ec + s];
+                q8[s] = ok ? q8[s] * e : 0.f;
+                k8[s] = ok ? k8[s] * frcp(e) : 0.f;
+                v8[s] = ok ? v8[s] : 0.f;
+            }
+            put<8>(sQT, et, ec, q8);
+            put<8>(sKP, et, ec, k8);
+            put<8>(sV, et, ec, v8);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
-                const bool ok = t < nt;
-                float q8[8], k8[8], v8[8];
-                unpack8<DT>(in.q[u], q8);
-                unpack8<DT>(in.k[u], k8);
-                unpack8<DT>(in.v[u], v8);
-                zy[u][0] = in.z[u];
-                zy[u][1] = in.dy[u];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const float e = sX[t][c + s];
-                    q8[s] = ok ? q8[s] * e : 0.f;
-                    k8[s] = ok ? k8[s] * frcp(e) : 0.f;
-                    v8[s] = ok ? v8[s] : 0.f;
-                }
-                put<8>(sQT, t, c, q8);
-                put<8>(sKP, t, c, k8);
-                put<8>(sV, t, c, v8);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+                const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
                 const float4 sv = in.S[u];
                 const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
                 put<4>(sSD, t, c, ss);
@@ -606,43 +672,39 @@ __global__ __launch_bounds__(NT, 1) void k_bdo(BdArgs p) {
         if (cn < total) request_do(in, p, ChunkAt(a, p.n_chunks, cn), srow[buf ^ 1], tid);
         if (slow) continue;  // the whole workgroup; the token-serial kernels take the chunk
 
-        f32x4 acc[4];
-        // ---- P = (Q~ K^^T) . M, rows i of wave w; P^T replaces K^
-        zero4(acc);
-        gemm<NAT, NAT>(acc, sQT, sKP, w, lr, g);     // B(k=c, n=j) = K^[j][c]
+        f32x4 acc[2];
+        // ---- P = (Q~ K^^T) . M; P^T replaces K^
+        zero2(acc);
+        gemm2<NAT, NAT>(acc, sQT, sKP, rs, ch2, lr, g);   // B(k=c, n=j) = K^[j][c]
         __syncthreads();  // K^ is read
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * ch2 + tt;
             float x[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * w + 4 * g + r) ? acc[t][r] : 0.f;
-            put<4>(sKP, 16 * t + lr, 16 * w + 4 * g, x);
+            for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * rs + 4 * g + r) ? acc[tt][r] : 0.f;
+            put<4>(sKP, 16 * t + lr, 16 * rs + 4 * g, x);
         }
         __syncthreads();
-        // ---- O = Q~ S + P V, rows i of wave w, staged
-        zero4(acc);
-        gemm<PERM, TRN>(acc, sQT, sSD, w, lr, g);    // A = Q~[i][c], B(k=c, n=d) = S[c][d]
-        gemm<TRN, TRN>(acc, sKP, sV, w, lr, g);      // A(m=i, k=j) = P[i][j], B(k=j, n=d) = V[j][d]
+        // ---- O = Q~ S + P V, staged
+        zero2(acc);
+        gemm2<PERM, TRN>(acc, sQT, sSD, rs, ch2, lr, g);  // A = Q~[i][c], B(k=c, n=d) = S[c][d]
+        gemm2<TRN, TRN>(acc, sKP, sV, rs, ch2, lr, g);    // A(m=i, k=j) = P[i][j], B(k=j, n=d) = V[j][d]
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sX[16 * w + 4 * g + r][16 * t + lr] = acc[t][r];
+            for (int r = 0; r < 4; ++r) sX[16 * rs + 4 * g + r][16 * (2 * ch2 + tt) + lr] = acc[tt][r];
         __syncthreads();  // O staged; S is read
 
-        // ---- epilogue backward in the load layout: rows t, columns c .. c + 7
-        float wp[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) wp[s] = 0.f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
-            const bool ok = t < nt;
+        // ---- epilogue backward in the load layout: row et, columns ec .. ec + 7
+        {
+            const bool ok = et < nt;
             float o[8], z8[8], dy8[8];
-            const float4 o0 = ld4(&sX[t][c]), o1 = ld4(&sX[t][c + 4]);
+            const float4 o0 = ld4(&sX[et][ec]), o1 = ld4(&sX[et][ec + 4]);
             o[0] = o0.x; o[1] = o0.y; o[2] = o0.z; o[3] = o0.w;
             o[4] = o1.x; o[5] = o1.y; o[6] = o1.z; o[7] = o1.w;
-            unpack8<DT>(zy[u][0], z8);
-            unpack8<DT>(zy[u][1], dy8);
+            unpack8<DT>(zk, z8);
+            unpack8<DT>(yk, dy8);
             float ss = 0.f;
 #pragma unroll
             for (int s = 0; s < 8; ++s) ss += o[s] * o[s];
@@ -654,7 +716,7 @@ __global__ __launch_bounds__(NT, 1) void k_bdo(BdArgs p) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 nn[s] = o[s] * r;
-                sg[s] = 1.0f / (1.0f + expf(-z8[s]));
+                sg[s] = frcp(1.0f + fexp2(-z8[s] * kLog2e));
                 dn[s] = dy8[s] * rw[s] * (z8[s] * sg[s]);
                 md += dn[s] * nn[s];
             }
@@ -662,51 +724,54 @@ __global__ __launch_bounds__(NT, 1) void k_bdo(BdArgs p) {
             md += __shfl_xor(md, 2);
             md += __shfl_xor(md, 4);
             md *= 1.0f / BC;
-            float dov[8], dzv[8];
+            float dov[8], dzv[8], wp[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 dov[s] = ok ? r * (dn[s] - nn[s] * md) : 0.f;
                 dzv[s] = dy8[s] * nn[s] * rw[s] * sg[s] * (1.0f + z8[s] * (1.0f - sg[s]));
-                wp[s] += ok ? dy8[s] * nn[s] * (z8[s] * sg[s]) : 0.f;
+                wp[s] = ok ? dy8[s] * nn[s] * (z8[s] * sg[s]) : 0.f;
             }
-            put<8>(sSD, t, c, dov);
+            put<8>(sSD, et, ec, dov);
             if (ok) {
-                float *dst = p.dO + rows[t] * BC + c;
+                float *dst = p.dO + rows[et] * BC + ec;
                 st4(dst, make_float4(dov[0], dov[1], dov[2], dov[3]));
                 st4(dst + 4, make_float4(dov[4], dov[5], dov[6], dov[7]));
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dz) + rows[t] * BC + c) = pack8<DT>(dzv);
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dz) + rows[et] * BC + ec) = pack8<DT>(dzv);
             }
-        }
-        // drms_w partial: the 8 rows of this wave that share the columns, then the waves
+            // drms_w partial: the 8 rows of this wave that share the columns
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            float x = wp[s];
-            x += __shfl_xor(x, 8);
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            wp[s] = x;
-        }
-        if (l < 8) {
+            for (int s = 0; s < 8; ++s) {
+                float x = wp[s];
+                x += __shfl_xor(x, 8);
+                x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                wp[s] = x;
+            }
+            if (l < 8) {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) sW[w][8 * l + s] = wp[s];
+                for (int s = 0; s < 8; ++s) sW[w][8 * l + s] = wp[s];
+            }
         }
         __syncthreads();  // dO in LDS; O is read
 
-        // ---- Ur = Q~^T dO, rows c of wave w, staged; G and the drms_w partial
-        zero4(acc);
-        gemm<TRN, TRN>(acc, sQT, sSD, w, lr, g);     // A(m=c, k=i) = Q~[i][c], B(k=i, n=d) = dO[i][d]
+        // ---- Ur = Q~^T dO (rows c), staged; G and the drms_w partial (waves in order)
+        zero2(acc);
+        gemm2<TRN, TRN>(acc, sQT, sSD, rs, ch2, lr, g);   // A(m=c, k=i) = Q~[i][c], B(k=i, n=d) = dO[i][d]
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sX[16 * w + 4 * g + r][16 * t + lr] = acc[t][r];
+            for (int r = 0; r < 4; ++r) sX[16 * rs + 4 * g + r][16 * (2 * ch2 + tt) + lr] = acc[tt][r];
         if (w == 0) {
+            float x = 0.f;
+#pragma unroll
+            for (int u = 0; u < NW; ++u) x += sW[u][l];
             p.Gr[at.ridx * BC + l] = tot;
-            p.dWp[at.cidx * BC + l] = (sW[0][l] + sW[1][l]) + (sW[2][l] + sW[3][l]);
+            p.dWp[at.cidx * BC + l] = x;
         }
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
             st4(p.Ur + at.ridx * MAT + t * BC + c, ld4(&sX[t][c]));
         }
         __syncthreads();  // LDS is rewritten by the next chunk
@@ -727,9 +792,9 @@ hipError_t bdo_launch(const GlaArgs &a, const void *dy, const float *Sx, float *
     const int64_t total = static_cast<int64_t>(a.B) * a.H * n_chunks;
     const dim3 grid(static_cast<unsigned>(total < kPersistent ? total : kPersistent));
     if (a.dtype == DT_F16)
-        hipLaunchKernelGGL((k_bdo<DT_F16>), grid, dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((k_bdo<DT_F16>), grid, dim3(NTB), 0, s, p);
     else if (a.dtype == DT_BF16)
-        hipLaunchKernelGGL((k_bdo<DT_BF16>), grid, dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((k_bdo<DT_BF16>), grid, dim3(NTB), 0, s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

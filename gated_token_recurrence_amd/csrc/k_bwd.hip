@@ -70,29 +70,30 @@ struct BwdArgs {
     float *dlog_g, *drms_w;
     const int *flags;    // chunks left to the token-serial gradients (matrix-core path)
     int n_chunks;
+    float *part2;        // [WS_BLOCKS][DV] drms_w block sums
+    unsigned *ctr;       // zero between calls
 };
 
-// Chunk of this workgroup and its token range
+// Chunk c (of B H N, sequence-major) and its token range
 struct ChunkPos {
     int n, bh, b, h;
-    int64_t t0, t1;
-    __device__ ChunkPos(const GlaArgs &a, int n_chunks) {
-        n = blockIdx.x % n_chunks;
-        bh = blockIdx.x / n_chunks;
+    int64_t t0, t1, c;
+    __device__ ChunkPos(const GlaArgs &a, int n_chunks, int64_t c_) : c(c_) {
+        n = static_cast<int>(c % n_chunks);
+        bh = static_cast<int>(c / n_chunks);
         b = bh / a.H;
         h = bh % a.H;
         t0 = static_cast<int64_t>(n) * a.chunk;
         t1 = (t0 + a.chunk < a.L) ? t0 + a.chunk : a.L;
     }
-    __device__ size_t cid() const { return static_cast<size_t>(blockIdx.x); }
+    __device__ size_t cid() const { return static_cast<size_t>(c); }
 };
 
 // ---- B1: forward walk.  Pass 1 (map A): o_t, epilogue backward -> do_t (global),
 // dz_t, drms_w partials.  Pass 2 (map B): dq_t = S_t do_t, q dq (fp32, global).
-// MODE 0: both passes; 1: pass 1 only; 2: pass 2 only, for the flagged chunks;
-// 3: pass 1 only, for the flagged chunks.
+// MODE 0: both passes; 1: pass 1 only; 2: pass 2 only.
 template <int DT, int DK, int DV, int MODE>
-__global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
+__device__ __forceinline__ void fwdwalk_body(const BwdArgs &p, const ChunkPos &cp) {
     using Sh = BwdShape<DK, DV>;
     constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, JSTEP = Sh::JSTEP, TILE = Sh::TILE;
     const GlaArgs &a = p.a;
@@ -103,9 +104,7 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
     __shared__ __attribute__((aligned(16))) float sinv[TILE], smdn[TILE];  // per token: RMSNorm factor, mean(dn n)
     __shared__ int64_t srow[TILE];
     const int tid = threadIdx.x;
-    const ChunkPos cp(a, p.n_chunks);
     const size_t soff = cp.cid() * DK * DV;
-    if ((MODE == 2 || MODE == 3) && p.flags[cp.cid()] == 0) return;  // the whole workgroup
 
     // ---- pass 1, map A
     if constexpr (MODE != 2) {
@@ -227,7 +226,7 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
             p.dWp[cp.cid() * DV + tid] = w;
         }
     }
-    if constexpr (MODE == 1 || MODE == 3) return;
+    if constexpr (MODE == 1) return;
     __syncthreads();  // this workgroup's do_t writes are visible to its own reads below
 
     // ---- pass 2, map B: dq_t = S_t do_t
@@ -295,10 +294,9 @@ __global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
 
 // ---- B2: reverse summary of each chunk (map A; no sums): dS walked from the
 // chunk's last token to its first from zero, then Diag(g_first) dS; written with
-// the chunk's summed gate (log2 units) at the reversed chunk index.  FLAGGED:
-// only the chunks left to the token-serial kernels.
-template <int DT, int DK, int DV, bool FLAGGED>
-__global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
+// the chunk's summed gate (log2 units) at the reversed chunk index.
+template <int DT, int DK, int DV>
+__device__ __forceinline__ void revsum_body(const BwdArgs &p, const ChunkPos &cp) {
     using Sh = BwdShape<DK, DV>;
     constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, TILE = Sh::TILE;
     const GlaArgs &a = p.a;
@@ -306,8 +304,6 @@ __global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
     __shared__ __attribute__((aligned(16))) float gpart[NT];
     __shared__ int64_t srow[TILE];
     const int tid = threadIdx.x;
-    const ChunkPos cp(a, p.n_chunks);
-    if (FLAGGED && p.flags[cp.cid()] == 0) return;  // the whole workgroup
     const int j = tid % DV, c0 = tid / DV;
     float s[PER], gnext[PER];
 #pragma unroll
@@ -364,9 +360,10 @@ __global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
 // ---- B3: reverse walk from the incoming gradient state E.  Pass A (map B):
 // dk_t = dS_t v_t, then q dq - k dk, its reverse cumulative sum inside the chunk
 // (written as dlog_g, completed by B4) and the chunk total.  Pass B (map A):
-// dv_t = dS_t^T k_t.
-template <int DT, int DK, int DV, bool FLAGGED>
-__global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
+// dv_t = dS_t^T k_t.  OFFSET: dlog_g is completed here (the matrix-core path's
+// fallback, which has no offset pass).
+template <int DT, int DK, int DV, bool OFFSET>
+__device__ __forceinline__ void revwalk_body(const BwdArgs &p, const ChunkPos &cp) {
     using Sh = BwdShape<DK, DV>;
     constexpr int PER = Sh::PER, CSTEP = Sh::CSTEP, JSTEP = Sh::JSTEP, TILE = Sh::TILE;
     const GlaArgs &a = p.a;
@@ -376,8 +373,6 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
     __shared__ __attribute__((aligned(16))) float sacc[DK];
     __shared__ int64_t srow[TILE];
     const int tid = threadIdx.x;
-    const ChunkPos cp(a, p.n_chunks);
-    if (FLAGGED && p.flags[cp.cid()] == 0) return;  // the whole workgroup
     const size_t eoff = (static_cast<size_t>(cp.bh) * p.n_chunks + (p.n_chunks - 1 - cp.n)) * DK * DV;
     const int64_t len = cp.t1 - cp.t0;
     const int64_t ntiles = (len + TILE - 1) / TILE;
@@ -426,7 +421,7 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
             // gradient at the next chunk's first token, sum_d E[c][d] S_out[c][d],
             // with S_out the next chunk's incoming state (none after the last chunk)
             float o = 0.f;
-            if (FLAGGED && cp.n + 1 < p.n_chunks) {
+            if (OFFSET && cp.n + 1 < p.n_chunks) {
                 const float *sn = p.Sx + (cp.cid() + 1) * DK * DV + static_cast<size_t>(tid) * DV;
                 const float *en = p.Er + eoff + static_cast<size_t>(tid) * DV;
 #pragma unroll 16
@@ -517,6 +512,39 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
     }
 }
 
+// Kernels of the fp32 path: one workgroup per chunk.
+template <int DT, int DK, int DV>
+__global__ __launch_bounds__(NT) void k_bwd_fwdwalk(BwdArgs p) {
+    fwdwalk_body<DT, DK, DV, 0>(p, ChunkPos(p.a, p.n_chunks, blockIdx.x));
+}
+template <int DT, int DK, int DV>
+__global__ __launch_bounds__(NT) void k_bwd_revsum(BwdArgs p) {
+    revsum_body<DT, DK, DV>(p, ChunkPos(p.a, p.n_chunks, blockIdx.x));
+}
+template <int DT, int DK, int DV>
+__global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
+    revwalk_body<DT, DK, DV, false>(p, ChunkPos(p.a, p.n_chunks, blockIdx.x));
+}
+
+// Token-serial fallback of the matrix-core path, one workgroup per chunk, for the
+// chunks it flagged.  PHASE 1 (after the epilogue kernel): dO, dz, drms_w partials,
+// then the reverse summary (from the dO just written).  PHASE 2 (after the
+// gradient kernel): dq and q dq, then dk, dv and the complete dlog_g.
+template <int DT, int DK, int DV, int PHASE>
+__global__ __launch_bounds__(NT) void k_bwd_fallback(BwdArgs p) {
+    const ChunkPos cp(p.a, p.n_chunks, blockIdx.x);
+    if (p.flags[cp.cid()] == 0) return;  // the whole workgroup
+    if constexpr (PHASE == 1) {
+        fwdwalk_body<DT, DK, DV, 1>(p, cp);
+        __syncthreads();  // dO of this chunk is in global memory
+        revsum_body<DT, DK, DV>(p, cp);
+    } else {
+        fwdwalk_body<DT, DK, DV, 2>(p, cp);
+        __syncthreads();  // q dq of this chunk is in global memory
+        revwalk_body<DT, DK, DV, true>(p, cp);
+    }
+}
+
 // ---- B4a: Tn[n] <- sum of the totals of the sequence's later chunks (exclusive
 // reverse scan, in place).  Thread = (sequence, channel); the loads of 16 chunks
 // are issued before their sums.
@@ -549,7 +577,7 @@ __global__ __launch_bounds__(NT) void k_bwd_gateoff(BwdArgs p) {
     const GlaArgs &a = p.a;
     __shared__ __attribute__((aligned(16))) float soff[DK];
     const int tid = threadIdx.x;
-    const ChunkPos cp(a, p.n_chunks);
+    const ChunkPos cp(a, p.n_chunks, blockIdx.x);
     if (tid < DK) soff[tid] = p.Tn[cp.cid() * DK + tid];
     __syncthreads();
     const int64_t len = cp.t1 - cp.t0;
@@ -561,22 +589,29 @@ __global__ __launch_bounds__(NT) void k_bwd_gateoff(BwdArgs p) {
     }
 }
 
-// ---- B5: drms_w = sum of the per-chunk partials (fixed order): 1024 threads, each
-// column summed by 1024 / DV threads over strided rows (8 loads in flight each),
-// then their partials in order.
-constexpr int WS_THREADS = 1024;
+// ---- B5: drms_w = sum of the per-chunk partials in a fixed order, two levels:
+// block b sums parts [b R, (b + 1) R) (256 threads: 256 / DV row groups of each
+// column, 8 loads in flight each, then the groups in order) into part2[b]; the
+// block that finishes last (device counter) adds part2[0 ..] in order and resets
+// the counter to zero for the next call.
+constexpr int WS_BLOCKS = 64;
 template <int DV>
-__global__ __launch_bounds__(WS_THREADS) void k_bwd_wsum(BwdArgs p, int64_t n_parts) {
-    __shared__ __attribute__((aligned(16))) float part[WS_THREADS];
+__global__ __launch_bounds__(NT) void k_bwd_wsum(BwdArgs p, int64_t n_parts, float *part2,
+                                                 unsigned *ctr) {
+    __shared__ float part[NT];
+    __shared__ bool last;
     const int tid = threadIdx.x;
     const int j = tid % DV, g = tid / DV;
-    constexpr int GS = WS_THREADS / DV;
+    constexpr int GS = NT / DV;
+    const int64_t R = (n_parts + gridDim.x - 1) / gridDim.x;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * R;
+    const int64_t r1 = (r0 + R < n_parts) ? r0 + R : n_parts;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int64_t r0 = g; r0 < n_parts; r0 += 8 * GS) {
+    for (int64_t rb = r0 + g; rb < r1; rb += 8 * GS) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t r = r0 + static_cast<int64_t>(u) * GS;
-            acc[u] += (r < n_parts) ? p.dWp[r * DV + j] : 0.f;
+            const int64_t r = rb + static_cast<int64_t>(u) * GS;
+            acc[u] += (r < r1) ? p.dWp[r * DV + j] : 0.f;
         }
     }
     part[tid] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
@@ -584,8 +619,27 @@ __global__ __launch_bounds__(WS_THREADS) void k_bwd_wsum(BwdArgs p, int64_t n_pa
     if (tid < DV) {
         float w = 0.f;
         for (int r = 0; r < GS; ++r) w += part[r * DV + tid];
+        part2[static_cast<int64_t>(blockIdx.x) * DV + tid] = w;
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last = atomicAdd(ctr, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    if (tid < DV) {  // in block order, 16 loads in flight
+        float w = 0.f;
+        for (unsigned b0 = 0; b0 < gridDim.x; b0 += 16) {
+            float x[16];
+#pragma unroll
+            for (unsigned u = 0; u < 16; ++u)
+                x[u] = (b0 + u < gridDim.x) ? part2[static_cast<int64_t>(b0 + u) * DV + tid] : 0.f;
+#pragma unroll
+            for (unsigned u = 0; u < 16; ++u) w += x[u];
+        }
         p.drms_w[tid] = w;
     }
+    if (tid == 0) atomicExch(ctr, 0u);
 }
 
 template <int DT, int DK, int DV>
@@ -608,13 +662,11 @@ hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hoo
         e = bdo_launch(p.a, p.dy, p.Sx, p.dO, p.dz, p.dWp, p.Ur, p.Gr, flags, p.n_chunks, st);
         if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
         // chunks out of the matrix path's exponent range: token-serial dO and summaries
-        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 3>), grid, dim3(NT), 0, st, q);
-        if ((e = done()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_bwd_revsum<DT, DK, DV, true>), grid, dim3(NT), 0, st, q);
+        hipLaunchKernelGGL((k_bwd_fallback<DT, DK, DV, 1>), grid, dim3(NT), 0, st, q);
     } else {
-        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 0>), grid, dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV>), grid, dim3(NT), 0, st, p);
         if ((e = done()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_bwd_revsum<DT, DK, DV, false>), grid, dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((k_bwd_revsum<DT, DK, DV>), grid, dim3(NT), 0, st, p);
     }
     if ((e = done()) != hipSuccess) return e;
     e = state_scan(p.Ur, p.Gr, static_cast<int>(p.a.B * p.a.H), p.n_chunks, DK, DV, st, true);
@@ -624,11 +676,9 @@ hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hoo
         e = bgrad_launch(p.a, p.dO, p.Sx, q.Er, p.dq, p.dk, p.dv, p.dlog_g, flags, p.n_chunks, st);
         if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
         // chunks out of the matrix path's exponent range: token-serial gradients
-        hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV, 2>), grid, dim3(NT), 0, st, q);
-        if ((e = done()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_bwd_revwalk<DT, DK, DV, true>), grid, dim3(NT), 0, st, q);
+        hipLaunchKernelGGL((k_bwd_fallback<DT, DK, DV, 2>), grid, dim3(NT), 0, st, q);
     } else {
-        hipLaunchKernelGGL((k_bwd_revwalk<DT, DK, DV, false>), grid, dim3(NT), 0, st, q);
+        hipLaunchKernelGGL((k_bwd_revwalk<DT, DK, DV>), grid, dim3(NT), 0, st, q);
     }
     if ((e = done()) != hipSuccess) return e;
     if (!mfma) {  // the matrix-core path writes complete gate gradients
@@ -639,7 +689,9 @@ hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hoo
         hipLaunchKernelGGL((k_bwd_gateoff<DK>), grid, dim3(NT), 0, st, q);
         if ((e = done()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_bwd_wsum<DV>), dim3(1), dim3(WS_THREADS), 0, st, q, ncb);
+    const int64_t nb = ncb < WS_BLOCKS ? ncb : WS_BLOCKS;
+    hipLaunchKernelGGL((k_bwd_wsum<DV>), dim3(static_cast<unsigned>(nb)), dim3(NT), 0, st, q, ncb,
+                       p.part2, p.ctr);
     return done();
 }
 
@@ -662,12 +714,13 @@ size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks) {
     return 4 * (2 * ncb * (static_cast<size_t>(a.dk) * a.dv + a.dk)  // forward and reverse states
                 + rows * (a.dv + a.dk)                                // do, q dq
                 + ncb * (a.dk + a.dv)                                 // chunk totals, drms_w parts
-                + ncb);                                               // chunk flags
+                + ncb                                                 // chunk flags
+                + static_cast<size_t>(WS_BLOCKS) * a.dv);             // drms_w block sums
 }
 
 hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
-                      float *dlog_g, void *dz, float *drms_w, void *ws, int n_chunks,
-                      hipStream_t st, const BwdLaunchHooks &hooks) {
+                      float *dlog_g, void *dz, float *drms_w, void *ws, unsigned *ctr,
+                      int n_chunks, hipStream_t st, const BwdLaunchHooks &hooks) {
     const size_t ncb = static_cast<size_t>(a.B) * a.H * n_chunks;
     const size_t rows = static_cast<size_t>(a.B) * a.L * a.H;
     const size_t dd = static_cast<size_t>(a.dk) * a.dv;
@@ -676,6 +729,7 @@ hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void
     float *dO = Gr + ncb * a.dk, *qdq = dO + rows * a.dv, *Tn = qdq + rows * a.dk;
     float *dWp = Tn + ncb * a.dk;
     int *flags = reinterpret_cast<int *>(dWp + ncb * a.dv);
+    float *part2 = reinterpret_cast<float *>(flags + ncb);
     // forward incoming states: the forward path's chunk summaries (the matrix-core
     // kernel with one chunk per segment where it applies; log2 gate totals) and scan
     auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
@@ -693,7 +747,7 @@ hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void
     e = state_scan(Uf, Gf, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st, msum);
     if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
     BwdArgs p{a, dy, Uf, nullptr, dO, qdq, Ur, Gr, Tn, dWp, dq, dk, dv, dz, dlog_g, drms_w,
-              nullptr, n_chunks};
+              nullptr, n_chunks, part2, ctr};
     switch (a.dtype) {
     case DT_F32: return run_dt<DT_F32>(p, st, hooks, flags);
     case DT_F16: return run_dt<DT_F16>(p, st, hooks, flags);
