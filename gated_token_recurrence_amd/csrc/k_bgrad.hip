@@ -1,5 +1,6 @@
-// k_bgrad.hip -- matrix-core gradients of q, k and v for one chunk (backward pass,
-// 16-bit I/O, dk = dv = 64, chunk <= 64).
+// k_bgrad.hip -- matrix-core kernels of the backward pass (16-bit I/O, dk = dv = 64,
+// chunk <= 64): the epilogue backward with the reverse chunk summaries (k_bdo)
+// and the gradients of q, k, v and the gates per chunk (k_bgrad).
 //
 // GTR write-up ("端侧实时感知新标杆！通用线性骨干网络GTR开源"): Method §1 gives the
 // recurrence S_t = Diag(g_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t; Method §4 its
@@ -22,12 +23,14 @@
 // (log2 units) in any channel is only flagged here, and the fp32 token-serial
 // kernels produce its gradients.
 //
-// Persistent workgroups of four waves, one chunk at a time; the next chunk's
+// Persistent workgroups of eight waves, one chunk at a time; the next chunk's
 // inputs are requested while the current chunk is computed.  Every product is a
 // 64 x 64 x 64 product on v_mfma_f32_16x16x32_bf16 with each operand split into
 // bf16 hi + lo (three products per pair), wave w computing output rows
-// [16 w, 16 w + 16).  Operands are split once, when written to LDS, into hi and
-// lo planes of 64 x 64 16-bit elements (rows XOR-swizzled by 16-byte piece); a
+// [16 (w % 4), + 16) and columns [32 (w / 4), + 32) (two waves per SIMD, so one
+// wave's waits overlap the other's work).  Operands are split once, when written
+// to LDS, into hi and lo planes of 64 x 64 16-bit elements (rows XOR-swizzled
+// by 16-byte piece); a
 // product reads rows of a plane (16- or 8-byte pieces) or columns of it (the
 // transposing ds_read_b64_tr_b16).  D and P are stored transposed, so that a
 // lane's four results per tile are one 8-byte piece.  E enters pre-scaled by
@@ -45,7 +48,7 @@ using namespace mf;
 constexpr int BC = 64;         // chunk tokens (rows of every matrix) and channels
 constexpr int LS = BC + 4;     // fp32 LDS row stride
 constexpr int MAT = BC * BC;   // elements of one 16-bit plane
-constexpr int64_t kPersistent = 256;  // workgroups: one per CU (LDS allows no second)
+constexpr int64_t kPersistent = 256;  // workgroups: one per CU
 
 struct BgArgs {
     GlaArgs a;
@@ -109,33 +112,6 @@ __device__ __forceinline__ void fetch(const uint16_t *X, int m, int lr, int g, i
     }
 }
 
-// acc[t] += A[16 w + .., :] B[:, 16 t + ..], t = 0..3.  Row modes: A stored
-// [m][k], B stored [n][k]; TRN: A stored [k][m], B stored [k][n].  Lane l:
-// output rows 16 w + 4 (l / 16) + r, column 16 t + l % 16 (acc[t][r]).
-template <int MA, int MB>
-__device__ __forceinline__ void gemm(f32x4 (&acc)[4], const uint16_t *A, const uint16_t *B, int w,
-                                     int lr, int g) {
-    static_assert((MA == NAT) == (MB == NAT), "both operands must use one k slot order");
-#pragma unroll
-    for (int kap = 0; kap < 2; ++kap) {
-        s16x8 ah, al;
-        fetch<MA>(A, 16 * w + lr, lr, g, kap, ah, al);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            s16x8 bh, bl;
-            fetch<MB>(B, 16 * t + lr, lr, g, kap, bh, bl);
-            acc[t] = mma<false>(ah, bh, acc[t]);
-            acc[t] = mma<false>(ah, bl, acc[t]);
-            acc[t] = mma<false>(al, bh, acc[t]);
-        }
-    }
-}
-
-__device__ __forceinline__ void zero4(f32x4 (&acc)[4]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
 // Position of chunk c (of B H N, sequence-major) and its token count
 struct ChunkAt {
     int n, bh, b, h, nt;
@@ -157,329 +133,12 @@ struct ChunkAt {
     }
 };
 
-// Global inputs of one chunk, held in registers from their request until they
-// are used.  Thread tid takes 16-byte pieces i = tid + 256 u: fp32 rows
-// t = i / 16, columns 4 (i % 16); 16-bit rows t = i / 8, columns 8 (i % 8).
-struct TokIn {   // per-token inputs, requested first
-    float4 g[4], dO[4];
-    uint4 q[2], k[2], v[2];
-};
-struct StateIn {  // the chunk's two boundary states, requested once the last are used
-    float4 S[4], E[4];
-};
-
-__device__ __forceinline__ void request_tok(TokIn &in, const BgArgs &p, const int64_t *rows, int tid) {
-    const GlaArgs &a = p.a;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
-        in.g[u] = ld4(a.log_g + rows[t] * DK + c);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
-        in.q[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + rows[t] * DK + c);
-        in.k[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + rows[t] * DK + c);
-        in.v[u] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + rows[t] * BC + c);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
-        in.dO[u] = ld4(p.dO + rows[t] * BC + c);
-    }
-}
-
-__device__ __forceinline__ void request_state(StateIn &in, const BgArgs &p, const ChunkAt &at, int tid) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
-        in.S[u] = ld4(p.Sx + at.cidx * MAT + t * BC + c);  // S[c'][d]: row c' = t, column d = c
-        in.E[u] = ld4(p.Er + at.ridx * MAT + t * BC + c);  // E[c'][d]
-    }
-}
-
-// Cumulative gates of a chunk from its log_g pieces (fp32 layout): A2[t][c] =
-// 2^a (a: in-chunk inclusive cumulative log2-gate, rows past nt add nothing),
-// G2[c] = 2^G; returns G of channel tid % 64 (log2).  A 4-segment scan: wave w
-// takes tokens [16 w, 16 w + 16).  Ends before a barrier the caller places.
-__device__ __forceinline__ float chunk_gates(const float4 (&xg)[4], float (*A2)[LS], float *G2,
-                                             float (*tot4)[BC], int nt, int tid) {
-    const int w = tid >> 6, l = tid & 63;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
-        const bool ok = t < nt;
-        const float4 x = xg[u];
-        st4(&A2[t][c], make_float4(ok ? x.x * kLog2e : 0.f, ok ? x.y * kLog2e : 0.f,
-                                   ok ? x.z * kLog2e : 0.f, ok ? x.w * kLog2e : 0.f));
-    }
-    __syncthreads();
-    float cum[16];
-    {
-        float acc = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            acc += A2[16 * w + s][l];
-            cum[s] = acc;
-        }
-        tot4[w][l] = acc;
-    }
-    __syncthreads();
-    float off = 0.f, tot = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const float x = tot4[u][l];
-        off += (u < w) ? x : 0.f;
-        tot += x;
-    }
-#pragma unroll
-    for (int s = 0; s < 16; ++s) A2[16 * w + s][l] = fexp2(cum[s] + off);
-    if (w == 0) G2[l] = fexp2(tot);
-    return tot;
-}
-
 template <int DT>
 __device__ __forceinline__ uint4 pack8(const float *x) {
     uint32_t u[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) u[e] = f2h<DT>(x[2 * e]) | (f2h<DT>(x[2 * e + 1]) << 16);
     return u4(u);
-}
-
-template <int DT>
-__global__ __launch_bounds__(NT, 1) void k_bgrad(BgArgs p) {
-    const GlaArgs &a = p.a;
-    // hi + lo planes; SE holds S, then E'
-    __shared__ __attribute__((aligned(16))) uint16_t sDO[2 * MAT], sQT[2 * MAT], sKH[2 * MAT], sV[2 * MAT];
-    __shared__ __attribute__((aligned(16))) uint16_t sSE[2 * MAT], sDT[2 * MAT], sPT[2 * MAT];
-    __shared__ __attribute__((aligned(16))) float sA2[BC][LS];  // 2^a, later q dq - k dk
-    __shared__ __attribute__((aligned(16))) float sX[BC][LS];   // fp32 staging: T, dq, dk, dv
-    __shared__ float sG[BC], sOff[BC], sTot[4][BC];
-    __shared__ int64_t srow[2][BC];
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
-    const int64_t total = static_cast<int64_t>(a.B) * a.H * p.n_chunks;
-
-    int64_t ch = blockIdx.x;
-    int buf = 0;
-    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, ch).row(a, tid);
-    __syncthreads();
-    TokIn in;
-    StateIn st_in;
-    request_tok(in, p, srow[0], tid);
-    request_state(st_in, p, ChunkAt(a, p.n_chunks, ch), tid);
-
-    for (; ch < total; ch += gridDim.x, buf ^= 1) {
-        const ChunkAt at(a, p.n_chunks, ch);
-        const int64_t *rows = srow[buf];
-        const int nt = at.nt;
-        const int64_t cn = ch + gridDim.x;  // next chunk of this workgroup
-
-        const float tot = chunk_gates(in.g, sA2, sG, sTot, nt, tid);
-        const bool slow = __syncthreads_or(-tot > kSpanMax);  // uniform over the workgroup
-        if (tid == 0) p.flags[at.cidx] = slow ? 1 : 0;
-
-        // ---- operands (rows past the chunk's end are zero); exact q and k kept
-        uint4 qk[2][2];
-        if (!slow) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
-                const bool ok = t < nt;
-                float q8[8], k8[8], v8[8];
-                unpack8<DT>(in.q[u], q8);
-                unpack8<DT>(in.k[u], k8);
-                unpack8<DT>(in.v[u], v8);
-                qk[u][0] = in.q[u];
-                qk[u][1] = in.k[u];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const float e = sA2[t][c + s];
-                    q8[s] = ok ? q8[s] * e : 0.f;
-                    k8[s] = ok ? k8[s] * frcp(e) : 0.f;
-                    v8[s] = ok ? v8[s] : 0.f;
-                }
-                put<8>(sQT, t, c, q8);
-                put<8>(sKH, t, c, k8);
-                put<8>(sV, t, c, v8);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
-                const float4 d = in.dO[u], sv = st_in.S[u];
-                const bool ok = t < nt;
-                const float dd[4] = {ok ? d.x : 0.f, ok ? d.y : 0.f, ok ? d.z : 0.f, ok ? d.w : 0.f};
-                const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
-                put<4>(sDO, t, c, dd);
-                put<4>(sSE, t, c, ss);
-            }
-        }
-        // ---- the next chunk's rows, then its per-token inputs (those registers are free)
-        if (cn < total && tid < BC) srow[buf ^ 1][tid] = ChunkAt(a, p.n_chunks, cn).row(a, tid);
-        __syncthreads();
-        if (cn < total) request_tok(in, p, srow[buf ^ 1], tid);
-        if (slow) {  // the whole workgroup; its gradients come from the token-serial kernels
-            if (cn < total) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
-            continue;
-        }
-
-        f32x4 acc[4];
-        // ---- D = (dO V^T) . M and P = (Q~ K^^T) . M, rows i of wave w, stored transposed
-        zero4(acc);
-        gemm<NAT, NAT>(acc, sDO, sV, w, lr, g);      // B(k=d, n=j) = V[j][d]
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float x[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * w + 4 * g + r) ? acc[t][r] : 0.f;
-            put<4>(sDT, 16 * t + lr, 16 * w + 4 * g, x);
-        }
-        zero4(acc);
-        gemm<NAT, NAT>(acc, sQT, sKH, w, lr, g);     // B(k=c, n=j) = K^[j][c]
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float x[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * w + 4 * g + r) ? acc[t][r] : 0.f;
-            put<4>(sPT, 16 * t + lr, 16 * w + 4 * g, x);
-        }
-        // ---- T = K^^T V (rows c of wave w), staged
-        zero4(acc);
-        gemm<TRN, TRN>(acc, sKH, sV, w, lr, g);      // A(m=c, k=j) = K^[j][c], B(k=j, n=d) = V[j][d]
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sX[16 * w + 4 * g + r][16 * t + lr] = acc[t][r];
-        __syncthreads();
-
-        // ---- offset of the gate gradient: sum_d E[c][d] S_out[c][d] with
-        // S_out = 2^G . (S + T); the 16 lanes of a channel row reduce together
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
-            const float4 sv = st_in.S[u], ev = st_in.E[u], tv = ld4(&sX[t][c]);
-            float x = ev.x * (sv.x + tv.x) + ev.y * (sv.y + tv.y) + ev.z * (sv.z + tv.z) +
-                      ev.w * (sv.w + tv.w);
-            x += __shfl_xor(x, 1);
-            x += __shfl_xor(x, 2);
-            x += __shfl_xor(x, 4);
-            x += __shfl_xor(x, 8);
-            if ((tid & 15) == 0) sOff[t] = sG[t] * x;
-        }
-
-        // ---- dQ = 2^a . (dO S^T + D K^), rows i of wave w
-        zero4(acc);
-        gemm<NAT, NAT>(acc, sDO, sSE, w, lr, g);     // B(k=d, n=c) = S[c][d]
-        gemm<TRN, TRN>(acc, sDT, sKH, w, lr, g);     // A(m=i, k=j) = D[i][j], B(k=j, n=c) = K^[j][c]
-        __syncthreads();  // S and T are read
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * g + r, c = 16 * t + lr;
-                sX[i][c] = sA2[i][c] * acc[t][r];
-            }
-        // E' = 2^G . E (rows c scaled), then the next chunk's states
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = tid + NT * u, t = i >> 4, c = (i & 15) * 4;
-            const float4 ev = st_in.E[u];
-            const float gt = sG[t];
-            const float ee[4] = {gt * ev.x, gt * ev.y, gt * ev.z, gt * ev.w};
-            put<4>(sSE, t, c, ee);
-        }
-        if (cn < total) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
-        __syncthreads();
-        // dq out; q . dq of this thread's pieces
-        float qdq[2][8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
-            float x[8], q8[8];
-            const float4 x0 = ld4(&sX[t][c]), x1 = ld4(&sX[t][c + 4]);
-            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-            unpack8<DT>(qk[u][0], q8);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) qdq[u][s] = q8[s] * x[s];
-            if (t < nt)
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dq) + rows[t] * DK + c) = pack8<DT>(x);
-        }
-
-        // ---- dK = 2^-a . (D^T Q~ + V E'^T), rows j of wave w
-        zero4(acc);
-        gemm<PERM, TRN>(acc, sDT, sQT, w, lr, g);    // A(m=j, k=i) = D[i][j], B(k=i, n=c) = Q~[i][c]
-        gemm<NAT, NAT>(acc, sV, sSE, w, lr, g);      // B(k=d, n=c) = E'[c][d]
-        __syncthreads();  // dq is read
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * w + 4 * g + r, c = 16 * t + lr;
-                sX[j][c] = acc[t][r] * frcp(sA2[j][c]);
-            }
-        __syncthreads();
-        // dk out; the gate gradient's terms q dq - k dk replace 2^a
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
-            float x[8], k8[8], y[8];
-            const float4 x0 = ld4(&sX[t][c]), x1 = ld4(&sX[t][c + 4]);
-            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-            unpack8<DT>(qk[u][1], k8);
-            const bool ok = t < nt;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) y[s] = ok ? qdq[u][s] - k8[s] * x[s] : 0.f;
-            st4(&sA2[t][c], make_float4(y[0], y[1], y[2], y[3]));
-            st4(&sA2[t][c + 4], make_float4(y[4], y[5], y[6], y[7]));
-            if (ok)
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dk) + rows[t] * DK + c) = pack8<DT>(x);
-        }
-
-        // ---- dV = P^T dO + K^ E', rows j of wave w
-        zero4(acc);
-        gemm<PERM, TRN>(acc, sPT, sDO, w, lr, g);    // A(m=j, k=i) = P[i][j], B(k=i, n=d) = dO[i][d]
-        gemm<PERM, TRN>(acc, sKH, sSE, w, lr, g);    // A(m=j, k=c) = K^[j][c], B(k=c, n=d) = E'[c][d]
-        __syncthreads();  // dk and the gate terms are through LDS
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sX[16 * w + 4 * g + r][16 * t + lr] = acc[t][r];
-        // dlog_g, part 1: wave w takes tokens [16 w, 16 w + 16) of channel l
-        float x16[16];
-        {
-            float s = 0.f;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                x16[u] = sA2[16 * w + u][l];
-                s += x16[u];
-            }
-            sTot[w][l] = s;
-        }
-        __syncthreads();
-        // dv out
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int i = tid + NT * u, t = i >> 3, c = (i & 7) * 8;
-            float x[8];
-            const float4 x0 = ld4(&sX[t][c]), x1 = ld4(&sX[t][c + 4]);
-            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-            if (t < nt)
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dv) + rows[t] * BC + c) = pack8<DT>(x);
-        }
-        // dlog_g, part 2: reverse cumulative sum from the offset and the later segments
-        float s = sOff[l];
-#pragma unroll
-        for (int u = 3; u > 0; --u) s += (u > w) ? sTot[u][l] : 0.f;
-#pragma unroll
-        for (int u = 15; u >= 0; --u) {
-            const int t = 16 * w + u;
-            s += x16[u];
-            if (t < nt) p.dlog_g[rows[t] * DK + l] = s;
-        }
-        __syncthreads();  // LDS is rewritten by the next chunk
-    }
 }
 
 // ---- The epilogue backward and the reverse chunk summary (they precede the
@@ -510,7 +169,9 @@ struct BdArgs {
 constexpr int NW = 8;
 constexpr int NTB = 64 * NW;
 
-// acc[tt] += A[16 rs + .., :] B[:, 16 (2 ch + tt) + ..], tt = 0, 1 (modes as gemm)
+// acc[tt] += A[16 rs + .., :] B[:, 16 (2 ch + tt) + ..], tt = 0, 1.  Row modes: A
+// stored [m][k], B stored [n][k]; TRN: A stored [k][m], B stored [k][n].  Lane l:
+// output rows 16 rs + 4 (l / 16) + r, column 16 (2 ch + tt) + l % 16 (acc[tt][r]).
 template <int MA, int MB>
 __device__ __forceinline__ void gemm2(f32x4 (&acc)[2], const uint16_t *A, const uint16_t *B, int rs,
                                       int ch, int lr, int g) {
@@ -535,8 +196,10 @@ __device__ __forceinline__ void zero2(f32x4 (&acc)[2]) {
     acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// chunk_gates for eight waves: fp32 pieces i = tid + 512 u (u < 2); wave w scans
-// tokens [8 w, 8 w + 8)
+// Cumulative gates of a chunk from its log_g pieces (fp32 pieces i = tid + 512 u,
+// u < 2): A2[t][c] = 2^a (a: in-chunk inclusive cumulative log2-gate, rows past
+// nt add nothing), G2[c] = 2^G; returns G of channel tid % 64 (log2).  Wave w
+// scans tokens [8 w, 8 w + 8).  Ends before a barrier the caller places.
 __device__ __forceinline__ float chunk_gates8(const float4 (&xg)[2], float (*A2)[LS], float *G2,
                                               float (*tot8)[BC], int nt, int tid) {
     const int w = tid >> 6, l = tid & 63;
@@ -778,6 +441,275 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
     }
 }
 
+// ---- The gradients (see the top of the file), eight waves.
+// Per-token inputs: fp32 pieces i = tid + 512 u (u < 2), rows i / 16, columns
+// 4 (i % 16); 16-bit pieces: row tid / 8, columns 8 (tid % 8).
+struct TokIn {
+    float4 g[2], dO[2];
+    uint4 q, k, v;
+};
+struct StateIn {  // the chunk's two boundary states, requested once the last are used
+    float4 S[2], E[2];
+};
+
+__device__ __forceinline__ void request_tok(TokIn &in, const BgArgs &p, const int64_t *rows, int tid) {
+    const GlaArgs &a = p.a;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
+        in.g[u] = ld4(a.log_g + rows[t] * DK + c);
+    }
+    {
+        const int t = tid >> 3, c = (tid & 7) * 8;
+        in.q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + rows[t] * DK + c);
+        in.k = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + rows[t] * DK + c);
+        in.v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + rows[t] * BC + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
+        in.dO[u] = ld4(p.dO + rows[t] * BC + c);
+    }
+}
+
+__device__ __forceinline__ void request_state(StateIn &in, const BgArgs &p, const ChunkAt &at, int tid) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
+        in.S[u] = ld4(p.Sx + at.cidx * MAT + t * BC + c);  // S[c'][d]: row c' = t, column d = c
+        in.E[u] = ld4(p.Er + at.ridx * MAT + t * BC + c);  // E[c'][d]
+    }
+}
+
+__device__ __forceinline__ void ld8(const float *src, float (&x)[8]) {
+    const float4 a = ld4(src), b = ld4(src + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <int DT>
+__global__ __launch_bounds__(NTB, 1) void k_bgrad(BgArgs p) {
+    const GlaArgs &a = p.a;
+    // hi + lo planes; SE holds S, then E'
+    __shared__ __attribute__((aligned(16))) uint16_t sDO[2 * MAT], sQT[2 * MAT], sKH[2 * MAT], sV[2 * MAT];
+    __shared__ __attribute__((aligned(16))) uint16_t sSE[2 * MAT], sDT[2 * MAT], sPT[2 * MAT];
+    __shared__ __attribute__((aligned(16))) float sA2[BC][LS];  // 2^a, later q dq - k dk
+    __shared__ __attribute__((aligned(16))) float sX[BC][LS];   // fp32 staging: T, dq, dk, dv
+    __shared__ float sG[BC], sOff[BC], sTot[NW][BC];
+    __shared__ int64_t srow[2][BC];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
+    const int rs = w & 3, ch2 = w >> 2;           // row stripe, column half
+    const int et = tid >> 3, ec = (tid & 7) * 8;  // load-layout row and columns (16-bit pieces)
+    const int64_t total = static_cast<int64_t>(a.B) * a.H * p.n_chunks;
+
+    int64_t chk = blockIdx.x;
+    int buf = 0;
+    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, chk).row(a, tid);
+    __syncthreads();
+    TokIn in;
+    StateIn st_in;
+    request_tok(in, p, srow[0], tid);
+    request_state(st_in, p, ChunkAt(a, p.n_chunks, chk), tid);
+
+    for (; chk < total; chk += gridDim.x, buf ^= 1) {
+        const ChunkAt at(a, p.n_chunks, chk);
+        const int64_t *rows = srow[buf];
+        const int nt = at.nt;
+        const int64_t cn = chk + gridDim.x;  // next chunk of this workgroup
+
+        const float tot = chunk_gates8(in.g, sA2, sG, sTot, nt, tid);
+        const bool slow = __syncthreads_or(-tot > kSpanMax);  // uniform over the workgroup
+        if (tid == 0) p.flags[at.cidx] = slow ? 1 : 0;
+
+        // ---- operands (rows past the chunk's end are zero); exact q and k kept
+        uint4 qkeep, kkeep;
+        if (!slow) {
+            const bool ok = et < nt;
+            float q8[8], k8[8], v8[8];
+            unpack8<DT>(in.q, q8);
+            unpack8<DT>(in.k, k8);
+            unpack8<DT>(in.v, v8);
+            qkeep = in.q;
+            kkeep = in.k;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const float e = sA2[et][ec + s];
+                q8[s] = ok ? q8[s] * e : 0.f;
+                k8[s] = ok ? k8[s] * frcp(e) : 0.f;
+                v8[s] = ok ? v8[s] : 0.f;
+            }
+            put<8>(sQT, et, ec, q8);
+            put<8>(sKH, et, ec, k8);
+            put<8>(sV, et, ec, v8);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
+                const float4 d = in.dO[u], sv = st_in.S[u];
+                const bool okr = t < nt;
+                const float dd[4] = {okr ? d.x : 0.f, okr ? d.y : 0.f, okr ? d.z : 0.f, okr ? d.w : 0.f};
+                const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
+                put<4>(sDO, t, c, dd);
+                put<4>(sSE, t, c, ss);
+            }
+        }
+        // ---- the next chunk's rows, then its per-token inputs (those registers are free)
+        if (cn < total && tid < BC) srow[buf ^ 1][tid] = ChunkAt(a, p.n_chunks, cn).row(a, tid);
+        __syncthreads();
+        if (cn < total) request_tok(in, p, srow[buf ^ 1], tid);
+        if (slow) {  // the whole workgroup; its gradients come from the token-serial kernels
+            if (cn < total) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
+            continue;
+        }
+
+        f32x4 acc[2];
+        // ---- D = (dO V^T) . M and P = (Q~ K^^T) . M, stored transposed
+        zero2(acc);
+        gemm2<NAT, NAT>(acc, sDO, sV, rs, ch2, lr, g);    // B(k=d, n=j) = V[j][d]
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * ch2 + tt;
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * rs + 4 * g + r) ? acc[tt][r] : 0.f;
+            put<4>(sDT, 16 * t + lr, 16 * rs + 4 * g, x);
+        }
+        zero2(acc);
+        gemm2<NAT, NAT>(acc, sQT, sKH, rs, ch2, lr, g);   // B(k=c, n=j) = K^[j][c]
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * ch2 + tt;
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * rs + 4 * g + r) ? acc[tt][r] : 0.f;
+            put<4>(sPT, 16 * t + lr, 16 * rs + 4 * g, x);
+        }
+        // ---- T = K^^T V (rows c), staged
+        zero2(acc);
+        gemm2<TRN, TRN>(acc, sKH, sV, rs, ch2, lr, g);    // A(m=c, k=j) = K^[j][c], B(k=j, n=d) = V[j][d]
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[16 * rs + 4 * g + r][16 * (2 * ch2 + tt) + lr] = acc[tt][r];
+        __syncthreads();
+
+        // ---- offset of the gate gradient: sum_d E[c][d] S_out[c][d] with
+        // S_out = 2^G . (S + T); the 16 lanes of a channel row reduce together
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
+            const float4 sv = st_in.S[u], ev = st_in.E[u], tv = ld4(&sX[t][c]);
+            float x = ev.x * (sv.x + tv.x) + ev.y * (sv.y + tv.y) + ev.z * (sv.z + tv.z) +
+                      ev.w * (sv.w + tv.w);
+            x += __shfl_xor(x, 1);
+            x += __shfl_xor(x, 2);
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+            if ((tid & 15) == 0) sOff[t] = sG[t] * x;
+        }
+
+        // ---- dQ = 2^a . (dO S^T + D K^)
+        zero2(acc);
+        gemm2<NAT, NAT>(acc, sDO, sSE, rs, ch2, lr, g);   // B(k=d, n=c) = S[c][d]
+        gemm2<TRN, TRN>(acc, sDT, sKH, rs, ch2, lr, g);   // A(m=i, k=j) = D[i][j], B(k=j, n=c) = K^[j][c]
+        __syncthreads();  // S and T are read
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * rs + 4 * g + r, c = 16 * (2 * ch2 + tt) + lr;
+                sX[i][c] = sA2[i][c] * acc[tt][r];
+            }
+        // E' = 2^G . E (rows c scaled), then the next chunk's states
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
+            const float4 ev = st_in.E[u];
+            const float gt = sG[t];
+            const float ee[4] = {gt * ev.x, gt * ev.y, gt * ev.z, gt * ev.w};
+            put<4>(sSE, t, c, ee);
+        }
+        if (cn < total) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
+        __syncthreads();
+        // dq out; q . dq of this thread's piece
+        float qdq[8];
+        {
+            float x[8], q8[8];
+            ld8(&sX[et][ec], x);
+            unpack8<DT>(qkeep, q8);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) qdq[s] = q8[s] * x[s];
+            if (et < nt)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dq) + rows[et] * DK + ec) = pack8<DT>(x);
+        }
+
+        // ---- dK = 2^-a . (D^T Q~ + V E'^T)
+        zero2(acc);
+        gemm2<PERM, TRN>(acc, sDT, sQT, rs, ch2, lr, g);  // A(m=j, k=i) = D[i][j], B(k=i, n=c) = Q~[i][c]
+        gemm2<NAT, NAT>(acc, sV, sSE, rs, ch2, lr, g);    // B(k=d, n=c) = E'[c][d]
+        __syncthreads();  // dq is read
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * rs + 4 * g + r, c = 16 * (2 * ch2 + tt) + lr;
+                sX[j][c] = acc[tt][r] * frcp(sA2[j][c]);
+            }
+        __syncthreads();
+        // dk out; the gate gradient's terms q dq - k dk replace 2^a
+        {
+            float x[8], k8[8], y[8];
+            ld8(&sX[et][ec], x);
+            unpack8<DT>(kkeep, k8);
+            const bool ok = et < nt;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) y[s] = ok ? qdq[s] - k8[s] * x[s] : 0.f;
+            st4(&sA2[et][ec], make_float4(y[0], y[1], y[2], y[3]));
+            st4(&sA2[et][ec + 4], make_float4(y[4], y[5], y[6], y[7]));
+            if (ok)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dk) + rows[et] * DK + ec) = pack8<DT>(x);
+        }
+
+        // ---- dV = P^T dO + K^ E'
+        zero2(acc);
+        gemm2<PERM, TRN>(acc, sPT, sDO, rs, ch2, lr, g);  // A(m=j, k=i) = P[i][j], B(k=i, n=d) = dO[i][d]
+        gemm2<PERM, TRN>(acc, sKH, sSE, rs, ch2, lr, g);  // A(m=j, k=c) = K^[j][c], B(k=c, n=d) = E'[c][d]
+        __syncthreads();  // dk and the gate terms are through LDS
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[16 * rs + 4 * g + r][16 * (2 * ch2 + tt) + lr] = acc[tt][r];
+        // dlog_g, part 1: wave w takes tokens [8 w, 8 w + 8) of channel l
+        float x8[8];
+        {
+            float s = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                x8[u] = sA2[8 * w + u][l];
+                s += x8[u];
+            }
+            sTot[w][l] = s;
+        }
+        __syncthreads();
+        // dv out
+        {
+            float x[8];
+            ld8(&sX[et][ec], x);
+            if (et < nt)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.dv) + rows[et] * BC + ec) = pack8<DT>(x);
+        }
+        // dlog_g, part 2: reverse cumulative sum from the offset and the later segments
+        float s = sOff[l];
+#pragma unroll
+        for (int u = NW - 1; u > 0; --u) s += (u > w) ? sTot[u][l] : 0.f;
+#pragma unroll
+        for (int u = 7; u >= 0; --u) {
+            const int t = 8 * w + u;
+            s += x8[u];
+            if (t < nt) p.dlog_g[rows[t] * DK + l] = s;
+        }
+        __syncthreads();  // LDS is rewritten by the next chunk
+    }
+}
+
 }  // namespace
 
 bool bgrad_supported(const GlaArgs &a) {
@@ -807,9 +739,9 @@ hipError_t bgrad_launch(const GlaArgs &a, const float *dO, const float *Sx, cons
     const int64_t total = static_cast<int64_t>(a.B) * a.H * n_chunks;
     const dim3 grid(static_cast<unsigned>(total < kPersistent ? total : kPersistent));
     if (a.dtype == DT_F16)
-        hipLaunchKernelGGL((k_bgrad<DT_F16>), grid, dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((k_bgrad<DT_F16>), grid, dim3(NTB), 0, s, p);
     else if (a.dtype == DT_BF16)
-        hipLaunchKernelGGL((k_bgrad<DT_BF16>), grid, dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((k_bgrad<DT_BF16>), grid, dim3(NTB), 0, s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
