@@ -197,9 +197,12 @@ size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks);
 // and left to the token-serial kernels.
 bool bgrad_supported(const GlaArgs &a);
 // Matrix-core epilogue backward and reverse chunk summaries (same support):
-// dO, dz, drms_w partials, Ur and Gr (log2) per chunk; flags as bgrad_launch.
-hipError_t bdo_launch(const GlaArgs &a, const void *dy, const float *Sx, float *dO, void *dz,
-                      float *dWp, float *Ur, float *Gr, int *flags, int n_chunks, hipStream_t s);
+// workgroup b walks chunks [b Q, b Q + Q) of pl in order from the incoming state
+// of its segment (Sseg[seg_id(b Q)]), writing each chunk's incoming state to Sx,
+// dO, dz, drms_w partials, Ur and Gr (log2); flags as bgrad_launch.
+hipError_t bdo_launch(const GlaArgs &a, const MfmaPlan &pl, const void *dy, const float *Sseg,
+                      float *Sx, float *dO, void *dz, float *dWp, float *Ur, float *Gr, int *flags,
+                      int n_chunks, hipStream_t s);
 hipError_t bgrad_launch(const GlaArgs &a, const float *dO, const float *Sx, const float *Er,
                         void *dq, void *dk, void *dv, float *dlog_g, int *flags, int n_chunks,
                         hipStream_t s);

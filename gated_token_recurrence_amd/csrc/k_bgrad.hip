@@ -154,13 +154,15 @@ __device__ __forceinline__ uint4 pack8(const float *x) {
 struct BdArgs {
     GlaArgs a;
     const void *dy;     // gradient of out, I/O type
-    const float *Sx;    // forward incoming state per chunk [bh N + n][64][64]
+    const float *Sseg;  // forward incoming state of each segment of pl [seg][64][64]
+    float *Sx;          // out: forward incoming state per chunk [bh N + n][64][64]
     float *dO;          // [rows][64]
     void *dz;
     float *dWp;         // [bh N + n][64] drms_w partials
     float *Ur, *Gr;     // reverse summaries and chunk gates (log2), reversed chunk order
     int *flags;         // per chunk: 1 = left to the token-serial kernels
     int n_chunks;
+    MfmaPlan pl;        // workgroup b takes chunks [b Q, b Q + Q) in order
 };
 
 // Eight waves (two per SIMD, so that one wave's LDS, matrix-unit and memory
@@ -198,10 +200,13 @@ __device__ __forceinline__ void zero2(f32x4 (&acc)[2]) {
 
 // Cumulative gates of a chunk from its log_g pieces (fp32 pieces i = tid + 512 u,
 // u < 2): A2[t][c] = 2^a (a: in-chunk inclusive cumulative log2-gate, rows past
-// nt add nothing), G2[c] = 2^G; returns G of channel tid % 64 (log2).  Wave w
+// nt add nothing; LOG: a itself, and Gl[c] = G), G2[c] = 2^G; returns G of
+// channel tid % 64 (log2).  Wave w
 // scans tokens [8 w, 8 w + 8).  Ends before a barrier the caller places.
+template <bool LOG = false>
 __device__ __forceinline__ float chunk_gates8(const float4 (&xg)[2], float (*A2)[LS], float *G2,
-                                              float (*tot8)[BC], int nt, int tid) {
+                                              float (*tot8)[BC], int nt, int tid,
+                                              float *Gl = nullptr) {
     const int w = tid >> 6, l = tid & 63;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -231,53 +236,51 @@ __device__ __forceinline__ float chunk_gates8(const float4 (&xg)[2], float (*A2)
         tot += x;
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) A2[8 * w + s][l] = fexp2(cum[s] + off);
-    if (w == 0) G2[l] = fexp2(tot);
+    for (int s = 0; s < 8; ++s) A2[8 * w + s][l] = LOG ? cum[s] + off : fexp2(cum[s] + off);
+    if (w == 0) {
+        G2[l] = fexp2(tot);
+        if (LOG) Gl[l] = tot;
+    }
     return tot;
 }
 
-// Per-chunk inputs of the epilogue kernel: fp32 pieces i = tid + 512 u (u < 2),
+// Per-token inputs of the epilogue kernel: fp32 pieces i = tid + 512 u (u < 2),
 // rows i / 16, columns 4 (i % 16); 16-bit pieces: row tid / 8, columns 8 (tid % 8).
 struct DoIn {
-    float4 g[2], S[2];
+    float4 g[2];
     uint4 q, k, v, z, dy;
 };
 
-__device__ __forceinline__ void request_do(DoIn &in, const BdArgs &p, const ChunkAt &at,
-                                           const int64_t *rows, int tid) {
+__device__ __forceinline__ void request_do(DoIn &in, const BdArgs &p, const int64_t *rows, int tid) {
     const GlaArgs &a = p.a;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
         in.g[u] = ld4(a.log_g + rows[t] * DK + c);
     }
-    {
-        const int t = tid >> 3, c = (tid & 7) * 8;
-        const int64_t rk = rows[t] * DK + c, rv = rows[t] * BC + c;
-        in.q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + rk);
-        in.k = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + rk);
-        in.v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + rv);
-        in.z = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.z) + rv);
-        in.dy = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.dy) + rv);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
-        in.S[u] = ld4(p.Sx + at.cidx * MAT + t * BC + c);
-    }
+    const int t = tid >> 3, c = (tid & 7) * 8;
+    const int64_t rk = rows[t] * DK + c, rv = rows[t] * BC + c;
+    in.q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + rk);
+    in.k = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + rk);
+    in.v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + rv);
+    in.z = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.z) + rv);
+    in.dy = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.dy) + rv);
 }
 
 template <int DT>
 __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
     const GlaArgs &a = p.a;
-    // hi + lo planes: Q~; K^, then P^T; V; S, then dO
-    __shared__ __attribute__((aligned(16))) uint16_t sQT[2 * MAT], sKP[2 * MAT], sV[2 * MAT], sSD[2 * MAT];
-    __shared__ __attribute__((aligned(16))) float sX[BC][LS];  // 2^a, then O, then Ur (staging)
-    __shared__ float sG[BC], sTot[NW][BC], sW[NW][BC];
+    // hi + lo planes: Q~; K^, then P^T; K~; V; S^T, then dO
+    __shared__ __attribute__((aligned(16))) uint16_t sQT[2 * MAT], sKP[2 * MAT], sKT[2 * MAT];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2 * MAT], sSD[2 * MAT];
+    __shared__ __attribute__((aligned(16))) float sX[BC][LS];  // a (log2), then O, then Ur (staging)
+    __shared__ float sG[BC], sGl[BC], sTot[NW][BC], sW[NW][BC];
     __shared__ int64_t srow[2][BC];
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
     const int rs = w & 3, ch2 = w >> 2;  // row stripe, column half
     const int64_t total = static_cast<int64_t>(a.B) * a.H * p.n_chunks;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * p.pl.Q;
+    const int64_t c1 = (c0 + p.pl.Q < total) ? c0 + p.pl.Q : total;
     const int et = tid >> 3, ec = (tid & 7) * 8;  // load-layout row and columns of this thread
     float rw[8];                                  // rms_w of those columns
     {
@@ -285,28 +288,56 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
         rw[0] = w0.x; rw[1] = w0.y; rw[2] = w0.z; rw[3] = w0.w;
         rw[4] = w1.x; rw[5] = w1.y; rw[6] = w1.z; rw[7] = w1.w;
     }
+    // carried forward state, MFMA layout: sreg[tt][r] = S[16 rs + 4 g + r][16 (2 ch2 + tt) + lr];
+    // a range's first chunk starts from its segment's incoming state (none at a
+    // sequence's first chunk)
+    float sreg[2][4];
+    {
+        const bool first = ChunkAt(a, p.n_chunks, c0).n == 0;
+        const float *src = p.Sseg + seg_id(c0, p.pl) * MAT;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sreg[tt][r] = first ? 0.f : src[(16 * rs + 4 * g + r) * BC + 16 * (2 * ch2 + tt) + lr];
+    }
 
-    int64_t chk = blockIdx.x;
     int buf = 0;
-    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, chk).row(a, tid);
+    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, c0).row(a, tid);
     __syncthreads();
     DoIn in;
-    request_do(in, p, ChunkAt(a, p.n_chunks, chk), srow[0], tid);
+    request_do(in, p, srow[0], tid);
 
-    for (; chk < total; chk += gridDim.x, buf ^= 1) {
+    for (int64_t chk = c0; chk < c1; ++chk, buf ^= 1) {
         const ChunkAt at(a, p.n_chunks, chk);
         const int64_t *rows = srow[buf];
         const int nt = at.nt;
-        const int64_t cn = chk + gridDim.x;
+        const int64_t cn = chk + 1;
+        if (at.n == 0) {  // a new sequence
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sreg[tt][r] = 0.f;
+        }
 
-        const float tot = chunk_gates8(in.g, sX, sG, sTot, nt, tid);
+        const float tot = chunk_gates8<true>(in.g, sX, sG, sTot, nt, tid, sGl);
         const bool slow = __syncthreads_or(-tot > kSpanMax);
         if (tid == 0) p.flags[at.cidx] = slow ? 1 : 0;
 
+        // ---- the chunk's incoming state: out to Sx, and as S^T planes
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int d = 16 * (2 * ch2 + tt) + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p.Sx[at.cidx * MAT + (16 * rs + 4 * g + r) * BC + d] = sreg[tt][r];
+            put<4>(sSD, d, 16 * rs + 4 * g, sreg[tt]);
+        }
+        // ---- operands (rows past the chunk's end are zero): K~ = k 2^(G - a) and V
+        // always (the state carry); Q~ = q 2^a and K^ = k 2^-a for the matrix path
         uint4 zk, yk;  // z and dy, kept for the epilogue
-        if (!slow) {
+        {
             const bool ok = et < nt;
-            float q8[8], k8[8], v8[8];
+            float q8[8], k8[8], v8[8], kt[8];
             unpack8<DT>(in.q, q8);
             unpack8<DT>(in.k, k8);
             unpack8<DT>(in.v, v8);
@@ -314,28 +345,36 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
             yk = in.dy;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const float e = sX[et][ec + s];
-                q8[s] = ok ? q8[s] * e : 0.f;
-                k8[s] = ok ? k8[s] * frcp(e) : 0.f;
+                const float av = sX[et][ec + s];
+                kt[s] = ok ? k8[s] * fexp2(sGl[ec + s] - av) : 0.f;
+                q8[s] = ok ? q8[s] * fexp2(av) : 0.f;
+                k8[s] = ok ? k8[s] * fexp2(-av) : 0.f;
                 v8[s] = ok ? v8[s] : 0.f;
             }
-            put<8>(sQT, et, ec, q8);
-            put<8>(sKP, et, ec, k8);
+            put<8>(sKT, et, ec, kt);
             put<8>(sV, et, ec, v8);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
-                const float4 sv = in.S[u];
-                const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
-                put<4>(sSD, t, c, ss);
+            if (!slow) {
+                put<8>(sQT, et, ec, q8);
+                put<8>(sKP, et, ec, k8);
             }
         }
-        if (cn < total && tid < BC) srow[buf ^ 1][tid] = ChunkAt(a, p.n_chunks, cn).row(a, tid);
+        if (cn < c1 && tid < BC) srow[buf ^ 1][tid] = ChunkAt(a, p.n_chunks, cn).row(a, tid);
         __syncthreads();
-        if (cn < total) request_do(in, p, ChunkAt(a, p.n_chunks, cn), srow[buf ^ 1], tid);
-        if (slow) continue;  // the whole workgroup; the token-serial kernels take the chunk
+        if (cn < c1) request_do(in, p, srow[buf ^ 1], tid);
 
         f32x4 acc[2];
+        // ---- the state after the chunk: S <- 2^G . S + K~^T V
+        zero2(acc);
+        gemm2<TRN, TRN>(acc, sKT, sV, rs, ch2, lr, g);    // A(m=c, k=j) = K~[j][c], B(k=j, n=d) = V[j][d]
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sreg[tt][r] = sG[16 * rs + 4 * g + r] * sreg[tt][r] + acc[tt][r];
+        if (slow) {  // the whole workgroup; the token-serial kernels take the chunk
+            __syncthreads();
+            continue;
+        }
+
         // ---- P = (Q~ K^^T) . M; P^T replaces K^
         zero2(acc);
         gemm2<NAT, NAT>(acc, sQT, sKP, rs, ch2, lr, g);   // B(k=c, n=j) = K^[j][c]
@@ -351,7 +390,7 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
         __syncthreads();
         // ---- O = Q~ S + P V, staged
         zero2(acc);
-        gemm2<PERM, TRN>(acc, sQT, sSD, rs, ch2, lr, g);  // A = Q~[i][c], B(k=c, n=d) = S[c][d]
+        gemm2<NAT, NAT>(acc, sQT, sSD, rs, ch2, lr, g);   // B(k=c, n=d) = S[c][d] = S^T[d][c]
         gemm2<TRN, TRN>(acc, sKP, sV, rs, ch2, lr, g);    // A(m=i, k=j) = P[i][j], B(k=j, n=d) = V[j][d]
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
@@ -718,11 +757,11 @@ bool bgrad_supported(const GlaArgs &a) {
            !a.resid && al16(a.q) && al16(a.k) && al16(a.v) && al16(a.log_g);
 }
 
-hipError_t bdo_launch(const GlaArgs &a, const void *dy, const float *Sx, float *dO, void *dz,
-                      float *dWp, float *Ur, float *Gr, int *flags, int n_chunks, hipStream_t s) {
-    const BdArgs p{a, dy, Sx, dO, dz, dWp, Ur, Gr, flags, n_chunks};
-    const int64_t total = static_cast<int64_t>(a.B) * a.H * n_chunks;
-    const dim3 grid(static_cast<unsigned>(total < kPersistent ? total : kPersistent));
+hipError_t bdo_launch(const GlaArgs &a, const MfmaPlan &pl, const void *dy, const float *Sseg,
+                      float *Sx, float *dO, void *dz, float *dWp, float *Ur, float *Gr, int *flags,
+                      int n_chunks, hipStream_t s) {
+    const BdArgs p{a, dy, Sseg, Sx, dO, dz, dWp, Ur, Gr, flags, n_chunks, pl};
+    const dim3 grid(static_cast<unsigned>(pl.n_wg));
     if (a.dtype == DT_F16)
         hipLaunchKernelGGL((k_bdo<DT_F16>), grid, dim3(NTB), 0, s, p);
     else if (a.dtype == DT_BF16)

@@ -643,23 +643,22 @@ __global__ __launch_bounds__(NT) void k_bwd_wsum(BwdArgs p, int64_t n_parts, flo
 }
 
 template <int DT, int DK, int DV>
-hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hooks, int *flags) {
+hipError_t run_shape(const BwdArgs &p, bool mfma, const MfmaPlan &ps, const float *Useg,
+                     hipStream_t st, const BwdLaunchHooks &hooks, int *flags) {
     const int64_t ncb = static_cast<int64_t>(p.a.B) * p.a.H * p.n_chunks;
     const dim3 grid(static_cast<unsigned>(ncb));
     auto done = [&]() {
         const hipError_t e = hipGetLastError();
         return e != hipSuccess ? e : hooks.after(st);
     };
-    // matrix-core gradients where the shape allows (16-bit I/O, dk = dv = 64)
-    auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
-    const bool mfma = DT != DT_F32 && DK == 64 && DV == 64 && bgrad_supported(p.a) && al16(p.dq) &&
-                      al16(p.dk) && al16(p.dv) && al16(p.dz) && al16(p.dy) && al16(p.a.z) &&
-                      al16(p.a.rms_w);
     BwdArgs q = p;
     q.flags = flags;
     hipError_t e;
     if (mfma) {
-        e = bdo_launch(p.a, p.dy, p.Sx, p.dO, p.dz, p.dWp, p.Ur, p.Gr, flags, p.n_chunks, st);
+        // the chunks' forward states (carried through each segment of ps from Useg),
+        // the epilogue backward and the reverse summaries
+        e = bdo_launch(p.a, ps, p.dy, Useg, const_cast<float *>(p.Sx), p.dO, p.dz, p.dWp, p.Ur, p.Gr,
+                       flags, p.n_chunks, st);
         if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
         // chunks out of the matrix path's exponent range: token-serial dO and summaries
         hipLaunchKernelGGL((k_bwd_fallback<DT, DK, DV, 1>), grid, dim3(NT), 0, st, q);
@@ -696,9 +695,11 @@ hipError_t run_shape(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hoo
 }
 
 template <int DT>
-hipError_t run_dt(const BwdArgs &p, hipStream_t st, const BwdLaunchHooks &hooks, int *flags) {
+hipError_t run_dt(const BwdArgs &p, bool mfma, const MfmaPlan &ps, const float *Useg, hipStream_t st,
+                  const BwdLaunchHooks &hooks, int *flags) {
 #define GTR_BWD_CASE(DK_, DV_) \
-    if (p.a.dk == DK_ && p.a.dv == DV_) return run_shape<DT, DK_, DV_>(p, st, hooks, flags);
+    if (p.a.dk == DK_ && p.a.dv == DV_)                                      \
+        return run_shape<DT, DK_, DV_>(p, mfma, ps, Useg, st, hooks, flags);
     GTR_BWD_CASE(32, 32) GTR_BWD_CASE(32, 64) GTR_BWD_CASE(32, 128)
     GTR_BWD_CASE(64, 32) GTR_BWD_CASE(64, 64) GTR_BWD_CASE(64, 128)
     GTR_BWD_CASE(128, 32) GTR_BWD_CASE(128, 64) GTR_BWD_CASE(128, 128)
@@ -715,7 +716,8 @@ size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks) {
                 + rows * (a.dv + a.dk)                                // do, q dq
                 + ncb * (a.dk + a.dv)                                 // chunk totals, drms_w parts
                 + ncb                                                 // chunk flags
-                + static_cast<size_t>(WS_BLOCKS) * a.dv);             // drms_w block sums
+                + static_cast<size_t>(WS_BLOCKS) * a.dv               // drms_w block sums
+                + ncb * (static_cast<size_t>(a.dk) * a.dv + a.dk));   // segment states (<= chunks)
 }
 
 hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
@@ -730,28 +732,45 @@ hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void
     float *dWp = Tn + ncb * a.dk;
     int *flags = reinterpret_cast<int *>(dWp + ncb * a.dv);
     float *part2 = reinterpret_cast<float *>(flags + ncb);
-    // forward incoming states: the forward path's chunk summaries (the matrix-core
-    // kernel with one chunk per segment where it applies; log2 gate totals) and scan
+    float *Useg = part2 + static_cast<size_t>(WS_BLOCKS) * a.dv, *Gseg = Useg + ncb * dd;
     auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
-    const bool msum = sum_supported(a) && !a.feat && !a.resid && al16(a.k) && al16(a.v) &&
-                      al16(a.log_g);
+    // matrix-core path where the shape allows (16-bit I/O, dk = dv = 64, chunk <= 64)
+    const bool mfma = a.dtype != DT_F32 && a.dk == 64 && a.dv == 64 && bgrad_supported(a) &&
+                      al16(dq) && al16(dk) && al16(dv) && al16(dz) && al16(dy) && al16(a.z) &&
+                      al16(a.rms_w);
+    // forward incoming states.  Matrix-core path: the forward path's segment
+    // summaries (log2 gate totals) and scan where its kernel applies, else
+    // per-chunk (one-chunk segments); the epilogue kernel carries the state
+    // through each segment and writes every chunk's.  fp32 path: per-chunk
+    // summaries and scan.
+    MfmaPlan ps{};
     hipError_t e;
-    if (msum) {
-        MfmaPlan ps, po;
-        mfma_plans(a, 1, &ps, &po);
-        e = sum_launch(a, ps, Uf, Gf, st);
+    if (mfma) {
+        const bool msum = sum_supported(a) && !a.feat && !a.resid && al16(a.k) && al16(a.v) &&
+                          al16(a.log_g);
+        if (msum) {
+            MfmaPlan po;
+            mfma_plans(a, 0, &ps, &po);
+            e = sum_launch(a, ps, Useg, Gseg, st);
+        } else {
+            ps = mfma_plan(a, 1);
+            e = serial_summary(a, Useg, Gseg, n_chunks, st);
+        }
+        if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+        e = msum ? state_scan_plan(Useg, Gseg, ps, static_cast<int>(a.B * a.H), a.dk, a.dv, st)
+                 : state_scan(Useg, Gseg, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st);
     } else {
         e = serial_summary(a, Uf, Gf, n_chunks, st);
+        if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+        e = state_scan(Uf, Gf, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st);
     }
-    if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
-    e = state_scan(Uf, Gf, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st, msum);
     if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
     BwdArgs p{a, dy, Uf, nullptr, dO, qdq, Ur, Gr, Tn, dWp, dq, dk, dv, dz, dlog_g, drms_w,
               nullptr, n_chunks, part2, ctr};
     switch (a.dtype) {
-    case DT_F32: return run_dt<DT_F32>(p, st, hooks, flags);
-    case DT_F16: return run_dt<DT_F16>(p, st, hooks, flags);
-    case DT_BF16: return run_dt<DT_BF16>(p, st, hooks, flags);
+    case DT_F32: return run_dt<DT_F32>(p, false, ps, Useg, st, hooks, flags);
+    case DT_F16: return run_dt<DT_F16>(p, mfma, ps, Useg, st, hooks, flags);
+    case DT_BF16: return run_dt<DT_BF16>(p, mfma, ps, Useg, st, hooks, flags);
     default: return hipErrorInvalidValue;
     }
 }
