@@ -184,28 +184,33 @@ bool lowrank_fused_supported(const GlaArgs &a);
 // value + bias) from u = [gate | value].
 hipError_t sswiglu_launch(const void *u, const float *w, const float *b, void *m, int B, int gh,
                           int gw, int F, int k, int dtype, hipStream_t s);
-// Backward pass (k_bwd.hip), fp32 chunk-parallel.  hooks.after() runs after every
-// launch (event recording).  ws: bwd_workspace_bytes(a, n_chunks) bytes.
+// Backward pass (k_bwd.hip: pipeline and the fp32 token-serial kernels; k_bgrad.hip:
+// the matrix-core kernels).  hooks.after() runs after every launch (event
+// recording).  ws: bwd_workspace_bytes(a, n_chunks) bytes.
 struct BwdLaunchHooks {
     hipError_t (*fn)(void *ctx, hipStream_t st) = nullptr;
     void *ctx = nullptr;
     hipError_t after(hipStream_t st) const { return fn ? fn(ctx, st) : hipSuccess; }
 };
 size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks);
-// Matrix-core gradients of q, k, v per chunk (k_bgrad.hip): 16-bit I/O, dk = dv = 64,
-// chunk <= 64.  Chunks whose decay span is out of range are flagged (flags[chunk] = 1)
-// and left to the token-serial kernels.
+// The matrix-core backward kernels' shape: 16-bit I/O, dk = dv = 64, chunk <= 64,
+// 16-byte aligned q, k, v, log_g.
 bool bgrad_supported(const GlaArgs &a);
-// Matrix-core epilogue backward and reverse chunk summaries (same support):
-// workgroup b walks chunks [b Q, b Q + Q) of pl in order from the incoming state
-// of its segment (Sseg[seg_id(b Q)]), writing each chunk's incoming state to Sx,
-// dO, dz, drms_w partials, Ur and Gr (log2); flags as bgrad_launch.
-hipError_t bdo_launch(const GlaArgs &a, const MfmaPlan &pl, const void *dy, const float *Sseg,
-                      float *Sx, float *dO, void *dz, float *dWp, float *Ur, float *Gr, int *flags,
-                      int n_chunks, hipStream_t s);
-hipError_t bgrad_launch(const GlaArgs &a, const float *dO, const float *Sx, const float *Er,
-                        void *dq, void *dk, void *dv, float *dlog_g, int *flags, int n_chunks,
-                        hipStream_t s);
+// Matrix-core epilogue backward and reverse chunk summaries: workgroup b walks
+// chunks [b R, b R + R) in order (R a multiple of pl.Q, so b R starts a segment
+// of pl), carrying the forward state from that segment's incoming state
+// (Sseg[seg_id(b R)]); it writes dO, dz, the
+// drms_w partials, Ur and Gr (log2), the per-chunk flags (1: the decay span
+// exceeds the matrix path's range; the token-serial kernels take the chunk), and
+// the incoming state of each flagged chunk and of its successor to Sx.
+hipError_t bdo_launch(const GlaArgs &a, const MfmaPlan &pl, int64_t R, const void *dy,
+                      const float *Sseg, float *Sx, float *dO, void *dz, float *dWp, float *Ur,
+                      float *Gr, int *flags, int n_chunks, hipStream_t s);
+// Matrix-core gradients (dq, dk, dv, complete dlog_g) of the chunks bdo_launch did
+// not flag, the same walk with the same plan; Er: the scanned reverse states.
+hipError_t bgrad_launch(const GlaArgs &a, const MfmaPlan &pl, int64_t R, const float *dO,
+                        const float *Sseg, const float *Sx, const float *Er, void *dq, void *dk,
+                        void *dv, float *dlog_g, const int *flags, int n_chunks, hipStream_t s);
 hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
                       float *dlog_g, void *dz, float *drms_w, void *ws, unsigned *ctr, int n_chunks,
                       hipStream_t st, const BwdLaunchHooks &hooks);

@@ -53,12 +53,15 @@ constexpr int64_t kPersistent = 256;  // workgroups: one per CU
 struct BgArgs {
     GlaArgs a;
     const float *dO;    // [rows][64]
-    const float *Sx;    // forward incoming state per chunk [bh N + n][64][64]
+    const float *Sseg;  // forward incoming state of each segment of pl [seg][64][64]
+    const float *Sx;    // forward incoming state per chunk, for the flagged chunks' successors
     const float *Er;    // reverse incoming gradient state per chunk, reversed chunk order
     void *dq, *dk, *dv;
     float *dlog_g;      // complete gate gradient
-    int *flags;         // per chunk: 1 = left to the token-serial kernels
+    const int *flags;   // per chunk: 1 = left to the token-serial kernels
     int n_chunks;
+    MfmaPlan pl;        // segments of the incoming states Sseg
+    int64_t R;          // workgroup b takes chunks [b R, b R + R) in order (R: a multiple of pl.Q)
 };
 
 __device__ __forceinline__ void st4(float *dst, float4 x) { *reinterpret_cast<float4 *>(dst) = x; }
@@ -155,14 +158,15 @@ struct BdArgs {
     GlaArgs a;
     const void *dy;     // gradient of out, I/O type
     const float *Sseg;  // forward incoming state of each segment of pl [seg][64][64]
-    float *Sx;          // out: forward incoming state per chunk [bh N + n][64][64]
+    float *Sx;          // out: forward incoming state of each flagged chunk and of its successor
     float *dO;          // [rows][64]
     void *dz;
     float *dWp;         // [bh N + n][64] drms_w partials
     float *Ur, *Gr;     // reverse summaries and chunk gates (log2), reversed chunk order
     int *flags;         // per chunk: 1 = left to the token-serial kernels
     int n_chunks;
-    MfmaPlan pl;        // workgroup b takes chunks [b Q, b Q + Q) in order
+    MfmaPlan pl;        // segments of the incoming states Sseg
+    int64_t R;          // workgroup b takes chunks [b R, b R + R) in order (R: a multiple of pl.Q)
 };
 
 // Eight waves (two per SIMD, so that one wave's LDS, matrix-unit and memory
@@ -279,8 +283,8 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
     const int rs = w & 3, ch2 = w >> 2;  // row stripe, column half
     const int64_t total = static_cast<int64_t>(a.B) * a.H * p.n_chunks;
-    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * p.pl.Q;
-    const int64_t c1 = (c0 + p.pl.Q < total) ? c0 + p.pl.Q : total;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * p.R;
+    const int64_t c1 = (c0 + p.R < total) ? c0 + p.R : total;
     const int et = tid >> 3, ec = (tid & 7) * 8;  // load-layout row and columns of this thread
     float rw[8];                                  // rms_w of those columns
     {
@@ -324,12 +328,15 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
         const bool slow = __syncthreads_or(-tot > kSpanMax);
         if (tid == 0) p.flags[at.cidx] = slow ? 1 : 0;
 
-        // ---- the chunk's incoming state: out to Sx, and as S^T planes
+        // ---- the chunk's incoming state as S^T planes; a flagged chunk's also to Sx
+        // (the token-serial kernels read it, and the state after it)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int d = 16 * (2 * ch2 + tt) + lr;
+            if (slow) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p.Sx[at.cidx * MAT + (16 * rs + 4 * g + r) * BC + d] = sreg[tt][r];
+                for (int r = 0; r < 4; ++r) p.Sx[at.cidx * MAT + (16 * rs + 4 * g + r) * BC + d] = sreg[tt][r];
+            }
             put<4>(sSD, d, 16 * rs + 4 * g, sreg[tt]);
         }
         // ---- operands (rows past the chunk's end are zero): K~ = k 2^(G - a) and V
@@ -371,6 +378,14 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) sreg[tt][r] = sG[16 * rs + 4 * g + r] * sreg[tt][r] + acc[tt][r];
         if (slow) {  // the whole workgroup; the token-serial kernels take the chunk
+            if (at.n + 1 < p.n_chunks) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        p.Sx[(at.cidx + 1) * MAT + (16 * rs + 4 * g + r) * BC + 16 * (2 * ch2 + tt) + lr] =
+                            sreg[tt][r];
+            }
             __syncthreads();
             continue;
         }
@@ -487,8 +502,8 @@ struct TokIn {
     float4 g[2], dO[2];
     uint4 q, k, v;
 };
-struct StateIn {  // the chunk's two boundary states, requested once the last are used
-    float4 S[2], E[2];
+struct StateIn {  // the chunk's reverse state, requested once the last is used
+    float4 E[2];
 };
 
 __device__ __forceinline__ void request_tok(TokIn &in, const BgArgs &p, const int64_t *rows, int tid) {
@@ -515,8 +530,7 @@ __device__ __forceinline__ void request_state(StateIn &in, const BgArgs &p, cons
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
-        in.S[u] = ld4(p.Sx + at.cidx * MAT + t * BC + c);  // S[c'][d]: row c' = t, column d = c
-        in.E[u] = ld4(p.Er + at.ridx * MAT + t * BC + c);  // E[c'][d]
+        in.E[u] = ld4(p.Er + at.ridx * MAT + t * BC + c);  // E[c'][d]: row c' = t, column d = c
     }
 }
 
@@ -539,25 +553,48 @@ __global__ __launch_bounds__(NTB, 1) void k_bgrad(BgArgs p) {
     const int rs = w & 3, ch2 = w >> 2;           // row stripe, column half
     const int et = tid >> 3, ec = (tid & 7) * 8;  // load-layout row and columns (16-bit pieces)
     const int64_t total = static_cast<int64_t>(a.B) * a.H * p.n_chunks;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * p.R;
+    const int64_t c1 = (c0 + p.R < total) ? c0 + p.R : total;
+    // carried forward state, transposed in the MFMA layout: sreg[tt][r] =
+    // S[16 (2 ch2 + tt) + lr][16 rs + 4 g + r] (four consecutive columns of a row of S),
+    // from the segment's incoming state (none at a sequence's first chunk)
+    float sreg[2][4];
+    auto load_state = [&](const float *src) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const float4 x = ld4(src + (16 * (2 * ch2 + tt) + lr) * BC + 16 * rs + 4 * g);
+            sreg[tt][0] = x.x; sreg[tt][1] = x.y; sreg[tt][2] = x.z; sreg[tt][3] = x.w;
+        }
+    };
+    auto zero_state = [&]() {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sreg[tt][r] = 0.f;
+    };
+    if (ChunkAt(a, p.n_chunks, c0).n == 0)
+        zero_state();
+    else
+        load_state(p.Sseg + seg_id(c0, p.pl) * MAT);
 
-    int64_t chk = blockIdx.x;
     int buf = 0;
-    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, chk).row(a, tid);
+    if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, c0).row(a, tid);
     __syncthreads();
     TokIn in;
     StateIn st_in;
     request_tok(in, p, srow[0], tid);
-    request_state(st_in, p, ChunkAt(a, p.n_chunks, chk), tid);
+    request_state(st_in, p, ChunkAt(a, p.n_chunks, c0), tid);
 
-    for (; chk < total; chk += gridDim.x, buf ^= 1) {
+    for (int64_t chk = c0; chk < c1; ++chk, buf ^= 1) {
         const ChunkAt at(a, p.n_chunks, chk);
         const int64_t *rows = srow[buf];
         const int nt = at.nt;
-        const int64_t cn = chk + gridDim.x;  // next chunk of this workgroup
+        const int64_t cn = chk + 1;  // next chunk of this workgroup (if below c1)
+        if (at.n == 0) zero_state();  // a new sequence
 
         const float tot = chunk_gates8(in.g, sA2, sG, sTot, nt, tid);
+        // the same decision as the epilogue kernel's (same inputs, same arithmetic)
         const bool slow = __syncthreads_or(-tot > kSpanMax);  // uniform over the workgroup
-        if (tid == 0) p.flags[at.cidx] = slow ? 1 : 0;
 
         // ---- operands (rows past the chunk's end are zero); exact q and k kept
         uint4 qkeep, kkeep;
@@ -582,20 +619,31 @@ __global__ __launch_bounds__(NTB, 1) void k_bgrad(BgArgs p) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
-                const float4 d = in.dO[u], sv = st_in.S[u];
+                const float4 d = in.dO[u];
                 const bool okr = t < nt;
                 const float dd[4] = {okr ? d.x : 0.f, okr ? d.y : 0.f, okr ? d.z : 0.f, okr ? d.w : 0.f};
-                const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
                 put<4>(sDO, t, c, dd);
-                put<4>(sSE, t, c, ss);
             }
+            // the incoming state as S planes (row c, columns d)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) put<4>(sSE, 16 * (2 * ch2 + tt) + lr, 16 * rs + 4 * g, sreg[tt]);
         }
         // ---- the next chunk's rows, then its per-token inputs (those registers are free)
-        if (cn < total && tid < BC) srow[buf ^ 1][tid] = ChunkAt(a, p.n_chunks, cn).row(a, tid);
+        if (cn < c1 && tid < BC) srow[buf ^ 1][tid] = ChunkAt(a, p.n_chunks, cn).row(a, tid);
         __syncthreads();
-        if (cn < total) request_tok(in, p, srow[buf ^ 1], tid);
+        if (cn < c1) request_tok(in, p, srow[buf ^ 1], tid);
         if (slow) {  // the whole workgroup; its gradients come from the token-serial kernels
-            if (cn < total) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
+            if (cn < c1) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
+            // the state after the chunk, as the epilogue kernel wrote it; waited for
+            // here (an empty asm reads the registers), so that no load into them is
+            // outstanding where the other path reuses registers
+            if (at.n + 1 < p.n_chunks)
+                load_state(p.Sx + (at.cidx + 1) * MAT);
+            else
+                zero_state();
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                asm volatile("" ::"v"(sreg[tt][0]), "v"(sreg[tt][1]), "v"(sreg[tt][2]), "v"(sreg[tt][3]));
             continue;
         }
 
@@ -621,28 +669,32 @@ __global__ __launch_bounds__(NTB, 1) void k_bgrad(BgArgs p) {
             for (int r = 0; r < 4; ++r) x[r] = (16 * t + lr <= 16 * rs + 4 * g + r) ? acc[tt][r] : 0.f;
             put<4>(sPT, 16 * t + lr, 16 * rs + 4 * g, x);
         }
-        // ---- T = K^^T V (rows c), staged
+        // ---- the state after the chunk, S_out^T = (S^T + V^T K^) . 2^G (columns c),
+        // carried and staged as S_out
         zero2(acc);
-        gemm2<TRN, TRN>(acc, sKH, sV, rs, ch2, lr, g);    // A(m=c, k=j) = K^[j][c], B(k=j, n=d) = V[j][d]
+        gemm2<TRN, TRN>(acc, sV, sKH, rs, ch2, lr, g);    // A(m=d, k=j) = V[j][d], B(k=j, n=c) = K^[j][c]
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
+            const int c = 16 * (2 * ch2 + tt) + lr;
+            const float gc = sG[c];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sX[16 * rs + 4 * g + r][16 * (2 * ch2 + tt) + lr] = acc[tt][r];
+            for (int r = 0; r < 4; ++r) sreg[tt][r] = gc * (sreg[tt][r] + acc[tt][r]);
+            st4(&sX[c][16 * rs + 4 * g], make_float4(sreg[tt][0], sreg[tt][1], sreg[tt][2], sreg[tt][3]));
+        }
         __syncthreads();
 
-        // ---- offset of the gate gradient: sum_d E[c][d] S_out[c][d] with
-        // S_out = 2^G . (S + T); the 16 lanes of a channel row reduce together
+        // ---- offset of the gate gradient: sum_d E[c][d] S_out[c][d]; the 16 lanes
+        // of a channel row reduce together
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
-            const float4 sv = st_in.S[u], ev = st_in.E[u], tv = ld4(&sX[t][c]);
-            float x = ev.x * (sv.x + tv.x) + ev.y * (sv.y + tv.y) + ev.z * (sv.z + tv.z) +
-                      ev.w * (sv.w + tv.w);
+            const float4 ev = st_in.E[u], sv = ld4(&sX[t][c]);
+            float x = ev.x * sv.x + ev.y * sv.y + ev.z * sv.z + ev.w * sv.w;
             x += __shfl_xor(x, 1);
             x += __shfl_xor(x, 2);
             x += __shfl_xor(x, 4);
             x += __shfl_xor(x, 8);
-            if ((tid & 15) == 0) sOff[t] = sG[t] * x;
+            if ((tid & 15) == 0) sOff[t] = x;
         }
 
         // ---- dQ = 2^a . (dO S^T + D K^)
@@ -666,7 +718,7 @@ __global__ __launch_bounds__(NTB, 1) void k_bgrad(BgArgs p) {
             const float ee[4] = {gt * ev.x, gt * ev.y, gt * ev.z, gt * ev.w};
             put<4>(sSE, t, c, ee);
         }
-        if (cn < total) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
+        if (cn < c1) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
         __syncthreads();
         // dq out; q . dq of this thread's piece
         float qdq[8];
@@ -757,11 +809,11 @@ bool bgrad_supported(const GlaArgs &a) {
            !a.resid && al16(a.q) && al16(a.k) && al16(a.v) && al16(a.log_g);
 }
 
-hipError_t bdo_launch(const GlaArgs &a, const MfmaPlan &pl, const void *dy, const float *Sseg,
-                      float *Sx, float *dO, void *dz, float *dWp, float *Ur, float *Gr, int *flags,
-                      int n_chunks, hipStream_t s) {
-    const BdArgs p{a, dy, Sseg, Sx, dO, dz, dWp, Ur, Gr, flags, n_chunks, pl};
-    const dim3 grid(static_cast<unsigned>(pl.n_wg));
+hipError_t bdo_launch(const GlaArgs &a, const MfmaPlan &pl, int64_t R, const void *dy,
+                      const float *Sseg, float *Sx, float *dO, void *dz, float *dWp, float *Ur,
+                      float *Gr, int *flags, int n_chunks, hipStream_t s) {
+    const BdArgs p{a, dy, Sseg, Sx, dO, dz, dWp, Ur, Gr, flags, n_chunks, pl, R};
+    const dim3 grid(static_cast<unsigned>((pl.T + R - 1) / R));
     if (a.dtype == DT_F16)
         hipLaunchKernelGGL((k_bdo<DT_F16>), grid, dim3(NTB), 0, s, p);
     else if (a.dtype == DT_BF16)
@@ -771,12 +823,11 @@ hipError_t bdo_launch(const GlaArgs &a, const MfmaPlan &pl, const void *dy, cons
     return hipGetLastError();
 }
 
-hipError_t bgrad_launch(const GlaArgs &a, const float *dO, const float *Sx, const float *Er,
-                        void *dq, void *dk, void *dv, float *dlog_g, int *flags, int n_chunks,
-                        hipStream_t s) {
-    const BgArgs p{a, dO, Sx, Er, dq, dk, dv, dlog_g, flags, n_chunks};
-    const int64_t total = static_cast<int64_t>(a.B) * a.H * n_chunks;
-    const dim3 grid(static_cast<unsigned>(total < kPersistent ? total : kPersistent));
+hipError_t bgrad_launch(const GlaArgs &a, const MfmaPlan &pl, int64_t R, const float *dO,
+                        const float *Sseg, const float *Sx, const float *Er, void *dq, void *dk,
+                        void *dv, float *dlog_g, const int *flags, int n_chunks, hipStream_t s) {
+    const BgArgs p{a, dO, Sseg, Sx, Er, dq, dk, dv, dlog_g, flags, n_chunks, pl, R};
+    const dim3 grid(static_cast<unsigned>((pl.T + R - 1) / R));
     if (a.dtype == DT_F16)
         hipLaunchKernelGGL((k_bgrad<DT_F16>), grid, dim3(NTB), 0, s, p);
     else if (a.dtype == DT_BF16)

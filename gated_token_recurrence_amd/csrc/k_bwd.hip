@@ -31,6 +31,7 @@ namespace {
 
 constexpr int NT = 256;
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int64_t kBwdWorkgroups = 256;  // matrix-core backward kernels: one per CU
 
 template <int DK, int DV> struct BwdShape {
     static constexpr int PER = DK * DV / NT;      // state elements per thread
@@ -647,6 +648,10 @@ hipError_t run_shape(const BwdArgs &p, bool mfma, const MfmaPlan &ps, const floa
                      hipStream_t st, const BwdLaunchHooks &hooks, int *flags) {
     const int64_t ncb = static_cast<int64_t>(p.a.B) * p.a.H * p.n_chunks;
     const dim3 grid(static_cast<unsigned>(ncb));
+    // chunks per workgroup of the matrix-core kernels: whole segments of ps, about
+    // one workgroup per CU (their LDS allows one)
+    const int64_t per = (ps.n_wg + kBwdWorkgroups / 2) / kBwdWorkgroups;
+    const int64_t R = ps.Q * (per > 1 ? per : 1);
     auto done = [&]() {
         const hipError_t e = hipGetLastError();
         return e != hipSuccess ? e : hooks.after(st);
@@ -655,10 +660,10 @@ hipError_t run_shape(const BwdArgs &p, bool mfma, const MfmaPlan &ps, const floa
     q.flags = flags;
     hipError_t e;
     if (mfma) {
-        // the chunks' forward states (carried through each segment of ps from Useg),
-        // the epilogue backward and the reverse summaries
-        e = bdo_launch(p.a, ps, p.dy, Useg, const_cast<float *>(p.Sx), p.dO, p.dz, p.dWp, p.Ur, p.Gr,
-                       flags, p.n_chunks, st);
+        // the epilogue backward and the reverse summaries, the forward state carried
+        // through each segment of ps from Useg (stored for the flagged chunks only)
+        e = bdo_launch(p.a, ps, R, p.dy, Useg, const_cast<float *>(p.Sx), p.dO, p.dz, p.dWp, p.Ur,
+                       p.Gr, flags, p.n_chunks, st);
         if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
         // chunks out of the matrix path's exponent range: token-serial dO and summaries
         hipLaunchKernelGGL((k_bwd_fallback<DT, DK, DV, 1>), grid, dim3(NT), 0, st, q);
@@ -672,7 +677,8 @@ hipError_t run_shape(const BwdArgs &p, bool mfma, const MfmaPlan &ps, const floa
     if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
     q.Er = p.Ur;  // scanned in place
     if (mfma) {
-        e = bgrad_launch(p.a, p.dO, p.Sx, q.Er, p.dq, p.dk, p.dv, p.dlog_g, flags, p.n_chunks, st);
+        e = bgrad_launch(p.a, ps, R, p.dO, Useg, p.Sx, q.Er, p.dq, p.dk, p.dv, p.dlog_g, flags,
+                         p.n_chunks, st);
         if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
         // chunks out of the matrix path's exponent range: token-serial gradients
         hipLaunchKernelGGL((k_bwd_fallback<DT, DK, DV, 2>), grid, dim3(NT), 0, st, q);
