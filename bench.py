@@ -676,9 +676,9 @@ def main():
             bbytes = w.tokens * w.H * ((2 * w.dk + 3 * w.dv) * s_io + 4 * w.dk      # reads
                                        + (2 * w.dk + 2 * w.dv) * s_io + 4 * w.dk)   # writes
             if w.dtype != "f32" and w.dk == 64 and w.dv == 64 and w.chunk <= 64:  # matrix-core gradients
-                names_b = ("forward_chunk_summary", "forward_state_scan", "chunk_do_and_summary_mfma",
-                           "fallback_do_and_summary", "reverse_state_scan", "chunk_gradients_mfma",
-                           "fallback_gradients", "rms_w_sum")
+                names_b = ("forward_segment_summary", "forward_segment_scan", "chunk_do_and_summary_mfma",
+                           "fallback_do_and_summary_rms_w", "reverse_state_scan", "chunk_gradients_mfma",
+                           "fallback_gradients")
             else:
                 names_b = ("forward_chunk_summary", "forward_state_scan", "forward_walk_dq",
                            "reverse_chunk_summary", "reverse_state_scan", "reverse_walk_dk_dv",

@@ -199,12 +199,12 @@ bool bgrad_supported(const GlaArgs &a);
 // Matrix-core epilogue backward and reverse chunk summaries: workgroup b walks
 // chunks [b R, b R + R) in order (R a multiple of pl.Q, so b R starts a segment
 // of pl), carrying the forward state from that segment's incoming state
-// (Sseg[seg_id(b R)]); it writes dO, dz, the
-// drms_w partials, Ur and Gr (log2), the per-chunk flags (1: the decay span
+// (Sseg[seg_id(b R)]).  It writes dO, dz, Ur and Gr (log2), the drms_w sum over
+// the range's unflagged chunks (wr[b]), the per-chunk flags (1: the decay span
 // exceeds the matrix path's range; the token-serial kernels take the chunk), and
 // the incoming state of each flagged chunk and of its successor to Sx.
 hipError_t bdo_launch(const GlaArgs &a, const MfmaPlan &pl, int64_t R, const void *dy,
-                      const float *Sseg, float *Sx, float *dO, void *dz, float *dWp, float *Ur,
+                      const float *Sseg, float *Sx, float *dO, void *dz, float *wr, float *Ur,
                       float *Gr, int *flags, int n_chunks, hipStream_t s);
 // Matrix-core gradients (dq, dk, dv, complete dlog_g) of the chunks bdo_launch did
 // not flag, the same walk with the same plan; Er: the scanned reverse states.

@@ -161,7 +161,7 @@ struct BdArgs {
     float *Sx;          // out: forward incoming state of each flagged chunk and of its successor
     float *dO;          // [rows][64]
     void *dz;
-    float *dWp;         // [bh N + n][64] drms_w partials
+    float *wr;          // [workgroup][64] drms_w sums over the range's unflagged chunks
     float *Ur, *Gr;     // reverse summaries and chunk gates (log2), reversed chunk order
     int *flags;         // per chunk: 1 = left to the token-serial kernels
     int n_chunks;
@@ -306,6 +306,7 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
                 sreg[tt][r] = first ? 0.f : src[(16 * rs + 4 * g + r) * BC + 16 * (2 * ch2 + tt) + lr];
     }
 
+    float wsum = 0.f;  // wave 0, lane l: drms_w partials of the range's unflagged chunks, in order
     int buf = 0;
     if (tid < BC) srow[0][tid] = ChunkAt(a, p.n_chunks, c0).row(a, tid);
     __syncthreads();
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
 #pragma unroll
             for (int u = 0; u < NW; ++u) x += sW[u][l];
             p.Gr[at.ridx * BC + l] = tot;
-            p.dWp[at.cidx * BC + l] = x;
+            wsum += x;
         }
         __syncthreads();
 #pragma unroll
@@ -493,6 +494,7 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
         }
         __syncthreads();  // LDS is rewritten by the next chunk
     }
+    if (w == 0) p.wr[static_cast<int64_t>(blockIdx.x) * BC + l] = wsum;
 }
 
 // ---- The gradients (see the top of the file), eight waves.
@@ -810,9 +812,9 @@ bool bgrad_supported(const GlaArgs &a) {
 }
 
 hipError_t bdo_launch(const GlaArgs &a, const MfmaPlan &pl, int64_t R, const void *dy,
-                      const float *Sseg, float *Sx, float *dO, void *dz, float *dWp, float *Ur,
+                      const float *Sseg, float *Sx, float *dO, void *dz, float *wr, float *Ur,
                       float *Gr, int *flags, int n_chunks, hipStream_t s) {
-    const BdArgs p{a, dy, Sseg, Sx, dO, dz, dWp, Ur, Gr, flags, n_chunks, pl, R};
+    const BdArgs p{a, dy, Sseg, Sx, dO, dz, wr, Ur, Gr, flags, n_chunks, pl, R};
     const dim3 grid(static_cast<unsigned>((pl.T + R - 1) / R));
     if (a.dtype == DT_F16)
         hipLaunchKernelGGL((k_bdo<DT_F16>), grid, dim3(NTB), 0, s, p);

@@ -471,7 +471,9 @@ __device__ __forceinline__ void revwalk_body(const BwdArgs &p, const ChunkPos &c
             }
         }
         __syncthreads();
-        if (tid < DK) p.Tn[cp.cid() * DK + tid] = sacc[tid];
+        // chunk totals for the fp32 path's offset pass (the OFFSET path has none, and
+        // there Tn holds the ranges' drms_w sums)
+        if (!OFFSET && tid < DK) p.Tn[cp.cid() * DK + tid] = sacc[tid];
     }
 
     // ---- pass B, map A: dv_t = dS_t^T k_t
@@ -527,22 +529,70 @@ __global__ __launch_bounds__(NT) void k_bwd_revwalk(BwdArgs p) {
     revwalk_body<DT, DK, DV, false>(p, ChunkPos(p.a, p.n_chunks, blockIdx.x));
 }
 
-// Token-serial fallback of the matrix-core path, one workgroup per chunk, for the
-// chunks it flagged.  PHASE 1 (after the epilogue kernel): dO, dz, drms_w partials,
-// then the reverse summary (from the dO just written).  PHASE 2 (after the
-// gradient kernel): dq and q dq, then dk, dv and the complete dlog_g.
+// Token-serial fallback of the matrix-core path for the chunks it flagged, by the
+// matrix-core kernels' ranges (workgroup b: chunks [b R, b R + R), in order).
+// PHASE 1 (after the epilogue kernel): dO, dz, drms_w partials, then the reverse
+// summary (from the dO just written); range b's drms_w sum (the epilogue
+// kernel's, over its unflagged chunks, in wr[b]) gains its flagged chunks'
+// partials in order.  PHASE 2 (after the gradient kernel): dq and q dq, then dk,
+// dv and the complete dlog_g; workgroup 0 also adds the ranges' sums in order
+// into drms_w.
 template <int DT, int DK, int DV, int PHASE>
-__global__ __launch_bounds__(NT) void k_bwd_fallback(BwdArgs p) {
-    const ChunkPos cp(p.a, p.n_chunks, blockIdx.x);
-    if (p.flags[cp.cid()] == 0) return;  // the whole workgroup
+__global__ __launch_bounds__(NT) void k_bwd_fallback(BwdArgs p, int64_t R, float *wr) {
+    __shared__ int sflag[64];
+    const int tid = threadIdx.x;
+    const int64_t total = static_cast<int64_t>(p.a.B) * p.a.H * p.n_chunks;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * R;
+    const int64_t c1 = (c0 + R < total) ? c0 + R : total;
+    float wacc = 0.f;  // PHASE 1, thread tid < DV: the flagged chunks' drms_w partials
+    for (int64_t b0 = c0; b0 < c1; b0 += 64) {
+        __syncthreads();
+        if (tid < 64) sflag[tid] = (b0 + tid < c1) ? p.flags[b0 + tid] : 0;
+        __syncthreads();
+        for (int k = 0; k < 64 && b0 + k < c1; ++k) {
+            if (sflag[k] == 0) continue;  // uniform: one LDS value
+            const ChunkPos cp(p.a, p.n_chunks, b0 + k);
+            if constexpr (PHASE == 1) {
+                fwdwalk_body<DT, DK, DV, 1>(p, cp);
+                __syncthreads();  // dO and the drms_w partial of this chunk are in global memory
+                revsum_body<DT, DK, DV>(p, cp);
+                if (tid < DV) wacc += p.dWp[cp.cid() * DV + tid];
+            } else {
+                fwdwalk_body<DT, DK, DV, 2>(p, cp);
+                __syncthreads();  // q dq of this chunk is in global memory
+                revwalk_body<DT, DK, DV, true>(p, cp);
+            }
+            __syncthreads();
+        }
+    }
     if constexpr (PHASE == 1) {
-        fwdwalk_body<DT, DK, DV, 1>(p, cp);
-        __syncthreads();  // dO of this chunk is in global memory
-        revsum_body<DT, DK, DV>(p, cp);
-    } else {
-        fwdwalk_body<DT, DK, DV, 2>(p, cp);
-        __syncthreads();  // q dq of this chunk is in global memory
-        revwalk_body<DT, DK, DV, true>(p, cp);
+        if (tid < DV && wacc != 0.f) wr[static_cast<int64_t>(blockIdx.x) * DV + tid] += wacc;
+    } else if (blockIdx.x == 0) {
+        // drms_w = the ranges' sums in order (complete: phase 1 ran before); NT / DV
+        // groups of threads take consecutive parts (16 loads in flight each), then
+        // the groups' sums in order
+        __shared__ float part[NT];
+        constexpr int GS = NT / DV;
+        const int j = tid % DV, gq = tid / DV;
+        const int64_t nr = (total + R - 1) / R;
+        const int64_t per = (nr + GS - 1) / GS;
+        const int64_t r0 = gq * per, r1 = (r0 + per < nr) ? r0 + per : nr;
+        float w = 0.f;
+        for (int64_t b0 = r0; b0 < r1; b0 += 16) {
+            float x[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) x[u] = (b0 + u < r1) ? wr[(b0 + u) * DV + j] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) w += x[u];
+        }
+        __syncthreads();
+        part[tid] = w;
+        __syncthreads();
+        if (tid < DV) {
+            float x = 0.f;
+            for (int r = 0; r < GS; ++r) x += part[r * DV + tid];
+            p.drms_w[tid] = x;
+        }
     }
 }
 
@@ -652,6 +702,7 @@ hipError_t run_shape(const BwdArgs &p, bool mfma, const MfmaPlan &ps, const floa
     // one workgroup per CU (their LDS allows one)
     const int64_t per = (ps.n_wg + kBwdWorkgroups / 2) / kBwdWorkgroups;
     const int64_t R = ps.Q * (per > 1 ? per : 1);
+    const dim3 ranges(static_cast<unsigned>(mfma ? (ncb + R - 1) / R : 1));
     auto done = [&]() {
         const hipError_t e = hipGetLastError();
         return e != hipSuccess ? e : hooks.after(st);
@@ -662,11 +713,12 @@ hipError_t run_shape(const BwdArgs &p, bool mfma, const MfmaPlan &ps, const floa
     if (mfma) {
         // the epilogue backward and the reverse summaries, the forward state carried
         // through each segment of ps from Useg (stored for the flagged chunks only)
-        e = bdo_launch(p.a, ps, R, p.dy, Useg, const_cast<float *>(p.Sx), p.dO, p.dz, p.dWp, p.Ur,
+        // (p.Tn, unused on this path, holds the ranges' drms_w sums)
+        e = bdo_launch(p.a, ps, R, p.dy, Useg, const_cast<float *>(p.Sx), p.dO, p.dz, p.Tn, p.Ur,
                        p.Gr, flags, p.n_chunks, st);
         if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
         // chunks out of the matrix path's exponent range: token-serial dO and summaries
-        hipLaunchKernelGGL((k_bwd_fallback<DT, DK, DV, 1>), grid, dim3(NT), 0, st, q);
+        hipLaunchKernelGGL((k_bwd_fallback<DT, DK, DV, 1>), ranges, dim3(NT), 0, st, q, R, p.Tn);
     } else {
         hipLaunchKernelGGL((k_bwd_fwdwalk<DT, DK, DV>), grid, dim3(NT), 0, st, p);
         if ((e = done()) != hipSuccess) return e;
@@ -680,20 +732,19 @@ hipError_t run_shape(const BwdArgs &p, bool mfma, const MfmaPlan &ps, const floa
         e = bgrad_launch(p.a, ps, R, p.dO, Useg, p.Sx, q.Er, p.dq, p.dk, p.dv, p.dlog_g, flags,
                          p.n_chunks, st);
         if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
-        // chunks out of the matrix path's exponent range: token-serial gradients
-        hipLaunchKernelGGL((k_bwd_fallback<DT, DK, DV, 2>), grid, dim3(NT), 0, st, q);
-    } else {
-        hipLaunchKernelGGL((k_bwd_revwalk<DT, DK, DV>), grid, dim3(NT), 0, st, q);
+        // chunks out of the matrix path's exponent range: token-serial gradients; drms_w
+        hipLaunchKernelGGL((k_bwd_fallback<DT, DK, DV, 2>), ranges, dim3(NT), 0, st, q, R, p.Tn);
+        return done();
     }
+    hipLaunchKernelGGL((k_bwd_revwalk<DT, DK, DV>), grid, dim3(NT), 0, st, q);
     if ((e = done()) != hipSuccess) return e;
-    if (!mfma) {  // the matrix-core path writes complete gate gradients
-        const int64_t nsc = static_cast<int64_t>(p.a.B) * p.a.H * DK;
-        hipLaunchKernelGGL(k_bwd_gatescan, dim3(static_cast<unsigned>((nsc + NT - 1) / NT)), dim3(NT),
-                           0, st, p.Tn, static_cast<int>(p.a.B * p.a.H), p.n_chunks, DK);
-        if ((e = done()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_bwd_gateoff<DK>), grid, dim3(NT), 0, st, q);
-        if ((e = done()) != hipSuccess) return e;
-    }
+    // fp32 path: gate offsets across chunks, then drms_w
+    const int64_t nsc = static_cast<int64_t>(p.a.B) * p.a.H * DK;
+    hipLaunchKernelGGL(k_bwd_gatescan, dim3(static_cast<unsigned>((nsc + NT - 1) / NT)), dim3(NT), 0,
+                       st, p.Tn, static_cast<int>(p.a.B * p.a.H), p.n_chunks, DK);
+    if ((e = done()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_gateoff<DK>), grid, dim3(NT), 0, st, q);
+    if ((e = done()) != hipSuccess) return e;
     const int64_t nb = ncb < WS_BLOCKS ? ncb : WS_BLOCKS;
     hipLaunchKernelGGL((k_bwd_wsum<DV>), dim3(static_cast<unsigned>(nb)), dim3(NT), 0, st, q, ncb,
                        p.part2, p.ctr);
