@@ -170,9 +170,11 @@ gtr_status gtr_gla_lowrank_fwd(const void *q, const void *k, const void *v, cons
  *   dlog_g : [B, grid_h, grid_w, H, dk]  float32
  *   drms_w : [dv]                        float32 (summed over every token and head)
  * Inputs q, k, v, log_g, z, rms_w, dims, direction and chunk as gtr_gla_fwd
- * (no stack residual); dout has out's shape and type.  Arithmetic is fp32
- * (the forward states are recomputed, not stored); gradients of 16-bit I/O are
- * rounded to nearest even.  No gradient buffer may overlap another buffer.
+ * (no stack residual); dout has out's shape and type.  Accumulation is fp32
+ * (16-bit I/O at dk = dv = 64, chunk <= 64: products on the matrix cores with
+ * bf16 hi + lo operands; the forward states are recomputed, not stored);
+ * gradients of 16-bit I/O are rounded to nearest even; results do not depend
+ * on timing (no atomics).  No gradient buffer may overlap another buffer.
  * events / n_events / n_launches as gtr_gla_fwd_events (NULL / 0 allowed).
  * Errors, ownership and asynchrony as gtr_gla_fwd.
  */
