@@ -142,6 +142,24 @@ def test_bwd_mixer_640_sampled(oracle_mod):
     _run_case(oracle_mod, x, w.dtype, 0, chunk=w.chunk, bh=[0, 3, 5], seed=11)
 
 
+def test_bwd_mixer_2048_sampled(oracle_mod):
+    """The 16.4K-token workload the benchmark times (H = 12, fp16): 12-chunk ranges of the
+    matrix-core kernels cross sequence boundaries (256 chunks per sequence); the first, a
+    middle and the last sequence checked."""
+    w = W.WORKLOADS["mixer_2048"]
+    x = W.make_inputs(w)
+    _note("bwd mixer_2048 (sequences 0, 5, 11)")
+    _run_case(oracle_mod, x, w.dtype, 0, chunk=w.chunk, bh=[0, 5, 11], seed=12)
+
+
+def test_bwd_ranges_cross_sequences(oracle_mod):
+    """201 chunks per sequence (67 x 192 grid, H = 3): two-chunk ranges, every other one
+    straddling a sequence boundary; bf16, direction 3."""
+    x = W.make_custom(1, 67, 192, 3, 64, 64, "bf16", seed=31)
+    _note("bwd 201-chunk sequences")
+    _run_case(oracle_mod, x, "bf16", 3, chunk=64, bh=[0, 1, 2], seed=13)
+
+
 def test_bwd_is_deterministic():
     x = W.make_custom(1, 10, 10, 2, 64, 64, "bf16", seed=5)
     t = inputs_to_dev(x, "bf16")
