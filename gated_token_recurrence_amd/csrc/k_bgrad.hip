@@ -48,7 +48,6 @@ using namespace mf;
 constexpr int BC = 64;         // chunk tokens (rows of every matrix) and channels
 constexpr int LS = BC + 4;     // fp32 LDS row stride
 constexpr int MAT = BC * BC;   // elements of one 16-bit plane
-constexpr int64_t kPersistent = 256;  // workgroups: one per CU
 
 struct BgArgs {
     GlaArgs a;
