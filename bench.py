@@ -683,7 +683,7 @@ def main():
                 names_b = ("forward_chunk_summary", "forward_state_scan", "forward_walk_dq",
                            "reverse_chunk_summary", "reverse_state_scan", "reverse_walk_dk_dv",
                            "gate_total_scan", "gate_offsets", "rms_w_sum")
-            backward = {"workload": f"{w.name}: backward of one call, fp32 arithmetic",
+            backward = {"workload": f"{w.name}: backward of one call (matrix cores, bf16 hi+lo operands, fp32 accumulation)",
                         "us_per_call": round(bus, 3),
                         "tokens_per_s": round(w.tokens / (bus * 1e-6), 1),
                         "algorithmic_bytes": bbytes,
