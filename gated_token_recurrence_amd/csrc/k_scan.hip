@@ -160,15 +160,15 @@ __global__ __launch_bounds__(NT) void k_scan_rows(float *__restrict__ U,
     }
 }
 
-// The same four-part fold for plain sequences of n_units units each (unit k of
+// The same fold in P parts (one wave each) for plain sequences of n_units units each (unit k of
 // sequence seq at index seq n_units + k), any dv: each lane takes its own key
 // channel.  Workgroup = (sequence, 64 consecutive state elements).  LOG2: the
 // unit gate totals G are in log2 units (else natural).
-template <int M, bool LOG2>
-__global__ __launch_bounds__(NT) void k_scan_rows_seq(float *__restrict__ U,
-                                                      const float *__restrict__ G, int n_units,
-                                                      int dk, int dv) {
-    __shared__ float sA[4][64], sB[4][64];
+template <int M, bool LOG2, int P>
+__global__ __launch_bounds__(64 * P) void k_scan_rows_seq(float *__restrict__ U,
+                                                          const float *__restrict__ G, int n_units,
+                                                          int dk, int dv) {
+    __shared__ float sA[P][64], sB[P][64];
     const int64_t dd = static_cast<int64_t>(dk) * dv;
     const uint32_t slices = static_cast<uint32_t>(dk * dv / 64);
     const uint32_t seq32 = blockIdx.x / slices;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(NT) void k_scan_rows_seq(float *__restrict__ U,
     const int64_t el = static_cast<int64_t>(blockIdx.x - seq32 * slices) * 64 + lane;
     const int c = static_cast<int>(el / dv);
     const int64_t s0 = seq * n_units, s1 = s0 + n_units;
-    const int64_t len = (n_units + 3) / 4;  // <= M (checked by the host)
+    const int64_t len = (n_units + P - 1) / P;  // <= M (checked by the host)
     const int64_t kb = s0 + part * len;
     const int n = static_cast<int>(kb < s1 ? (kb + len < s1 ? len : s1 - kb) : 0);
     float x[M], e[M];
@@ -231,28 +231,30 @@ hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_s
 }
 
 namespace {
-template <int M>
+template <int M, int P>
 void launch_rows_seq(float *U, const float *G, int n_units, int dk, int dv, bool log2_gates,
                      dim3 grid, hipStream_t s) {
     if (log2_gates)
-        hipLaunchKernelGGL((k_scan_rows_seq<M, true>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+        hipLaunchKernelGGL((k_scan_rows_seq<M, true, P>), grid, dim3(64 * P), 0, s, U, G, n_units,
+                           dk, dv);
     else
-        hipLaunchKernelGGL((k_scan_rows_seq<M, false>), grid, dim3(NT), 0, s, U, G, n_units, dk, dv);
+        hipLaunchKernelGGL((k_scan_rows_seq<M, false, P>), grid, dim3(64 * P), 0, s, U, G, n_units,
+                           dk, dv);
 }
 }  // namespace
 
 hipError_t state_scan(float *U, const float *G, int n_seq, int n_units, int dk, int dv,
                       hipStream_t s, bool log2_gates) {
     const int64_t n_elem = static_cast<int64_t>(n_seq) * dk * dv;
-    if ((static_cast<int64_t>(dk) * dv) % 64 == 0 && n_units <= 4 * 64) {
-        // the four-part fold: memory latency paid about once per sequence
+    if ((static_cast<int64_t>(dk) * dv) % 64 == 0 && n_units <= 16 * 16) {
+        // the folds in parts: memory latency paid about once per sequence
         const dim3 grid(static_cast<unsigned>(n_elem / 64));
         if (n_units <= 4 * 16)
-            launch_rows_seq<16>(U, G, n_units, dk, dv, log2_gates, grid, s);
-        else if (n_units <= 4 * 32)
-            launch_rows_seq<32>(U, G, n_units, dk, dv, log2_gates, grid, s);
+            launch_rows_seq<16, 4>(U, G, n_units, dk, dv, log2_gates, grid, s);
+        else if (n_units <= 8 * 16)
+            launch_rows_seq<16, 8>(U, G, n_units, dk, dv, log2_gates, grid, s);
         else
-            launch_rows_seq<64>(U, G, n_units, dk, dv, log2_gates, grid, s);
+            launch_rows_seq<16, 16>(U, G, n_units, dk, dv, log2_gates, grid, s);
         return hipGetLastError();
     }
     const dim3 grid(static_cast<unsigned>((n_elem + NT - 1) / NT));
