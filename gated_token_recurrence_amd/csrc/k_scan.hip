@@ -106,18 +106,18 @@ __global__ __launch_bounds__(NT) void k_state_scan_plan(float *__restrict__ U,
     }
 }
 
-// The same recurrence with each element's chain of segments cut into 4 parts,
+// The same recurrence with each element's chain of segments cut into P parts,
 // one per wave, so that memory latency is paid about once: a wave loads all the
 // segments of its part at once (64 consecutive state elements of one key
 // channel: one 256-byte row per segment, and the decay as a wave-uniform value)
 // and folds them into its own (decay product, partial state); the parts' folds
 // are combined through LDS; each wave then writes its exclusive prefixes.
 // Workgroup: (sequence, 64-element slice of the state).
-template <int M>
-__global__ __launch_bounds__(NT) void k_scan_rows(float *__restrict__ U,
-                                                  const float *__restrict__ G, MfmaPlan pl,
-                                                  int dk, int dv) {
-    __shared__ float sA[4][64], sB[4][64];
+template <int M, int P>
+__global__ __launch_bounds__(64 * P) void k_scan_rows(float *__restrict__ U,
+                                                      const float *__restrict__ G, MfmaPlan pl,
+                                                      int dk, int dv) {
+    __shared__ float sA[P][64], sB[P][64];
     const int64_t dd = static_cast<int64_t>(dk) * dv;
     const uint32_t slices = static_cast<uint32_t>(dk * dv / 64);  // 32-bit: no long division
     const uint32_t seq32 = blockIdx.x / slices;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(NT) void k_scan_rows(float *__restrict__ U,
     const int64_t el = el0 + lane;
     const int c = static_cast<int>(el0 / static_cast<uint32_t>(dv));  // the slice's key channel
     const int64_t s0 = seg_id(seq * pl.N, pl), s1 = seg_id((seq + 1) * pl.N, pl);
-    const int64_t len = (s1 - s0 + 3) / 4;  // <= M (checked by the host)
+    const int64_t len = (s1 - s0 + P - 1) / P;  // <= M (checked by the host)
     const int64_t kb = s0 + part * len;
     const int n = static_cast<int>(kb < s1 ? (kb + len < s1 ? len : s1 - kb) : 0);
     float x[M], e[M];
@@ -219,10 +219,11 @@ hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_s
     const int64_t n_el = static_cast<int64_t>(n_seq) * dd;
     const int64_t most = (pl.N + pl.Q - 1) / pl.Q + 1;  // segments of one sequence, at most
     const dim3 rows_grid(static_cast<unsigned>(n_el / 64));
+    // four parts (more parts measured no faster at 16.4K tokens: 44 segments per sequence)
     if (most <= 4 * 16) {
-        hipLaunchKernelGGL((k_scan_rows<16>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);
+        hipLaunchKernelGGL((k_scan_rows<16, 4>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);
     } else if (most <= 4 * 32) {
-        hipLaunchKernelGGL((k_scan_rows<32>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);
+        hipLaunchKernelGGL((k_scan_rows<32, 4>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);
     } else {
         hipLaunchKernelGGL(k_state_scan_plan, dim3(static_cast<unsigned>(n_el / NT)), dim3(NT), 0,
                            s, U, G, pl, dk, dv);
