@@ -502,13 +502,16 @@ __global__ __launch_bounds__(NTB, 1) void k_bdo(BdArgs p) {
 struct TokIn {
     float4 g[2], dO[2];
     uint4 q, k, v;
+    int flag;  // the chunk's flag (same address in every lane)
 };
 struct StateIn {  // the chunk's reverse state, requested once the last is used
     float4 E[2];
 };
 
-__device__ __forceinline__ void request_tok(TokIn &in, const BgArgs &p, const int64_t *rows, int tid) {
+__device__ __forceinline__ void request_tok(TokIn &in, const BgArgs &p, const int64_t *rows,
+                                            int64_t chunk, int tid) {
     const GlaArgs &a = p.a;
+    in.flag = p.flags[chunk];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = tid + NTB * u, t = i >> 4, c = (i & 15) * 4;
@@ -583,7 +586,7 @@ __global__ __launch_bounds__(NTB, 1) void k_bgrad(BgArgs p) {
     __syncthreads();
     TokIn in;
     StateIn st_in;
-    request_tok(in, p, srow[0], tid);
+    request_tok(in, p, srow[0], c0, tid);
     request_state(st_in, p, ChunkAt(a, p.n_chunks, c0), tid);
 
     for (int64_t chk = c0; chk < c1; ++chk, buf ^= 1) {
@@ -593,9 +596,9 @@ __global__ __launch_bounds__(NTB, 1) void k_bgrad(BgArgs p) {
         const int64_t cn = chk + 1;  // next chunk of this workgroup (if below c1)
         if (at.n == 0) zero_state();  // a new sequence
 
-        const float tot = chunk_gates8(in.g, sA2, sG, sTot, nt, tid);
-        // the same decision as the epilogue kernel's (same inputs, same arithmetic)
-        const bool slow = __syncthreads_or(-tot > kSpanMax);  // uniform over the workgroup
+        chunk_gates8(in.g, sA2, sG, sTot, nt, tid);
+        const bool slow = in.flag != 0;  // the epilogue kernel's decision; uniform
+        __syncthreads();
 
         // ---- operands (rows past the chunk's end are zero); exact q and k kept
         uint4 qkeep, kkeep;
@@ -632,7 +635,7 @@ __global__ __launch_bounds__(NTB, 1) void k_bgrad(BgArgs p) {
         // ---- the next chunk's rows, then its per-token inputs (those registers are free)
         if (cn < c1 && tid < BC) srow[buf ^ 1][tid] = ChunkAt(a, p.n_chunks, cn).row(a, tid);
         __syncthreads();
-        if (cn < c1) request_tok(in, p, srow[buf ^ 1], tid);
+        if (cn < c1) request_tok(in, p, srow[buf ^ 1], cn, tid);
         if (slow) {  // the whole workgroup; its gradients come from the token-serial kernels
             if (cn < c1) request_state(st_in, p, ChunkAt(a, p.n_chunks, cn), tid);
             // the state after the chunk, as the epilogue kernel wrote it; waited for
