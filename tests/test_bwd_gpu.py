@@ -88,6 +88,8 @@ SHAPES = [
     (1, 1, 1, 2, 64, 64, "f16", 64),
     (1, 1, 70, 1, 64, 64, "bf16", 32),
     (1, 70, 1, 1, 64, 64, "f16", 16),
+    (2, 9, 13, 3, 64, 64, "bf16", 64),   # matrix path, two images
+    (1, 64, 64, 2, 64, 64, "f16", 32),   # matrix path, 128 chunks per sequence of one-chunk segments
 ]
 
 
