@@ -322,28 +322,49 @@ def time_backward(w, dev, hip, stream_ptr, steps, warmup):
         grads.append({k: torch.empty_like(s_[src]) for k, src in
                       (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dlog_g", "log_g"), ("dz", "z"),
                        ("drms_w", "rms_w"))})
+    # the forward's segment states of each set (gtr_gla_fwd_states), for the variant
+    # that takes them instead of recomputing
+    nbytes = lib.gtr_gla_states_bytes(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk,
+                                      W.DTYPE_CODE[w.dtype])
+    states = []
+    for s_ in sets if nbytes else []:
+        buf = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        out = torch.empty_like(s_["v"])
+        _lib.check(lib.gtr_gla_fwd_states(
+            s_["q"].data_ptr(), s_["k"].data_ptr(), s_["v"].data_ptr(), s_["log_g"].data_ptr(),
+            s_["z"].data_ptr(), s_["rms_w"].data_ptr(), out.data_ptr(), w.B, w.H, w.grid_h,
+            w.grid_w, w.dk, w.dv, 0, w.chunk, W.DTYPE_CODE[w.dtype], buf.data_ptr(), nbytes,
+            stream_ptr))
+        states.append(buf)
     torch.cuda.synchronize(dev)
 
-    def run(i, events=None, n_events=0, nl=None):
+    def run(i, events=None, n_events=0, nl=None, with_states=False):
         s_, g_ = sets[i % 2], grads[i % 2]
-        _lib.check(lib.gtr_gla_bwd(
+        st = states[i % 2] if with_states else None
+        _lib.check(lib.gtr_gla_bwd_states(
             s_["q"].data_ptr(), s_["k"].data_ptr(), s_["v"].data_ptr(), s_["log_g"].data_ptr(),
             s_["z"].data_ptr(), s_["rms_w"].data_ptr(), s_["dy"].data_ptr(), g_["dq"].data_ptr(),
             g_["dk"].data_ptr(), g_["dv"].data_ptr(), g_["dlog_g"].data_ptr(), g_["dz"].data_ptr(),
             g_["drms_w"].data_ptr(), w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, 0, w.chunk,
-            W.DTYPE_CODE[w.dtype], events, n_events, nl, stream_ptr))
+            W.DTYPE_CODE[w.dtype], None if st is None else st.data_ptr(),
+            0 if st is None else nbytes, events, n_events, nl, stream_ptr))
 
-    for i in range(warmup):
-        run(i)
-    torch.cuda.synchronize(dev)
-    ev = hip.events(2)
-    hip.record(ev[0], stream_ptr)
-    for i in range(steps):
-        run(i)
-    hip.record(ev[1], stream_ptr)
-    us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
-    torch.cuda.synchronize(dev)
-    hip.destroy(ev)
+    def timed(with_states):
+        for i in range(warmup):
+            run(i, with_states=with_states)
+        torch.cuda.synchronize(dev)
+        ev = hip.events(2)
+        hip.record(ev[0], stream_ptr)
+        for i in range(steps):
+            run(i, with_states=with_states)
+        hip.record(ev[1], stream_ptr)
+        t = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+        torch.cuda.synchronize(dev)
+        hip.destroy(ev)
+        return t
+
+    us = timed(False)
+    us_states = timed(True) if states else None
     evs = hip.events(16)
     nl = ctypes.c_int(0)
     per = []
@@ -352,9 +373,9 @@ def time_backward(w, dev, hip, stream_ptr, steps, warmup):
         torch.cuda.synchronize(dev)
         per.append([hip.elapsed_ms(evs[j], evs[j + 1]) * 1e3 for j in range(min(nl.value, 15))])
     hip.destroy(evs)
-    del sets, grads
+    del sets, grads, states
     torch.cuda.empty_cache()
-    return us, [statistics.fmean(p[j] for p in per) for j in range(len(per[0]))]
+    return us, [statistics.fmean(p[j] for p in per) for j in range(len(per[0]))], us_states
 
 
 def graph_time(lib, w, sets, n_sets, dev, direction, chunk, path, steps):
@@ -671,7 +692,7 @@ def main():
     backward = None
     if not args.no_extra:
         try:
-            bus, blaunch = time_backward(w, dev, hip, sp, max(10, args.steps // 4), 3)
+            bus, blaunch, bus_states = time_backward(w, dev, hip, sp, max(10, args.steps // 4), 3)
             s_io = W.DTYPE_BYTES[w.dtype]
             bbytes = w.tokens * w.H * ((2 * w.dk + 3 * w.dv) * s_io + 4 * w.dk      # reads
                                        + (2 * w.dk + 2 * w.dv) * s_io + 4 * w.dk)   # writes
@@ -689,7 +710,10 @@ def main():
                         "algorithmic_bytes": bbytes,
                         "hbm_frac": round(bbytes / (bus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                         "launch_us_mean": {n: round(t, 2) for n, t in zip(names_b, blaunch)}}
-            log(f"  backward: {bus:.1f} us/call, launches {['%.1f' % t for t in blaunch]}")
+            if bus_states is not None:  # given the forward's segment states (gtr_gla_bwd_states)
+                backward["us_per_call_with_forward_states"] = round(bus_states, 3)
+            log(f"  backward: {bus:.1f} us/call, launches {['%.1f' % t for t in blaunch]}, "
+                f"with forward states {bus_states}")
         except Exception as exc:  # report, do not hide
             backward = {"error": str(exc)[:300]}
     backbone = None

@@ -13,7 +13,8 @@ import torch
 from . import _lib
 from ._lib import (GtrError, PATH_AUTO, PATH_FAST, PATH_MFMA, PATH_SERIAL)  # noqa: F401
 
-__all__ = ["gla_fwd", "gla_stack_fwd", "gla_lowrank_fwd", "gla_bwd", "sswiglu_mix", "GtrError", "DIRECTIONS", "dtype_code", "version"]
+__all__ = ["gla_fwd", "gla_fwd_states", "gla_states_bytes", "gla_stack_fwd", "gla_lowrank_fwd",
+           "gla_bwd", "sswiglu_mix", "GtrError", "DIRECTIONS", "dtype_code", "version"]
 
 DIRECTIONS = {"LR": 0, "RL": 1, "TB": 2, "BT": 3}
 _DT = {torch.float32: _lib.GTR_F32, torch.float16: _lib.GTR_F16, torch.bfloat16: _lib.GTR_BF16}
@@ -78,6 +79,43 @@ def gla_fwd(q, k, v, log_g, z, rms_w, direction=0, chunk: int = 0, path: int = P
                                   int(path), _stream_ptr(dev))
     _lib.check(st)
     return out
+
+
+def gla_states_bytes(B, H, gh, gw, dk, dv, chunk, dtype) -> int:
+    """Bytes of the forward segment states of this shape (0: the shape has none)."""
+    return int(_lib.load().gtr_gla_states_bytes(B, H, gh, gw, dk, dv, int(chunk), dtype_code(dtype)))
+
+
+def gla_fwd_states(q, k, v, log_g, z, rms_w, direction=0, chunk: int = 0):
+    """``gla_fwd`` on the matrix-core path that also returns the forward segment states
+    (a float32 tensor) for ``gla_bwd(..., states=...)``.  Returns (out, states)."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    B, gh, gw, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or log_g.shape != q.shape or v.shape != (B, gh, gw, H, dv) or \
+            z.shape != v.shape or rms_w.shape != (dv,):
+        raise ValueError("shape mismatch")
+    if not (q.dtype == k.dtype == v.dtype == z.dtype):
+        raise TypeError("q, k, v, z must share one dtype")
+    if log_g.dtype != torch.float32 or rms_w.dtype != torch.float32:
+        raise TypeError("log_g and rms_w must be float32")
+    out = torch.empty_like(v)
+    _check_tensors((("q", q), ("k", k), ("v", v), ("log_g", log_g), ("z", z),
+                    ("rms_w", rms_w), ("out", out)), dev)
+    nbytes = gla_states_bytes(B, H, gh, gw, dk, dv, chunk, q.dtype)
+    if nbytes == 0:
+        raise ValueError("this shape has no forward states (16-bit I/O, dk = dv = 64, chunk 64)")
+    states = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        st = lib.gtr_gla_fwd_states(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_g.data_ptr(),
+                                    z.data_ptr(), rms_w.data_ptr(), out.data_ptr(), B, H, gh, gw,
+                                    dk, dv, _dir(direction), int(chunk), dtype_code(q.dtype),
+                                    states.data_ptr(), nbytes, _stream_ptr(dev))
+    _lib.check(st)
+    return out, states
 
 
 def gla_stack_fwd(q, k, v, log_g, z, rms_w, first_direction=0, chunk: int = 0, out=None):
@@ -184,8 +222,11 @@ def sswiglu_mix(u, w_conv, b_conv, out=None):
     return out
 
 
-def gla_bwd(q, k, v, log_g, z, rms_w, dout, direction=0, chunk: int = 0, events=None):
+def gla_bwd(q, k, v, log_g, z, rms_w, dout, direction=0, chunk: int = 0, events=None,
+            states=None):
     """Backward pass of ``gla_fwd`` (same inputs, no residual) given dout = dL/dout.
+    ``states``: the forward segment states from ``gla_fwd_states`` with the same inputs
+    and arguments (skips their recomputation), or None.
 
     Returns (grads, n_launches) with grads a dict of dq, dk, dv (I/O dtype), dlog_g
     (float32), dz (I/O dtype) and drms_w ([dv] float32)."""
@@ -204,6 +245,10 @@ def gla_bwd(q, k, v, log_g, z, rms_w, dout, direction=0, chunk: int = 0, events=
         raise TypeError("log_g and rms_w must be float32")
     _check_tensors((("q", q), ("k", k), ("v", v), ("log_g", log_g), ("z", z),
                     ("rms_w", rms_w), ("dout", dout)), dev)
+    if states is not None:
+        if states.dtype != torch.float32:
+            raise TypeError("states must be float32")
+        _check_tensors((("states", states),), dev)
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
          "dlog_g": torch.empty_like(log_g), "dz": torch.empty_like(z),
          "drms_w": torch.empty_like(rms_w)}
@@ -212,11 +257,13 @@ def gla_bwd(q, k, v, log_g, z, rms_w, dout, direction=0, chunk: int = 0, events=
     n_launch = ctypes.c_int(0)
     lib = _lib.load()
     with torch.cuda.device(dev):
-        st = lib.gtr_gla_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_g.data_ptr(),
-                             z.data_ptr(), rms_w.data_ptr(), dout.data_ptr(), g["dq"].data_ptr(),
-                             g["dk"].data_ptr(), g["dv"].data_ptr(), g["dlog_g"].data_ptr(),
-                             g["dz"].data_ptr(), g["drms_w"].data_ptr(), B, H, gh, gw, dk, dv,
-                             _dir(direction), int(chunk), dtype_code(q.dtype), ev_arr, n_ev,
-                             ctypes.byref(n_launch), _stream_ptr(dev))
+        st = lib.gtr_gla_bwd_states(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), log_g.data_ptr(), z.data_ptr(),
+            rms_w.data_ptr(), dout.data_ptr(), g["dq"].data_ptr(), g["dk"].data_ptr(),
+            g["dv"].data_ptr(), g["dlog_g"].data_ptr(), g["dz"].data_ptr(), g["drms_w"].data_ptr(),
+            B, H, gh, gw, dk, dv, _dir(direction), int(chunk), dtype_code(q.dtype),
+            None if states is None else states.data_ptr(),
+            0 if states is None else states.numel() * 4, ev_arr, n_ev, ctypes.byref(n_launch),
+            _stream_ptr(dev))
     _lib.check(st)
     return g, n_launch.value

@@ -17,8 +17,9 @@ GTR_F32, GTR_F16, GTR_BF16 = 0, 1, 2
 PATH_AUTO, PATH_MFMA, PATH_FAST, PATH_SERIAL = 0, 1, 2, 3
 
 EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_path", "gtr_gla_fwd_events", "gtr_gla_stack_fwd",
-           "gtr_gla_lowrank_fwd", "gtr_gla_bwd", "gtr_sswiglu_mix", "gtr_gla_auto_path", "gtr_last_error", "gtr_version", "gtr_release_workspace",
-           "gtr_set_segment_chunks")
+           "gtr_gla_lowrank_fwd", "gtr_gla_bwd", "gtr_gla_states_bytes", "gtr_gla_fwd_states",
+           "gtr_gla_bwd_states", "gtr_sswiglu_mix", "gtr_gla_auto_path", "gtr_last_error",
+           "gtr_version", "gtr_release_workspace", "gtr_set_segment_chunks")
 
 _lib = None
 
@@ -57,6 +58,16 @@ def load():
     lib.gtr_gla_bwd.argtypes = ([vp, vp, vp, fp, vp, fp, vp, vp, vp, vp, fp, vp, fp] + [i] * 9 +
                                 [ctypes.POINTER(ctypes.c_void_p), i, ctypes.POINTER(ctypes.c_int),
                                  vp])
+    lib.gtr_gla_states_bytes.restype = ctypes.c_size_t
+    lib.gtr_gla_states_bytes.argtypes = [i] * 8
+    lib.gtr_gla_fwd_states.restype = i
+    lib.gtr_gla_fwd_states.argtypes = ([vp, vp, vp, fp, vp, fp, vp] + [i] * 9 +
+                                       [fp, ctypes.c_size_t, vp])
+    lib.gtr_gla_bwd_states.restype = i
+    lib.gtr_gla_bwd_states.argtypes = ([vp, vp, vp, fp, vp, fp, vp, vp, vp, vp, fp, vp, fp] +
+                                       [i] * 9 + [fp, ctypes.c_size_t,
+                                                  ctypes.POINTER(ctypes.c_void_p), i,
+                                                  ctypes.POINTER(ctypes.c_int), vp])
     lib.gtr_sswiglu_mix.restype = i
     lib.gtr_sswiglu_mix.argtypes = [vp, fp, fp, vp] + [i] * 6 + [vp]
     lib.gtr_gla_auto_path.restype = i

@@ -194,18 +194,20 @@ gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk) {
     return GTR_OK;
 }
 
-gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk) {
+// states_out: where the segment states go (the caller's buffer of gtr_gla_fwd_states),
+// else the workspace
+gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk, float *states_out = nullptr) {
     MfmaPlan pl, po;
     mfma_plans(a, g_chunks_per_wg, &pl, &po);
     const int64_t n_seq = static_cast<int64_t>(a.B) * a.H;
     if (pl.n_wg > 0x7fffffff || n_seq * a.dk * a.dv > 0x7fffffff)
         return fail(GTR_ERR_UNSUPPORTED, "too many chunks");
-    const size_t ubytes = static_cast<size_t>(pl.n_seg) * a.dk * a.dv * 4;
+    const size_t ubytes = states_out ? 0 : static_cast<size_t>(pl.n_seg) * a.dk * a.dv * 4;
     const size_t gbytes = static_cast<size_t>(pl.n_seg) * a.dk * 4;
     void *ws = nullptr;
     gtr_status s = workspace(st, ubytes + gbytes, &ws);
     if (s != GTR_OK) return s;
-    float *U = static_cast<float *>(ws);
+    float *U = states_out ? states_out : static_cast<float *>(ws);
     float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
     hipError_t e = mk.start(st);
     if (e == hipSuccess) e = sum_supported(a) ? sum_launch(a, pl, U, G, st) : mfma_summary(a, pl, U, G, st);
@@ -365,6 +367,25 @@ gtr_status fwd_impl(const void *q, const void *k, const void *v, const float *lo
     return run(a, path, stream, mk);
 }
 
+// Forward segment states shared by gtr_gla_fwd_states and gtr_gla_bwd_states: the
+// shapes whose backward takes the matrix-core path with the segment summaries (16-bit
+// I/O, dk = dv = 64, chunk 64).  0 bytes where there are none.
+size_t states_bytes_of(const GlaArgs &a) {
+    if ((a.dtype != GTR_F16 && a.dtype != GTR_BF16) || a.dk != 64 || a.dv != 64 || a.chunk != 64 ||
+        !sum_supported(a) || !mfma_supported(a))
+        return 0;
+    MfmaPlan pl, po;
+    mfma_plans(a, g_chunks_per_wg, &pl, &po);
+    return static_cast<size_t>(pl.n_seg) * a.dk * a.dv * 4;
+}
+
+GlaArgs shape_args(int B, int H, int gh, int gw, int dk, int dv, int direction, int chunk,
+                   int dtype) {
+    return GlaArgs{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H,
+                   gh, gw, dk, dv, direction, chunk ? chunk : kDefaultChunk, dtype,
+                   static_cast<int64_t>(gh) * gw};
+}
+
 }  // namespace
 
 extern "C" {
@@ -401,6 +422,43 @@ gtr_status gtr_gla_fwd_events(const void *q, const void *k, const void *v, const
                             dv, direction, chunk, dtype, path, stream, mk);
     if (n_launches) *n_launches = mk.launches;
     return s;
+}
+
+size_t gtr_gla_states_bytes(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
+                            gtr_dtype dtype) {
+    if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0) return 0;
+    return states_bytes_of(shape_args(B, H, grid_h, grid_w, dk, dv, 0, chunk, dtype));
+}
+
+gtr_status gtr_gla_fwd_states(const void *q, const void *k, const void *v, const float *log_g,
+                              const void *z, const float *rms_w, void *out, int B, int H,
+                              int grid_h, int grid_w, int dk, int dv, int direction, int chunk,
+                              gtr_dtype dtype, float *states, size_t states_bytes,
+                              hipStream_t stream) {
+    g_err.clear();
+    gtr_status s = check(q, k, v, log_g, z, rms_w, out, B, H, grid_h, grid_w, dk, dv, direction,
+                         chunk, dtype, GTR_PATH_MFMA);
+    if (s != GTR_OK) return s;
+    if (!states) return fail(GTR_ERR_ARG, "null states pointer");
+    GlaArgs a{q, k, v, log_g, z, rms_w, out, nullptr, B, H, grid_h, grid_w, dk, dv, direction,
+              chunk ? chunk : kDefaultChunk, dtype, static_cast<int64_t>(grid_h) * grid_w};
+    const size_t need = states_bytes_of(a);
+    if (need == 0)
+        return fail(GTR_ERR_UNSUPPORTED,
+                    "forward states need 16-bit I/O, dk = dv = 64 and chunk 64");
+    if (states_bytes < need)
+        return fail(GTR_ERR_ARG, "states buffer of %zu bytes, need %zu", states_bytes, need);
+    const size_t rows = static_cast<size_t>(B) * grid_h * grid_w * H;
+    const size_t eb = elem_bytes(dtype);
+    const void *ins[] = {q, k, v, log_g, z, rms_w, out};
+    const size_t nb[] = {rows * dk * eb, rows * dk * eb, rows * dv * eb, rows * dk * 4,
+                         rows * dv * eb, static_cast<size_t>(dv) * 4, rows * dv * eb};
+    s = check_aliasing(out, rows * dv * eb, ins, nb, 6);
+    if (s == GTR_OK) s = check_aliasing(states, need, ins, nb, 7);
+    if (s != GTR_OK) return s;
+    if (!device_ok()) return GTR_ERR_HIP;
+    Marks mk;
+    return run_mfma(a, stream, mk, states);
 }
 
 gtr_status gtr_gla_stack_fwd(const void *q, const void *k, const void *v, const float *log_g,
@@ -488,6 +546,18 @@ gtr_status gtr_gla_bwd(const void *q, const void *k, const void *v, const float 
                        int grid_h, int grid_w, int dk_, int dv_, int direction, int chunk,
                        gtr_dtype dtype, hipEvent_t *events, int n_events, int *n_launches,
                        hipStream_t stream) {
+    return gtr_gla_bwd_states(q, k, v, log_g, z, rms_w, dout, dq, dk, dv, dlog_g, dz, drms_w, B, H,
+                              grid_h, grid_w, dk_, dv_, direction, chunk, dtype, nullptr, 0, events,
+                              n_events, n_launches, stream);
+}
+
+gtr_status gtr_gla_bwd_states(const void *q, const void *k, const void *v, const float *log_g,
+                              const void *z, const float *rms_w, const void *dout, void *dq,
+                              void *dk, void *dv, float *dlog_g, void *dz, float *drms_w, int B,
+                              int H, int grid_h, int grid_w, int dk_, int dv_, int direction,
+                              int chunk, gtr_dtype dtype, const float *states,
+                              size_t states_bytes, hipEvent_t *events, int n_events,
+                              int *n_launches, hipStream_t stream) {
     g_err.clear();
     if (n_launches) *n_launches = 0;
     if (n_events < 0 || (n_events > 0 && !events))
@@ -512,10 +582,23 @@ gtr_status gtr_gla_bwd(const void *q, const void *k, const void *v, const float 
             if (a0 < o1 && o0 < a1) return fail(GTR_ERR_ARG, "gradient %d overlaps buffer %d", o - 7, i);
         }
     }
-    if (!device_ok()) return GTR_ERR_HIP;
     GlaArgs a{q, k, v, log_g, z, rms_w, nullptr, nullptr, B, H, grid_h, grid_w, dk_, dv_,
               direction, chunk ? chunk : kDefaultChunk, dtype,
               static_cast<int64_t>(grid_h) * grid_w};
+    if (states) {  // the forward's segment states (gtr_gla_fwd_states with the same arguments)
+        const size_t need = states_bytes_of(a);
+        if (need == 0)
+            return fail(GTR_ERR_UNSUPPORTED,
+                        "forward states need 16-bit I/O, dk = dv = 64 and chunk 64");
+        if (states_bytes < need)
+            return fail(GTR_ERR_ARG, "states buffer of %zu bytes, need %zu", states_bytes, need);
+        for (int o = 7; o < 13; ++o) {
+            const char *a0 = reinterpret_cast<const char *>(states), *a1 = a0 + need;
+            const char *o0 = static_cast<const char *>(bufs[o]), *o1 = o0 + nb[o];
+            if (a0 < o1 && o0 < a1) return fail(GTR_ERR_ARG, "gradient %d overlaps the states", o - 7);
+        }
+    }
+    if (!device_ok()) return GTR_ERR_HIP;
     const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
     if (static_cast<int64_t>(B) * H * n_chunks > 0x7fffffff)
         return fail(GTR_ERR_UNSUPPORTED, "too many chunks");
@@ -534,7 +617,7 @@ gtr_status gtr_gla_bwd(const void *q, const void *k, const void *v, const float 
     hipError_t e = mk.start(stream);
     if (e == hipSuccess)
         e = bwd_launch(a, dout, dq, dk, dv, dlog_g, dz, drms_w, ws, static_cast<unsigned *>(ctr),
-                       static_cast<int>(n_chunks), stream, hooks);
+                       static_cast<int>(n_chunks), g_chunks_per_wg, states, stream, hooks);
     if (n_launches) *n_launches = mk.launches;
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return GTR_OK;

@@ -212,8 +212,9 @@ hipError_t bgrad_launch(const GlaArgs &a, const MfmaPlan &pl, int64_t R, const f
                         const float *Sseg, const float *Sx, const float *Er, void *dq, void *dk,
                         void *dv, float *dlog_g, const int *flags, int n_chunks, hipStream_t s);
 hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
-                      float *dlog_g, void *dz, float *drms_w, void *ws, unsigned *ctr, int n_chunks,
-                      hipStream_t st, const BwdLaunchHooks &hooks);
+                      float *dlog_g, void *dz, float *drms_w, void *ws, unsigned *ctr,
+                      int n_chunks, int64_t chunks_per_wg, const float *fwd_states, hipStream_t st,
+                      const BwdLaunchHooks &hooks);
 // State scan over the segments of a plan, in place: U[k] <- state before segment k.
 hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_seq, int dk,
                            int dv, hipStream_t s);

@@ -779,7 +779,8 @@ size_t bwd_workspace_bytes(const GlaArgs &a, int n_chunks) {
 
 hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void *dv,
                       float *dlog_g, void *dz, float *drms_w, void *ws, unsigned *ctr,
-                      int n_chunks, hipStream_t st, const BwdLaunchHooks &hooks) {
+                      int n_chunks, int64_t chunks_per_wg, const float *fwd_states, hipStream_t st,
+                      const BwdLaunchHooks &hooks) {
     const size_t ncb = static_cast<size_t>(a.B) * a.H * n_chunks;
     const size_t rows = static_cast<size_t>(a.B) * a.L * a.H;
     const size_t dd = static_cast<size_t>(a.dk) * a.dv;
@@ -801,27 +802,32 @@ hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void
     // through each segment and writes every chunk's.  fp32 path: per-chunk
     // summaries and scan.
     MfmaPlan ps{};
-    hipError_t e;
+    hipError_t e = hipSuccess;
     if (mfma) {
         const bool msum = sum_supported(a) && !a.feat && !a.resid && al16(a.k) && al16(a.v) &&
                           al16(a.log_g);
         if (msum) {
             MfmaPlan po;
-            mfma_plans(a, 0, &ps, &po);
-            e = sum_launch(a, ps, Useg, Gseg, st);
+            mfma_plans(a, chunks_per_wg, &ps, &po);  // the forward's segments
         } else {
             ps = mfma_plan(a, 1);
-            e = serial_summary(a, Useg, Gseg, n_chunks, st);
         }
-        if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
-        e = msum ? state_scan_plan(Useg, Gseg, ps, static_cast<int>(a.B * a.H), a.dk, a.dv, st)
-                 : state_scan(Useg, Gseg, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st);
+        if (msum && fwd_states) {
+            // the forward's segment states, given (gtr_gla_fwd_states): two launches fewer
+            Useg = const_cast<float *>(fwd_states);
+        } else {
+            e = msum ? sum_launch(a, ps, Useg, Gseg, st) : serial_summary(a, Useg, Gseg, n_chunks, st);
+            if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+            e = msum ? state_scan_plan(Useg, Gseg, ps, static_cast<int>(a.B * a.H), a.dk, a.dv, st)
+                     : state_scan(Useg, Gseg, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st);
+            if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
+        }
     } else {
         e = serial_summary(a, Uf, Gf, n_chunks, st);
         if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
         e = state_scan(Uf, Gf, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st);
+        if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
     }
-    if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
     BwdArgs p{a, dy, Uf, nullptr, dO, qdq, Ur, Gr, Tn, dWp, dq, dk, dv, dz, dlog_g, drms_w,
               nullptr, n_chunks, part2, ctr};
     switch (a.dtype) {

@@ -186,6 +186,48 @@ gtr_status gtr_gla_bwd(const void *q, const void *k, const void *v, const float 
                        int *n_launches, hipStream_t stream);
 
 /*
+ * Forward states kept for the backward (GTR write-up "端侧实时感知新标杆！通用线性骨干网络GTR开源",
+ * Method §4: the chunk summaries and the boundary-state scan, whose result is
+ * the state entering each piece of the scan).  A forward call on the
+ * matrix-core path can leave the incoming state of every segment (run of
+ * chunks one workgroup summarises) in a caller buffer; a backward call with the
+ * same inputs and arguments then takes them instead of recomputing them.
+ *
+ * gtr_gla_states_bytes: the buffer size for this shape, or 0 where the shape
+ * has no such states (they exist for 16-bit I/O with dk = dv = 64 and chunk 64
+ * or 0).  Pure host computation; the size depends on gtr_set_segment_chunks,
+ * which must not change between the two calls.
+ *
+ * gtr_gla_fwd_states: gtr_gla_fwd on the matrix-core path that also writes the
+ * segment states, float32 [segment][dk][dv], to `states` (device memory owned
+ * by the caller, states_bytes >= gtr_gla_states_bytes(...), overlapping no
+ * other buffer).  out is bit for bit gtr_gla_fwd's on that path.
+ * GTR_ERR_UNSUPPORTED for other shapes; GTR_ERR_ARG for a null or short buffer;
+ * otherwise errors as gtr_gla_fwd.
+ *
+ * gtr_gla_bwd_states: gtr_gla_bwd given those states (NULL: recomputed, as
+ * gtr_gla_bwd).  The states must come from gtr_gla_fwd_states with the same q,
+ * k, v, log_g, shape, direction, chunk and dtype; the library cannot check
+ * their content.  Where the backward does not take the matrix-core path (the
+ * gradient or input pointers not 16-byte aligned) they are not used.  The
+ * gradients are bit for bit gtr_gla_bwd's; two launches fewer.
+ */
+size_t gtr_gla_states_bytes(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
+                            gtr_dtype dtype);
+gtr_status gtr_gla_fwd_states(const void *q, const void *k, const void *v, const float *log_g,
+                              const void *z, const float *rms_w, void *out, int B, int H,
+                              int grid_h, int grid_w, int dk, int dv, int direction, int chunk,
+                              gtr_dtype dtype, float *states, size_t states_bytes,
+                              hipStream_t stream);
+gtr_status gtr_gla_bwd_states(const void *q, const void *k, const void *v, const float *log_g,
+                              const void *z, const float *rms_w, const void *dout, void *dq,
+                              void *dk, void *dv, float *dlog_g, void *dz, float *drms_w, int B,
+                              int H, int grid_h, int grid_w, int dk_, int dv_, int direction,
+                              int chunk, gtr_dtype dtype, const float *states,
+                              size_t states_bytes, hipEvent_t *events, int n_events,
+                              int *n_launches, hipStream_t stream);
+
+/*
  * The fused middle of the Spatial SwiGLU feed-forward block (GTR write-up
  * "端侧实时感知新标杆！通用线性骨干网络GTR开源", Method §2 "Spatial SwiGLU": in the
  * channel expansion the value branch is reshaped to the 2-D token grid and

@@ -183,6 +183,42 @@ def test_sswiglu_null_misaligned_and_aliasing():
     assert _sswiglu(ptrs=p) == _lib.GTR_ERR_ARG and "overlaps" in _lib.last_error()
 
 
+def test_states_sizes():
+    """Forward segment states exist for 16-bit I/O at dk = dv = 64, chunk 64: one
+    dk x dv float32 state per segment.  16.4K tokens, 12 heads: 3072 chunks in ranges of 6
+    (512 starts), plus the 12 sequence starts, less the 4 starts both share = 520 segments."""
+    lib = _lib.load()
+    assert lib.gtr_gla_states_bytes(1, 12, 128, 128, 64, 64, 64, _lib.GTR_F16) == 520 * 64 * 64 * 4
+    assert lib.gtr_gla_states_bytes(1, 12, 128, 128, 64, 64, 0, _lib.GTR_BF16) == 520 * 64 * 64 * 4
+    for args in ((1, 12, 128, 128, 64, 64, 64, _lib.GTR_F32), (1, 12, 128, 128, 64, 128, 64, _lib.GTR_F16),
+                 (1, 12, 128, 128, 64, 64, 32, _lib.GTR_F16), (0, 12, 128, 128, 64, 64, 64, _lib.GTR_F16)):
+        assert lib.gtr_gla_states_bytes(*args) == 0, args
+
+
+def test_states_argument_errors():
+    lib = _lib.load()
+    need = lib.gtr_gla_states_bytes(1, 2, 8, 8, 64, 64, 64, _lib.GTR_F16)
+    assert need > 0
+    S = 9 << 36
+    # forward: null or short buffer, unsupported shape, buffer on top of an input
+    st = lib.gtr_gla_fwd_states(*P, 1, 2, 8, 8, 64, 64, 0, 0, 1, None, need, None)
+    assert st == _lib.GTR_ERR_ARG and "null states" in _lib.last_error()
+    st = lib.gtr_gla_fwd_states(*P, 1, 2, 8, 8, 64, 64, 0, 0, 1, S, need - 4, None)
+    assert st == _lib.GTR_ERR_ARG and "states buffer" in _lib.last_error()
+    st = lib.gtr_gla_fwd_states(*P, 1, 2, 8, 8, 64, 64, 0, 32, 1, S, need, None)
+    assert st == _lib.GTR_ERR_UNSUPPORTED
+    st = lib.gtr_gla_fwd_states(*P, 1, 2, 8, 8, 64, 64, 0, 0, 1, P[2], need, None)
+    assert st == _lib.GTR_ERR_ARG and "overlap" in _lib.last_error()
+    # backward: short buffer, unsupported shape, a gradient on top of the states
+    P13 = [(i + 1) << 36 for i in range(13)]
+    st = lib.gtr_gla_bwd_states(*P13, 1, 2, 8, 8, 64, 64, 0, 0, 1, S, need - 4, None, 0, None, None)
+    assert st == _lib.GTR_ERR_ARG and "states buffer" in _lib.last_error()
+    st = lib.gtr_gla_bwd_states(*P13, 1, 2, 8, 8, 64, 64, 0, 0, 0, S, need, None, 0, None, None)
+    assert st == _lib.GTR_ERR_UNSUPPORTED
+    st = lib.gtr_gla_bwd_states(*P13, 1, 2, 8, 8, 64, 64, 0, 0, 1, P13[8], need, None, 0, None, None)
+    assert st == _lib.GTR_ERR_ARG and "overlaps the states" in _lib.last_error()
+
+
 def test_bwd_argument_errors():
     lib = _lib.load()
     P13 = [(i + 1) << 36 for i in range(13)]
