@@ -108,6 +108,15 @@ def test_bwd_directions(oracle_mod, direction):
     _run_case(oracle_mod, x, "f32", direction, chunk=16, seed=direction)
 
 
+@pytest.mark.parametrize("direction", [0, 1, 2, 3])
+def test_bwd_matrix_path_directions(oracle_mod, direction):
+    """The matrix-core path in every scan order (fp16, 24 x 20 grid: 8 chunks per
+    sequence with a 32-token tail)."""
+    x = W.make_custom(1, 24, 20, 2, 64, 64, "f16", seed=50 + direction)
+    _note(f"bwd matrix path direction {direction}")
+    _run_case(oracle_mod, x, "f16", direction, chunk=64, seed=20 + direction)
+
+
 @pytest.mark.parametrize("log_g", [0.0, -1e-4, -3.0])
 def test_bwd_extreme_gates(oracle_mod, log_g):
     x = W.make_custom(1, 8, 12, 2, 64, 64, "f32", seed=7, log_g_const=log_g)
