@@ -409,37 +409,50 @@ def graph_time(lib, w, sets, n_sets, dev, direction, chunk, path, steps):
 
 
 # ----------------------------------------------------------- CPU baseline --
-def cpu_baseline(w: W.Workload, x: dict, target_s: float = 12.0):
+def cpu_baseline(w: W.Workload, x: dict, target_s: float = 12.0, single_s: float = 4.0):
     """The fp64 oracle (test infrastructure, untuned) on a bounded sample of the
-    same workload: whole calls repeated for about target_s seconds, or, when one
-    call would take longer, the first (batch, head) sequences that fit."""
+    same workload, on every host thread and on one: whole calls repeated for about
+    target_s seconds (at least three), or, when one call would take longer, the
+    first (batch, head) sequences that fit, run three times; the median run is
+    reported.  The one-thread figure samples fewer sequences (single_s seconds)."""
     import oracle
     oracle.build(force=False)
     f = {key: W.io_to_f64(x[key], w.dtype) for key in ("q", "k", "v", "z")}
     lg = x["log_g"].astype(np.float64)
     rw = x["rms_w"].astype(np.float64)
     n_seq = w.B * w.H
-    t0 = time.perf_counter()
-    oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0, bh=[0])
-    t_one = time.perf_counter() - t0
-    if t_one * n_seq <= target_s:
-        reps, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < target_s:
-            oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0)
-            reps += 1
-        dt = time.perf_counter() - t0
-        per_call = dt / reps
-        sample = f"{reps} whole calls of {w.name} (LR scan), {dt:.1f} s"
-    else:
-        n = max(1, int(target_s / t_one))
+
+    def one(bh):
         t0 = time.perf_counter()
-        oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0, bh=list(range(n)))
-        dt = time.perf_counter() - t0
-        per_call = dt / n * n_seq
-        sample = (f"{n} of {n_seq} (batch, head) sequences of {w.name} (LR scan), {dt:.1f} s, "
-                  f"scaled to the whole call")
-    return {"value": w.tokens / per_call, "unit": "tokens/s", "cores": oracle.threads(),
-            "kind": "oracle", "sample": sample, "us_per_call": per_call * 1e6}
+        oracle.fwd(f["q"], f["k"], f["v"], lg, f["z"], rw, 0, bh=bh)
+        return time.perf_counter() - t0
+
+    def measure(budget_s):
+        t_one = one([0])
+        if t_one * n_seq * 3 <= budget_s:  # whole calls
+            times = []
+            t0 = time.perf_counter()
+            while len(times) < 3 or time.perf_counter() - t0 < budget_s:
+                times.append(one(None))
+            per_call = statistics.median(times)
+            return per_call, f"{len(times)} whole calls of {w.name} (LR scan), median"
+        n = max(1, min(n_seq, int(budget_s / 3 / t_one)))
+        times = [one(list(range(n))) for _ in range(3)]
+        per_call = statistics.median(times) / n * n_seq
+        return per_call, (f"{n} of {n_seq} (batch, head) sequences of {w.name} (LR scan), "
+                          f"median of 3 runs, scaled to the whole call")
+
+    all_threads = oracle.threads()
+    per_call, sample = measure(target_s)
+    oracle.set_threads(1)
+    try:
+        per_one, sample_one = measure(single_s)
+    finally:
+        oracle.set_threads(all_threads)
+    return {"value": w.tokens / per_call, "unit": "tokens/s", "cores": all_threads,
+            "kind": "oracle", "sample": sample, "us_per_call": per_call * 1e6,
+            "single_thread": {"value": w.tokens / per_one, "unit": "tokens/s", "cores": 1,
+                              "sample": sample_one, "us_per_call": per_one * 1e6}}
 
 
 # --------------------------------------------------------------- roofline --

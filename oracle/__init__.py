@@ -67,12 +67,19 @@ def _load():
         lib.gtr_oracle_fwd.argtypes = [dp] * 7 + [ctypes.c_int] * 7 + [
             ctypes.c_double, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
         lib.gtr_oracle_threads.restype = ctypes.c_int
+        lib.gtr_oracle_set_threads.restype = None
+        lib.gtr_oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
 
 def threads() -> int:
     return _load().gtr_oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of later oracle calls (the OpenMP runtime's setting)."""
+    _load().gtr_oracle_set_threads(int(n))
 
 
 def _f64(a):

@@ -161,3 +161,14 @@ int gtr_oracle_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the threads of later calls (timing at one thread and at all of them). */
+void gtr_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
