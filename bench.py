@@ -273,6 +273,44 @@ def time_sswiglu(ws, dev, hip, stream_ptr, steps, warmup):
     return {"us_per_call": us, "n_sets": n_sets}
 
 
+def time_stack(dev, hip, stream_ptr, steps, warmup):
+    """gtr_gla_stack_fwd on the 12-block stack workload (B = 8, 64 x 64, H = 12, dk = 64,
+    dv = 128, bf16).  Inputs are drawn on the device from a seeded generator with the
+    workload's distributions (~6 GB; parity of this configuration is tested on host-drawn
+    inputs): q, k, v, z ~ N(0, 1)/8, log_g = logsigmoid(N(0, 1))/16, rms_w ~ 1 + 0.1 N(0, 1)."""
+    w = W.WORKLOADS["stack_1024"]
+    nb = w.n_blocks
+    gen = torch.Generator(device=dev).manual_seed(1000 * w.wid)
+    qk = (nb, w.B, w.grid_h, w.grid_w, w.H, w.dk)
+    vz = (nb, w.B, w.grid_h, w.grid_w, w.H, w.dv)
+
+    def io(shape):
+        return (torch.randn(shape, generator=gen, device=dev) * w.scale).to(torch.bfloat16)
+
+    q, k, v, z = io(qk), io(qk), io(vz), io(vz)
+    log_g = torch.nn.functional.logsigmoid(torch.randn(qk, generator=gen, device=dev)) / 16.0
+    rms_w = 1.0 + 0.1 * torch.randn((nb, w.dv), generator=gen, device=dev)
+    out = torch.empty_like(v)
+    torch.cuda.synchronize(dev)
+    for _ in range(warmup):
+        g.gla_stack_fwd(q, k, v, log_g, z, rms_w, 0, w.chunk, out=out)
+    torch.cuda.synchronize(dev)
+    ev = hip.events(2)
+    hip.record(ev[0], stream_ptr)
+    for _ in range(steps):
+        g.gla_stack_fwd(q, k, v, log_g, z, rms_w, 0, w.chunk, out=out)
+    hip.record(ev[1], stream_ptr)
+    ms = hip.elapsed_ms(ev[0], ev[1]) / steps
+    torch.cuda.synchronize(dev)
+    hip.destroy(ev)
+    th = w.B * w.L * w.H
+    per_th = (2 * w.dk + 3 * w.dv) * 2 + 4 * w.dk  # 16-bit I/O
+    nbytes = th * per_th * nb + th * w.dv * 2 * (nb - 1)  # + the residual read of blocks 1..
+    del q, k, v, z, log_g, rms_w, out
+    torch.cuda.empty_cache()
+    return w, ms, nbytes
+
+
 def time_backbone(dev, steps):
     """12-block random-weight backbone at 640 x 640, batch 1: eager and HIP-graph replay."""
     from gated_token_recurrence_amd import backbone as bb
@@ -742,6 +780,20 @@ def main():
             log(f"  backbone: graph {graph_ms:.3f} ms, eager {eager_ms:.3f} ms per image")
         except Exception as exc:  # report, do not hide
             backbone = {"error": str(exc)[:300]}
+    stack = None
+    if not args.no_extra:
+        try:
+            ws, ms, sbytes = time_stack(dev, hip, sp, 5, 2)
+            stack = {"workload": f"{ws.name}: {ws.n_blocks}-block stack, B = {ws.B}, grid "
+                                 f"{ws.grid_h}x{ws.grid_w}, H = {ws.H}, dk = {ws.dk}, dv = {ws.dv}, "
+                                 f"{ws.dtype}, inputs drawn on the device",
+                     "ms_per_stack": round(ms, 4),
+                     "us_per_block": round(ms * 1e3 / ws.n_blocks, 2),
+                     "algorithmic_bytes": sbytes,
+                     "hbm_frac": round(sbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"  stack: {ms:.3f} ms ({ms * 1e3 / ws.n_blocks:.1f} us per block)")
+        except Exception as exc:  # report, do not hide
+            stack = {"error": str(exc)[:300]}
     cpu = None
     if not args.no_cpu:
         log("  timing the fp64 oracle on the host (bounded sample)")
@@ -780,6 +832,7 @@ def main():
         "lowrank_gate": lowrank,
         "sswiglu_mix": sswiglu,
         "backbone_640": backbone,
+        "stack_1024": stack,
         "backward": backward,
     }
     print(json.dumps(line), flush=True)

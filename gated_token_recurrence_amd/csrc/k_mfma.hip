@@ -169,7 +169,10 @@ void mfma_plans(const GlaArgs &a, int64_t chunks_per_wg, MfmaPlan *ps, MfmaPlan 
     if (chunks_per_wg <= 0) {
         const int64_t t1 = kSummaryWorkgroups < T ? kSummaryWorkgroups : T;
         q1 = (T + t1 - 1) / t1;
-        const int64_t t2 = kMfmaWorkgroups < T ? kMfmaWorkgroups : T;
+        // dv = 128 output workgroups take a whole CU (eight waves, or four at one wave
+        // per SIMD): one per CU
+        const int64_t most = a.dv == 128 ? kMfmaWorkgroups / 2 : kMfmaWorkgroups;
+        const int64_t t2 = most < T ? most : T;
         const int64_t want = (T + t2 - 1) / t2;
         const int64_t m = (want + q1 / 2) / q1;
         q2 = q1 * (m > 1 ? m : 1);

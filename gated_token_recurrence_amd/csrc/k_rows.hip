@@ -66,11 +66,15 @@ __device__ __forceinline__ int dcol(int dd, int m) { return colB(dd, m >> 2) + (
 template <int DT, int DV, bool RES, bool LRG>
 struct RowTile {
     static constexpr int C = 64, NB = 4;
+    static constexpr int CS = DV / 64;  // value halves (dv = 128: two groups of four waves)
+    static constexpr int NW = 4 * CS;   // waves
+    static constexpr int NTH = 64 * NW; // threads
     static constexpr int ND = DV / 16;  // value tiles
-    static constexpr int NS = ND / 4;   // state tiles per wave
+    static constexpr int NDW = 4;       // value tiles of a wave's outputs (its half)
+    static constexpr int NS = ND / NW;  // state tiles per wave (one)
     static constexpr int VP = DV / 64;  // 64-column planes of V
     static constexpr int NV = (DT == DT_F16) ? 2 : 1;  // V as bf16 hi (+ lo for fp16)
-    static constexpr int NE = DV / 32;  // 16-byte value pieces per lane (epilogue, V loads)
+    static constexpr int NE = 2;        // 16-byte value pieces per lane of its half (epilogue, V loads)
     static constexpr int MAT = C * 64;
     // LDS carve-up (bytes).  Token-serial chunks reuse K (raw q, k) and S (fp32
     // gates, then the output exchange).
@@ -78,18 +82,19 @@ struct RowTile {
     static constexpr int O_V = O_K + 2 * MAT * 2;           // V [part][plane][64][64]
     static constexpr int O_S = O_V + NV * VP * MAT * 2;     // S^T hi, lo [2][DV][64]
     static constexpr int O_TOT = O_S + 2 * DV * 64 * 2;     // float [NB][DK]
-    static constexpr int O_TAB = O_TOT + NB * DK * 4;       // float [4 waves][2][DK]
-    static constexpr int O_RW = O_TAB + 4 * 2 * DK * 4;     // float [DV]
-    static constexpr int O_GATE = O_RW + DV * 4;            // low-rank gate weights (LRG)
+    static constexpr int O_TAB = O_TOT + NB * DK * 4;       // float [NW waves][2][DK]
+    static constexpr int O_RW = O_TAB + NW * 2 * DK * 4;    // float [DV]
+    static constexpr int O_SS = O_RW + DV * 4;              // float [CS][C]: halves' sums of squares
+    static constexpr int O_GATE = O_SS + CS * C * 4;        // low-rank gate weights (LRG)
     static constexpr int BYTES = O_GATE + (LRG ? LowRankGate<DT>::LDS_BYTES : 0);
     static_assert(C * DK * 4 <= 2 * DV * 64 * 2, "fp32 gates must fit the state area");
     static_assert(ND * 4 * 64 * 16 <= 2 * DV * 64 * 2, "output exchange must fit the state area");
 
     GlaArgs a;
     uint16_t *sK, *sV, *sS;
-    float *sTot, *sTab, *sRw;
+    float *sTot, *sTab, *sRw, *sSS;
     char *sGate;
-    int w, l, lr, g;
+    int w, tw, hv, l, lr, g;  // wave, its token rows [16 tw, 16 tw + 16), its value half
 
     // this lane's token: rows (negative = past the end, ~row of the last token) and
     // token indices b L + grid position (of the row read)
@@ -101,9 +106,9 @@ struct RowTile {
     uint2 pf;
     float cs[16];
     // state tiles (S[s][ct][r] = S[16 ct + 4 g + r][dcol(NS w + s, lr)]) and the
-    // output tiles of this wave's tokens (O[dd][r] = O^T[dcol(dd, 4 g + r)][token lr])
+    // output tiles of this wave's tokens in its half (O[e][r] = O^T[dcol(NDW hv + e, 4 g + r)][token lr])
     f32x4 S[NS][4];
-    f32x4 O[ND];
+    f32x4 O[NDW];
     s16x8 qh[2], ql[2];  // Q~ of this wave's tokens, B-operand layout
 
     __device__ __forceinline__ void init(const GlaArgs &args, char *smem) {
@@ -113,9 +118,12 @@ struct RowTile {
         sS = reinterpret_cast<uint16_t *>(smem + O_S);
         sTot = reinterpret_cast<float *>(smem + O_TOT);
         sRw = reinterpret_cast<float *>(smem + O_RW);
+        sSS = reinterpret_cast<float *>(smem + O_SS);
         sGate = smem + O_GATE;
         const int tid = threadIdx.x;
         w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        tw = CS == 1 ? w : w & 3;
+        hv = CS == 1 ? 0 : w >> 2;
         l = tid & 63;
         lr = l & 15;
         g = l >> 4;
@@ -129,7 +137,7 @@ struct RowTile {
     // and the state after the sequence's last chunk, which is never used).
     __device__ __forceinline__ int64_t row_of(uint32_t b, uint32_t h, int64_t ch, int64_t &tok) const {
         const uint32_t L32 = static_cast<uint32_t>(a.L);
-        const uint32_t t0 = static_cast<uint32_t>(ch) * C + 16 * w + lr;
+        const uint32_t t0 = static_cast<uint32_t>(ch) * C + 16 * tw + lr;
         uint32_t t = t0 < L32 ? t0 : L32 - 1;
         if (a.direction & 1) t = L32 - 1 - t;  // RL, BT: reversed sequence
         uint32_t pos = t;
@@ -159,7 +167,7 @@ struct RowTile {
         }
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-            const int d0 = 32 * e + 8 * g;
+            const int d0 = 64 * hv + 32 * e + 8 * g;
             pv[e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + row * DV + d0);
             if constexpr (RES)
                 pr[e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.resid) + row * DV + d0);
@@ -181,7 +189,7 @@ struct RowTile {
 #pragma unroll
         for (int e = 0; e < NE; ++e)
             pz[e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.z) + row * DV +
-                                                     32 * e + 8 * g);
+                                                     64 * hv + 32 * e + 8 * g);
     }
 
     // incoming state (fp32 [DK][DV]) of the owned tiles
@@ -233,20 +241,20 @@ struct RowTile {
             }
         }
         row_scan(cs);
-        if (lr == 15) {
+        if (lr == 15 && hv == 0) {
 #pragma unroll
             for (int kap = 0; kap < 2; ++kap) {
-                float *dst = sTot + w * DK + 32 * kap + 8 * g;
+                float *dst = sTot + tw * DK + 32 * kap + 8 * g;
                 *reinterpret_cast<float4 *>(dst) =
                     make_float4(cs[8 * kap], cs[8 * kap + 1], cs[8 * kap + 2], cs[8 * kap + 3]);
                 *reinterpret_cast<float4 *>(dst + 4) =
                     make_float4(cs[8 * kap + 4], cs[8 * kap + 5], cs[8 * kap + 6], cs[8 * kap + 7]);
             }
         }
-        const int i = 16 * w + lr;
+        const int i = 16 * tw + lr;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-            const int d0 = 32 * e + 8 * g;
+            const int d0 = 64 * hv + 32 * e + 8 * g;
             uint16_t *m = sV + (d0 >> 6) * MAT + swv(i, d0 & 63);
             uint4 vx = pv[e];
             if constexpr (RES) vx = add_io<DT>(vx, pr[e]);  // stack residual
@@ -273,7 +281,7 @@ struct RowTile {
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
             const float t = sTot[J * DK + l];
-            if (J < w) r_l += t;
+            if (J < tw) r_l += t;
             tot_l += t;
         }
         r_l *= kLog2e;
@@ -285,10 +293,13 @@ struct RowTile {
         sTab[l] = r_l;
         sTab[DK + l] = fexp2(tot_l);
         __builtin_amdgcn_wave_barrier();
-        const int i = 16 * w + lr;
+        const int i = 16 * tw + lr;
 #pragma unroll
         for (int kap = 0; kap < 2; ++kap) {
             const int c0 = 32 * kap + 8 * g;
+            // the two halves of a dv = 128 workgroup share K^ and the token-serial
+            // operands: half hv forms those of the channels [32 hv, 32 hv + 32)
+            const bool mine = CS == 1 || kap == hv;
             if (!slow) {
                 float rI[8];
 #pragma unroll
@@ -296,24 +307,29 @@ struct RowTile {
                     const float4 x = *reinterpret_cast<const float4 *>(sTab + c0 + 4 * h4);
                     rI[4 * h4] = x.x; rI[4 * h4 + 1] = x.y; rI[4 * h4 + 2] = x.z; rI[4 * h4 + 3] = x.w;
                 }
-                float qt[8], kh[8];
+                float qt[8], aa[8];
                 unpack8<DT>(pq[kap], qt);
-                unpack8<DT>(pk[kap], kh);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    const float aa = fmaf(cs[8 * kap + s], kLog2e, rI[s]);
-                    qt[s] *= fexp2(aa);   // q 2^a
-                    kh[s] *= fexp2(-aa);  // k 2^-a
+                    aa[s] = fmaf(cs[8 * kap + s], kLog2e, rI[s]);
+                    qt[s] *= fexp2(aa[s]);  // q 2^a
                 }
-                uint32_t qhi[4], qlo[4], khi[4], klo[4];
+                uint32_t qhi[4], qlo[4];
                 split_pk<false>(qt, qhi, qlo);
-                split_pk<false>(kh, khi, klo);
                 qh[kap] = __builtin_bit_cast(s16x8, u4(qhi));
                 ql[kap] = __builtin_bit_cast(s16x8, u4(qlo));
-                const int off = swn(i, c0);
-                *reinterpret_cast<uint4 *>(sK + off) = u4(khi);
-                *reinterpret_cast<uint4 *>(sK + MAT + off) = u4(klo);
-            } else {
+                if (mine) {
+                    float kh[8];
+                    unpack8<DT>(pk[kap], kh);
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) kh[s] *= fexp2(-aa[s]);  // k 2^-a
+                    uint32_t khi[4], klo[4];
+                    split_pk<false>(kh, khi, klo);
+                    const int off = swn(i, c0);
+                    *reinterpret_cast<uint4 *>(sK + off) = u4(khi);
+                    *reinterpret_cast<uint4 *>(sK + MAT + off) = u4(klo);
+                }
+            } else if (mine) {
                 // token-serial operands, [token][channel] without swizzle: q and k as
                 // stored (K area), g = 2^(a_i - a_{i-1}) in fp32 (state area)
                 *reinterpret_cast<uint4 *>(sK + i * DK + c0) = pq[kap];
@@ -359,17 +375,17 @@ struct RowTile {
         // inter-chunk readout O^T = S^T Q~_w^T
         const uint16_t *sh = sS, *sl = sS + DV * 64;
 #pragma unroll
-        for (int dd = 0; dd < ND; ++dd) {
-            O[dd] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int d = dcol(dd, lr);
+        for (int e = 0; e < NDW; ++e) {
+            O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int d = dcol(NDW * hv + e, lr);
 #pragma unroll
             for (int kap = 0; kap < 2; ++kap) {
                 const int off = sws(d, 32 * kap + 8 * g);
                 const s16x8 ah = *reinterpret_cast<const s16x8 *>(sh + off);
                 const s16x8 al = *reinterpret_cast<const s16x8 *>(sl + off);
-                O[dd] = mma<false>(ah, qh[kap], O[dd]);
-                O[dd] = mma<false>(ah, ql[kap], O[dd]);
-                O[dd] = mma<false>(al, qh[kap], O[dd]);
+                O[e] = mma<false>(ah, qh[kap], O[e]);
+                O[e] = mma<false>(ah, ql[kap], O[e]);
+                O[e] = mma<false>(al, qh[kap], O[e]);
             }
         }
         __builtin_amdgcn_sched_barrier(0);  // keeps the operand loads of each step near it
@@ -378,7 +394,7 @@ struct RowTile {
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
             ph[J][0] = ph[J][1] = pl[J][0] = pl[J][1] = 0u;
-            if (J <= w) {
+            if (J <= tw) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kap = 0; kap < 2; ++kap) {
@@ -391,7 +407,7 @@ struct RowTile {
                 }
                 float x[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = (J == w && 4 * g + r > lr) ? 0.f : acc[r];  // j <= i
+                for (int r = 0; r < 4; ++r) x[r] = (J == tw && 4 * g + r > lr) ? 0.f : acc[r];  // j <= i
                 split_pk<false>(x, ph[J], pl[J]);
             }
         }
@@ -399,17 +415,17 @@ struct RowTile {
         // intra-chunk readout O^T += V^T P^T, 32 tokens per step
 #pragma unroll
         for (int kt = 0; kt < NB / 2; ++kt) {
-            if (2 * kt <= w) {
+            if (2 * kt <= tw) {
                 const s16x8 bh = __builtin_bit_cast(
                     s16x8, make_uint4(ph[2 * kt][0], ph[2 * kt][1], ph[2 * kt + 1][0], ph[2 * kt + 1][1]));
                 const s16x8 bl = __builtin_bit_cast(
                     s16x8, make_uint4(pl[2 * kt][0], pl[2 * kt][1], pl[2 * kt + 1][0], pl[2 * kt + 1][1]));
 #pragma unroll
-                for (int dd = 0; dd < ND; ++dd) {
-                    const s16x8 av = op_v(0, dd, 32 * kt);
-                    O[dd] = mma<false>(av, bh, O[dd]);
-                    O[dd] = mma<false>(av, bl, O[dd]);
-                    if (NV == 2) O[dd] = mma<false>(op_v(NV - 1, dd, 32 * kt), bh, O[dd]);
+                for (int e = 0; e < NDW; ++e) {
+                    const s16x8 av = op_v(0, NDW * hv + e, 32 * kt);
+                    O[e] = mma<false>(av, bh, O[e]);
+                    O[e] = mma<false>(av, bl, O[e]);
+                    if (NV == 2) O[e] = mma<false>(op_v(NV - 1, NDW * hv + e, 32 * kt), bh, O[e]);
                 }
             }
         }
@@ -511,25 +527,40 @@ struct RowTile {
             for (int tb = 0; tb < NB; ++tb) X[((NS * w + s) * NB + tb) * 64 + l] = Os[s][tb];
         __syncthreads();
 #pragma unroll
-        for (int dd = 0; dd < ND; ++dd) O[dd] = X[(dd * NB + w) * 64 + l];
+        for (int e = 0; e < NDW; ++e) O[e] = X[((NDW * hv + e) * NB + tw) * 64 + l];
     }
 
     // ---- epilogue: y = o / sqrt(mean_j o_j^2 + eps) * rms_w * z * sigmoid(z) for the
     // wave's tokens, stored at the token's grid position (pairs rounded to nearest
     // even by the packed conversion)
-    __device__ __forceinline__ void epilogue() {
+    __device__ __forceinline__ float half_ss() const {
         float ss = 0.f;
 #pragma unroll
-        for (int dd = 0; dd < ND; ++dd)
+        for (int e = 0; e < NDW; ++e)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ss += O[dd][r] * O[dd][r];
+            for (int r = 0; r < 4; ++r) ss += O[e][r] * O[e][r];
         ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
+        return ss;
+    }
+    // two halves: each puts its tokens' sum before a barrier, and the epilogue adds
+    // both in half order (the same sum in both)
+    __device__ __forceinline__ void put_ss() {
+        const float ss = half_ss();
+        if (g == 0) sSS[hv * C + 16 * tw + lr] = ss;
+    }
+    __device__ __forceinline__ void epilogue() {
+        float ss;
+        if constexpr (CS == 1) {
+            ss = half_ss();
+        } else {
+            ss = sSS[16 * tw + lr] + sSS[C + 16 * tw + lr];
+        }
         const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + GTR_RMS_EPS);
         const bool odd = g & 1;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-            const int d0 = 32 * e + 8 * g;
+            const int d0 = 64 * hv + 32 * e + 8 * g;
             const f32x4 lo4 = odd ? O[2 * e + 1] : O[2 * e];
             const f32x4 hi4 = odd ? O[2 * e] : O[2 * e + 1];
             const float o[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
@@ -553,9 +584,10 @@ struct RowTile {
 };
 
 template <int DT, int DV, bool RES, bool LRG>
-__global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const float *__restrict__ Sx,
+__global__ __launch_bounds__(64 * 4 * (DV / 64), DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const float *__restrict__ Sx,
                                                                MfmaPlan pl, MfmaPlan ps) {
     using R = RowTile<DT, DV, RES, LRG>;
+    static_assert(R::NTH == 64 * 4 * (DV / 64), "launch bounds");
     __shared__ __attribute__((aligned(16))) char smem[R::BYTES];
     R t;
     t.init(a, smem);
@@ -607,11 +639,18 @@ __global__ __launch_bounds__(NT, DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const 
                 t.compute();
             else
                 t.serial();
-            t.epilogue();
-            t.prefetch_z(t.rowN);
+            if constexpr (R::CS == 1) {
+                t.epilogue();
+                t.prefetch_z(t.rowN);
+                __syncthreads();  // B3: LDS is rewritten by the next chunk
+            } else {
+                t.put_ss();
+                __syncthreads();  // B3: as above; both halves' sums of squares
+                t.epilogue();
+                t.prefetch_z(t.rowN);
+            }
             t.rowC = t.rowN;
             t.tokC = t.tokN;
-            __syncthreads();  // B3: LDS is rewritten by the next chunk
             ch = last_in_seq ? 0 : ch + 1;
             b = nb;
             h = nh;
@@ -626,14 +665,14 @@ hipError_t launch_rows(const GlaArgs &a, const float *Sx, const MfmaPlan &po, co
     if (a.feat) {  // gates from rank-16 features: dv = 64, no residual
         if constexpr (DV == 64) {
             if (a.resid || a.rank != kFusedGateRank) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((k_rows<DT, DV, false, true>), grid, dim3(NT), 0, st, a, Sx, po, ps);
+            hipLaunchKernelGGL((k_rows<DT, DV, false, true>), grid, dim3(RowTile<DT, DV, false, true>::NTH), 0, st, a, Sx, po, ps);
         } else {
             return hipErrorInvalidValue;
         }
     } else if (a.resid) {
-        hipLaunchKernelGGL((k_rows<DT, DV, true, false>), grid, dim3(NT), 0, st, a, Sx, po, ps);
+        hipLaunchKernelGGL((k_rows<DT, DV, true, false>), grid, dim3(RowTile<DT, DV, true, false>::NTH), 0, st, a, Sx, po, ps);
     } else {
-        hipLaunchKernelGGL((k_rows<DT, DV, false, false>), grid, dim3(NT), 0, st, a, Sx, po, ps);
+        hipLaunchKernelGGL((k_rows<DT, DV, false, false>), grid, dim3(RowTile<DT, DV, false, false>::NTH), 0, st, a, Sx, po, ps);
     }
     return hipGetLastError();
 }

@@ -160,6 +160,44 @@ __global__ __launch_bounds__(64 * P) void k_scan_rows(float *__restrict__ U,
     }
 }
 
+// Few segments per sequence (at most M): one wave per (sequence, 64-element
+// slice), W of them per workgroup, each lane loading its element of every
+// segment at once and folding them in order.  With several slices per workgroup
+// the launch has W times fewer workgroups than k_scan_rows (whose workgroups
+// then carry a segment or two per wave, and dispatch, not memory, bounds it).
+template <int M, int W>
+__global__ __launch_bounds__(64 * W) void k_scan_slices(float *__restrict__ U,
+                                                        const float *__restrict__ G, MfmaPlan pl,
+                                                        int dk, int dv) {
+    const int64_t dd = static_cast<int64_t>(dk) * dv;
+    const uint32_t slices = static_cast<uint32_t>(dk * dv / 64);
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(threadIdx.x >> 6));
+    const uint32_t sl = blockIdx.x * W + wv;  // global slice (the host sizes the grid exactly)
+    const uint32_t seq32 = sl / slices;
+    const int64_t seq = seq32;
+    const int lane = threadIdx.x & 63;
+    const uint32_t el0 = (sl - seq32 * slices) * 64;
+    const int64_t el = el0 + lane;
+    const int c = static_cast<int>(el0 / static_cast<uint32_t>(dv));
+    const int64_t s0 = seg_id(seq * pl.N, pl), s1 = seg_id((seq + 1) * pl.N, pl);
+    const int n = static_cast<int>(s1 - s0);  // <= M (checked by the host)
+    float x[M], e[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int64_t k = (i < n) ? s0 + i : s1 - 1;  // in bounds; unused past n
+        x[i] = U[k * dd + el];
+        e[i] = __builtin_amdgcn_exp2f(G[k * dk + c]);
+    }
+    float st = 0.f;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        if (i < n) {
+            U[(s0 + i) * dd + el] = st;
+            st = e[i] * st + x[i];
+        }
+    }
+}
+
 // The same fold in P parts (one wave each) for plain sequences of n_units units each (unit k of
 // sequence seq at index seq n_units + k), any dv: each lane takes its own key
 // channel.  Workgroup = (sequence, 64 consecutive state elements).  LOG2: the
@@ -219,8 +257,12 @@ hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_s
     const int64_t n_el = static_cast<int64_t>(n_seq) * dd;
     const int64_t most = (pl.N + pl.Q - 1) / pl.Q + 1;  // segments of one sequence, at most
     const dim3 rows_grid(static_cast<unsigned>(n_el / 64));
-    // four parts (more parts measured no faster at 16.4K tokens: 44 segments per sequence)
-    if (most <= 4 * 16) {
+    const int64_t n_slices = n_el / 64;
+    if (most <= 8 && n_slices % 16 == 0 && n_slices / 16 <= 0x7fffffff) {
+        hipLaunchKernelGGL((k_scan_slices<8, 16>), dim3(static_cast<unsigned>(n_slices / 16)),
+                           dim3(64 * 16), 0, s, U, G, pl, dk, dv);
+    } else if (most <= 4 * 16) {
+        // four parts (more parts measured no faster at 16.4K tokens: 44 segments per sequence)
         hipLaunchKernelGGL((k_scan_rows<16, 4>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);
     } else if (most <= 4 * 32) {
         hipLaunchKernelGGL((k_scan_rows<32, 4>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);

@@ -164,6 +164,35 @@ def test_mfma_extreme_gates(oracle_mod, dtype, log_g):
         assert_parity(got, ref, dtype, oracle_mod, f"mfma log_g {log_g}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("log_g", [-0.5, -20.0])
+def test_mfma_dv128_extreme_gates(oracle_mod, dtype, log_g):
+    """dv = 128, whose output workgroups split the value columns into two halves of
+    four waves; at -20 per token every chunk runs token by token."""
+    x = W.make_custom(1, 16, 16, 2, 64, 128, dtype, seed=6, log_g_const=log_g)
+    for direction in (1, 2):
+        _note(f"MFMA dv=128 constant log_g={log_g} {dtype} direction={direction}")
+        got = _run(x, dtype, direction, chunk=64, path=g.PATH_MFMA)
+        ref = _oracle(oracle_mod, x, dtype, direction)
+        assert_parity(got, ref, dtype, oracle_mod, f"mfma dv128 log_g {log_g}")
+
+
+@pytest.mark.parametrize("sc", [1, 5])
+def test_mfma_dv128_workgroup_ranges(oracle_mod, segment_chunks, sc):
+    """dv = 128 with forced chunks per workgroup (ranges crossing sequences), sharp
+    gates on a few tokens so that some chunks run token by token."""
+    x = W.make_custom(1, 30, 31, 2, 64, 128, "bf16", seed=19)
+    lg = x["log_g"].reshape(-1, 2, 64)
+    hit = np.random.default_rng(19).choice(lg.shape[0], size=12, replace=False)
+    lg[hit] = -12.0
+    segment_chunks(sc)
+    for direction in (0, 3):
+        _note(f"dv=128, {sc} chunks per workgroup, direction {direction}")
+        got = _run(x, "bf16", direction, chunk=64, path=g.PATH_MFMA)
+        ref = _oracle(oracle_mod, x, "bf16", direction)
+        assert_parity(got, ref, "bf16", oracle_mod, f"dv128 segments of {sc}")
+
+
 def test_mfma_mixed_spans(oracle_mod):
     """Sharp gates on a few tokens: some sub-blocks take the pairwise diagonal, others not."""
     x = W.make_custom(1, 24, 24, 2, 64, 64, "f16", seed=5)
