@@ -700,6 +700,22 @@ def main():
                               "path": PATH_NAMES[pe]}
                 log(f"  {key}: {r['us_per_call']:.2f} us/call, graph {r['us_per_call_graph']}"
                     f"{' (' + r['graph_error'] + ')' if r.get('graph_error') else ''}")
+    directions = {}
+    if not args.no_extra:
+        # the other scan orders on the same workload (TB and BT gather columns with a stride
+        # of grid_w rows)
+        directions["LR"] = {"us_per_call": round(us, 3), "hbm_frac": roofline["whole_call_frac"]}
+        for d, dn in ((1, "RL"), (2, "TB"), (3, "BT")):
+            try:
+                _, r = time_workload(w, dev, hip, sp, args.steps, args.warmup, path, chunk,
+                                     direction=d, per_kernel=False, graph=False)
+            except Exception as exc:  # report, do not hide
+                directions[dn] = {"error": str(exc)[:300]}
+                continue
+            directions[dn] = {"us_per_call": round(r["us_per_call"], 3),
+                              "hbm_frac": round(comp / (r["us_per_call"] * 1e-6) / 1e9
+                                                / HBM_PEAK_GBS, 4)}
+            log(f"  direction {dn}: {r['us_per_call']:.2f} us/call")
     lowrank = None
     if not args.no_extra and w.dtype != "f32":
         # the same shapes with the gate formed from rank-16 features inside the kernels
@@ -828,6 +844,7 @@ def main():
         "rotating_sets": res["n_sets"],
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "directions": directions,
         "extra_1p6k": extra,
         "lowrank_gate": lowrank,
         "sswiglu_mix": sswiglu,
