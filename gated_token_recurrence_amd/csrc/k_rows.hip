@@ -26,6 +26,15 @@
 // update, V for the intra product and the state update, and the state S^T
 // (hi, lo) that every wave reads for Q~ S.  Three barriers per chunk.
 //
+// dv = 128 runs eight waves in two value halves: waves w and w + 4 own the same
+// 16 tokens, wave w takes the value columns [64 (w / 4), 64 (w / 4) + 64) of
+// them and state tile w, so each wave holds what a dv = 64 wave holds (the
+// four-wave form would need about 450 registers per lane, one wave per SIMD).
+// Both halves form Q~ and the score tiles; each forms K^ for 32 of the 64 key
+// channels.  The RMSNorm sum over all 128 columns is completed through LDS:
+// each half puts its tokens' partial sums before the end-of-chunk barrier and
+// both add the two in the same order.
+//
 // Low-rank gate variant (LRG): instead of reading log_g, each wave forms its
 // tokens' gates from their rank-16 features (Method §1: a light low-rank
 // projection with a temperature) with four 16x16x16 products against the
