@@ -553,7 +553,9 @@ struct RowTile {
         return ss;
     }
     // two halves: each puts its tokens' sum before a barrier, and the epilogue adds
-    // both in half order (the same sum in both)
+    // both in half order (the same sum in both).  One buffer is enough: the next
+    // chunk's sums are written after that chunk's first two barriers, which no wave
+    // passes before it has read this chunk's.
     __device__ __forceinline__ void put_ss() {
         const float ss = half_ss();
         if (g == 0) sSS[hv * C + 16 * tw + lr] = ss;
