@@ -38,6 +38,10 @@ def _order(gh: int, gw: int, direction: int) -> np.ndarray:
 def bwd(q, k, v, log_g, z, rms_w, dout, direction: int, eps: float = RMS_EPS, bh=None):
     """Returns dict dq, dk, dv, dlog_g, dz (shapes of the inputs) and drms_w [dv], fp64.
 
+    The dict also holds ``y``: the forward output that the kept states give
+    (o_t = S_t^T q_t, then the epilogue), stored at grid positions, so that the
+    forward half of this oracle can be checked against the C oracle.
+
     ``bh``: optional iterable of b*H + h sequences to differentiate; the other
     sequences' gradients are NaN and drms_w sums over the chosen ones only."""
     q, k, v, log_g, z, w, dy = (np.asarray(a, dtype=np.float64) for a in
@@ -47,7 +51,7 @@ def bwd(q, k, v, log_g, z, rms_w, dout, direction: int, eps: float = RMS_EPS, bh
     L = gh * gw
     order = _order(gh, gw, direction)
     out = {name: np.full(a.shape, np.nan) for name, a in
-           (("dq", q), ("dk", k), ("dv", v), ("dlog_g", log_g), ("dz", z))}
+           (("dq", q), ("dk", k), ("dv", v), ("dlog_g", log_g), ("dz", z), ("y", z))}
     drms = np.zeros(dv)
     seqs = range(B * H) if bh is None else bh
     for s in seqs:
@@ -73,6 +77,7 @@ def bwd(q, k, v, log_g, z, rms_w, dout, direction: int, eps: float = RMS_EPS, bh
         dO = r[:, None] * (dN - N * (dN * N).mean(axis=1)[:, None])
         dZ = DY * N * w * sig * (1.0 + Z * (1.0 - sig))
         drms += (DY * N * silu).sum(axis=0)
+        Y = N * w * silu
         # recurrence backward
         dQ = np.einsum("tcd,td->tc", Ss[1:], dO)
         dK, dV, dLG = np.zeros((L, dk)), np.zeros((L, dv)), np.zeros((L, dk))
@@ -85,7 +90,7 @@ def bwd(q, k, v, log_g, z, rms_w, dout, direction: int, eps: float = RMS_EPS, bh
             dV[t] = dS.T @ K[t]
             dLG[t] = G[t] * (dS * Ss[t]).sum(axis=1)
         for name, val, d in (("dq", dQ, dk), ("dk", dK, dk), ("dv", dV, dv),
-                             ("dlog_g", dLG, dk), ("dz", dZ, dv)):
+                             ("dlog_g", dLG, dk), ("dz", dZ, dv), ("y", Y, dv)):
             dst = out[name][b].reshape(L, H, d)
             dst[order, h] = val
             out[name][b] = dst.reshape(out[name][b].shape)

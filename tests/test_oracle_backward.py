@@ -2,12 +2,14 @@
 
 (1) torch autograd of an independent fp64 forward written as the O(L^2) closed
 form o_t = sum_{s<=t} ((q_t exp(A_t - A_s)) . k_s) v_s (A = inclusive cumulative
-log-gate) with torch's own rms_norm and silu; (2) central finite differences of
-the C forward oracle along random directions; (3) the oracle's forward states
-reproduce the C oracle's output.  A slip in any gradient term (a missing decay
-in the reverse recurrence, the gate gradient taken at the wrong state, the
-RMSNorm backward without its projection term, silu' wrong, a direction map
-mismatch) fails (1) and (2).
+log-gate) with torch's own rms_norm and silu, its scan order built here from
+reshapes and flips of the grid (not from the oracle's order); (2) central finite
+differences of the C forward oracle along random directions; (3) the oracle's
+forward states reproduce the C oracle's output.  All three run in every scan
+direction.  A slip in any gradient term (a missing decay in the reverse
+recurrence, the gate gradient taken at the wrong state, the RMSNorm backward
+without its projection term, silu' wrong) fails (1) and (2); a wrong scan order
+in any direction fails all three.
 """
 import numpy as np
 import pytest
@@ -25,12 +27,29 @@ def _inputs(B, gh, gw, H, dk, dv, seed, temp=4.0):
     return q, k, v, lg, z, w, dy
 
 
+def _scan_order(gh, gw, direction):
+    """Grid index of each scan step, from the grid itself: LR the row-major
+    raster, RL its reverse, TB the row-major raster of the transposed grid
+    (columns top to bottom, left to right), BT its reverse."""
+    grid = np.arange(gh * gw).reshape(gh, gw)
+    raster = grid.T.ravel() if direction >= 2 else grid.ravel()
+    return raster[::-1].copy() if direction & 1 else raster
+
+
+def test_scan_order_by_hand():
+    # 2 x 3 grid: positions 0 1 2 / 3 4 5
+    assert _scan_order(2, 3, 0).tolist() == [0, 1, 2, 3, 4, 5]
+    assert _scan_order(2, 3, 1).tolist() == [5, 4, 3, 2, 1, 0]
+    assert _scan_order(2, 3, 2).tolist() == [0, 3, 1, 4, 2, 5]
+    assert _scan_order(2, 3, 3).tolist() == [5, 2, 4, 1, 3, 0]
+
+
 def _torch_closed_form(q, k, v, lg, z, w, direction, eps=1e-5):
     """Independent forward: O(L^2) closed form per sequence, torch ops, fp64."""
     B, gh, gw, H, dk = q.shape
     dv = v.shape[-1]
     L = gh * gw
-    order = torch.as_tensor(ob._order(gh, gw, direction))
+    order = torch.as_tensor(_scan_order(gh, gw, direction))
     inv = torch.empty_like(order)
     inv[order] = torch.arange(L)
     def seq(x, d):
@@ -59,11 +78,11 @@ def test_matches_torch_autograd_of_closed_form(direction):
                                    err_msg=name)
 
 
-def test_central_differences_of_the_c_oracle(oracle_mod):
+@pytest.mark.parametrize("direction", [0, 1, 2, 3])
+def test_central_differences_of_the_c_oracle(oracle_mod, direction):
     B, gh, gw, H, dk, dv = 1, 4, 3, 2, 3, 4
-    arrs = list(_inputs(B, gh, gw, H, dk, dv, seed=7))
+    arrs = list(_inputs(B, gh, gw, H, dk, dv, seed=7 + direction))
     dy = arrs[6]
-    direction = 2
     got = ob.bwd(*arrs, direction)
     rng = np.random.default_rng(8)
     h = 1e-6
@@ -87,3 +106,11 @@ def test_restricted_sequences_match_full_run():
         np.testing.assert_array_equal(part[name][0, :, :, 1], full[name][0, :, :, 1])
         np.testing.assert_array_equal(part[name][1, :, :, 1], full[name][1, :, :, 1])
         assert np.isnan(part[name][0, :, :, 0]).all()
+
+
+@pytest.mark.parametrize("direction", [0, 1, 2, 3])
+def test_forward_states_reproduce_the_c_oracle(oracle_mod, direction):
+    arrs = _inputs(2, 3, 5, 2, 4, 3, seed=20 + direction)
+    got = ob.bwd(*arrs, direction)["y"]
+    ref = oracle_mod.fwd(*arrs[:6], direction)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
