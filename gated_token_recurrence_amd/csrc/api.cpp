@@ -49,6 +49,22 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 // log_g written out by the low-rank gate kernel (kept apart from the states)
 std::map<std::pair<int, hipStream_t>, Workspace> g_gws;
 
+// A stream under graph capture cannot synchronise, free or allocate: a buffer that
+// would have to be created or grown then is refused with a clear error instead of
+// invalidating the capture.  (Work captured into a graph keeps the buffer's address,
+// so the buffer must not change while such a graph may still be replayed.)
+gtr_status no_growth_while_capturing(hipStream_t stream, const char *what) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(GTR_ERR_UNSUPPORTED,
+                    "the %s would have to grow while the stream is being captured; make the same "
+                    "call once on this stream before capturing",
+                    what);
+    return GTR_OK;
+}
+
 gtr_status workspace(hipStream_t stream, size_t bytes, void **out,
                      std::map<std::pair<int, hipStream_t>, Workspace> &pool = g_ws) {
     int dev = 0;
@@ -57,6 +73,8 @@ gtr_status workspace(hipStream_t stream, size_t bytes, void **out,
     std::lock_guard<std::mutex> lock(g_ws_mu);
     Workspace &w = pool[std::make_pair(dev, stream)];
     if (w.bytes < bytes) {
+        gtr_status cs = no_growth_while_capturing(stream, "workspace");
+        if (cs != GTR_OK) return cs;
         if (w.ptr) {
             e = hipStreamSynchronize(stream);
             if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -89,6 +107,8 @@ gtr_status counters(hipStream_t stream, size_t n, void **out) {
     Workspace &w = g_ctr[std::make_pair(dev, stream)];
     const size_t bytes = n * sizeof(unsigned);
     if (w.bytes < bytes) {
+        gtr_status cs = no_growth_while_capturing(stream, "counter block");
+        if (cs != GTR_OK) return cs;
         if (w.ptr) {
             e = hipStreamSynchronize(stream);
             if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -133,6 +153,12 @@ gtr_status check(const void *q, const void *k, const void *v, const float *log_g
         return fail(GTR_ERR_ARG, "unknown path %d", path);
     if (!head_width_ok(dk) || !head_width_ok(dv))
         return fail(GTR_ERR_UNSUPPORTED, "dk and dv must be 32, 64 or 128 (got %d, %d)", dk, dv);
+    const uintptr_t eb = dtype == GTR_F32 ? 4 : 2;
+    for (const void *p : {q, k, v, z, static_cast<const void *>(out)})
+        if (reinterpret_cast<uintptr_t>(p) % eb != 0)
+            return fail(GTR_ERR_ARG, "q, k, v, z and out must be aligned to their element size");
+    if (reinterpret_cast<uintptr_t>(log_g) % 4 != 0 || reinterpret_cast<uintptr_t>(rms_w) % 4 != 0)
+        return fail(GTR_ERR_ARG, "log_g and rms_w must be 4-byte aligned");
     const __int128 rows = static_cast<__int128>(B) * gh * gw * H;
     if (rows * (dk > dv ? dk : dv) * 4 > (static_cast<__int128>(1) << 62) ||
         static_cast<int64_t>(gh) * gw > (static_cast<int64_t>(1) << 40))
@@ -233,19 +259,46 @@ bool gtr::lowrank_fused_supported(const GlaArgs &a) {
 
 namespace {
 
+// The matrix-core and single-launch kernels move token rows in 16-byte pieces:
+// every row pointer they touch must be 16-byte aligned (a contiguous view with a
+// storage offset may not be).  Null pointers (log_g of a low-rank call, no
+// residual) do not count.
+bool vec16(const GlaArgs &a) {
+    for (const void *p : {a.q, a.k, a.v, static_cast<const void *>(a.log_g), a.z,
+                          static_cast<const void *>(a.out), a.resid})
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return false;
+    return true;
+}
+
+bool mfma_ok(const GlaArgs &a) { return a.dtype != GTR_F32 && mfma_supported(a) && vec16(a); }
+
 // The single-launch path: batch one, at most kFastMaxTokens tokens.
 bool fast_ok(const GlaArgs &a) {
-    if (a.dtype == GTR_F32 || !fast_supported(a)) return false;
+    if (!mfma_ok(a) || !fast_supported(a)) return false;
     return a.B == 1 && a.L <= kFastMaxTokens;
 }
 
-// AUTO takes the matrix-core path for 16-bit I/O and the token-serial path
-// otherwise.  The single-launch path is taken only when asked for: on MI355X the
-// three-launch path is measured faster at 1.6K tokens too, because per-chunk
-// latency, not launch overhead, bounds both.
-int auto_path(const GlaArgs &a) {
-    const bool mfma_ok = a.dtype != GTR_F32 && mfma_supported(a);
-    return mfma_ok ? GTR_PATH_MFMA : GTR_PATH_SERIAL;
+// AUTO takes the matrix-core path for 16-bit I/O at its shapes with 16-byte
+// aligned rows and the token-serial path otherwise.  The single-launch path is
+// taken only when asked for: on MI355X the three-launch path is measured faster
+// at 1.6K tokens too, because per-chunk latency, not launch overhead, bounds both.
+int auto_path(const GlaArgs &a) { return mfma_ok(a) ? GTR_PATH_MFMA : GTR_PATH_SERIAL; }
+
+// Resolves AUTO and checks that an explicit path can take the arguments (before
+// anything touches the device).
+gtr_status resolve_path(const GlaArgs &a, int path, int *out) {
+    if (path == GTR_PATH_AUTO) path = auto_path(a);
+    if (path == GTR_PATH_MFMA && !mfma_ok(a))
+        return fail(GTR_ERR_UNSUPPORTED,
+                    "MFMA path needs 16-bit I/O, dk = 64, dv in {64, 128}, chunk in {32, 64} and "
+                    "16-byte aligned tensors");
+    if (path == GTR_PATH_FAST && !fast_ok(a))
+        return fail(GTR_ERR_UNSUPPORTED,
+                    "single-launch path needs 16-bit I/O, dk = 64, dv in {64, 128}, chunk in "
+                    "{32, 64}, 16-byte aligned tensors, B = 1 and at most %d tokens",
+                    kFastMaxTokens);
+    *out = path;
+    return GTR_OK;
 }
 
 gtr_status run_fast(const GlaArgs &a, hipStream_t st, Marks &mk) {
@@ -266,24 +319,33 @@ gtr_status run_fast(const GlaArgs &a, hipStream_t st, Marks &mk) {
 gtr_status run(const GlaArgs &a0, int path, hipStream_t st, Marks &mk) {
     GlaArgs a = a0;
     if (a.chunk == 0) a.chunk = kDefaultChunk;
-    const bool mfma_ok = a.dtype != GTR_F32 && mfma_supported(a);
-    if (path == GTR_PATH_AUTO) path = auto_path(a);
+    gtr_status s = resolve_path(a, path, &path);
+    if (s != GTR_OK) return s;
     switch (path) {
     case GTR_PATH_SERIAL: return run_serial(a, st, mk);
-    case GTR_PATH_MFMA:
-        if (!mfma_ok)
-            return fail(GTR_ERR_UNSUPPORTED,
-                        "MFMA path needs 16-bit I/O, dk = 64, dv in {64, 128}, chunk in {32, 64}");
-        return run_mfma(a, st, mk);
-    case GTR_PATH_FAST:
-        if (!fast_ok(a))
-            return fail(GTR_ERR_UNSUPPORTED,
-                        "single-launch path needs 16-bit I/O, dk = 64, dv in {64, 128}, chunk in "
-                        "{32, 64}, B = 1 and at most %d tokens",
-                        kFastMaxTokens);
-        return run_fast(a, st, mk);
+    case GTR_PATH_MFMA: return run_mfma(a, st, mk);
+    case GTR_PATH_FAST: return run_fast(a, st, mk);
     default: return fail(GTR_ERR_ARG, "unknown path %d", path);
     }
+}
+
+// Workspace bytes a run() of these arguments on this path needs (so that a caller
+// issuing several runs can size it once, before the first launch).
+size_t run_workspace_bytes(const GlaArgs &a0, int path) {
+    GlaArgs a = a0;
+    if (a.chunk == 0) a.chunk = kDefaultChunk;
+    if (path == GTR_PATH_AUTO) path = auto_path(a);
+    if (path == GTR_PATH_MFMA) {
+        MfmaPlan pl, po;
+        mfma_plans(a, g_chunks_per_wg, &pl, &po);
+        return static_cast<size_t>(pl.n_seg) * a.dk * a.dv * 4 + static_cast<size_t>(pl.n_seg) * a.dk * 4;
+    }
+    if (path == GTR_PATH_FAST) {
+        const size_t T = static_cast<size_t>(fast_chunks(a));
+        return T * a.dk * a.dv * 4 + T * a.dk * 4;
+    }
+    const size_t n = static_cast<size_t>(a.B) * a.H * ((a.L + a.chunk - 1) / a.chunk);
+    return n * a.dk * a.dv * 4 + n * a.dk * 4;
 }
 
 int device_ok() {
@@ -323,7 +385,6 @@ gtr_status lowrank_impl(const void *q, const void *k, const void *v, const void 
                          static_cast<size_t>(dv) * 4};
     s = check_aliasing(out, rows * dv * eb, ins, nb, 8);
     if (s != GTR_OK) return s;
-    if (!device_ok()) return GTR_ERR_HIP;
     GlaArgs a{q, k, v, nullptr, z, rms_w, out, nullptr, B, H, gh, gw, dk, dv, direction,
               chunk ? chunk : kDefaultChunk, dtype, static_cast<int64_t>(gh) * gw};
     a.feat = feat;
@@ -331,7 +392,10 @@ gtr_status lowrank_impl(const void *q, const void *k, const void *v, const void 
     a.gate_b = gate_b;
     a.inv_tau = 1.f / tau;
     a.rank = rank;
-    const int p = path == GTR_PATH_AUTO ? auto_path(a) : path;
+    int p = path;
+    s = resolve_path(a, path, &p);  // log_g is null here: the gate buffer is aligned
+    if (s != GTR_OK) return s;
+    if (!device_ok()) return GTR_ERR_HIP;
     if (p == GTR_PATH_MFMA && lowrank_fused_supported(a)) return run_mfma(a, stream, mk);
     // every other path reads log_g: write it out first
     void *lg = nullptr;
@@ -361,10 +425,13 @@ gtr_status fwd_impl(const void *q, const void *k, const void *v, const float *lo
                          rows * dv * eb, static_cast<size_t>(dv) * 4, rows * dv * eb};
     s = check_aliasing(out, rows * dv * eb, ins, nb, 7);
     if (s != GTR_OK) return s;
+    GlaArgs a{q, k, v, log_g, z, rms_w, out, resid, B, H, gh, gw, dk, dv, direction,
+              chunk ? chunk : kDefaultChunk, dtype, static_cast<int64_t>(gh) * gw};
+    int resolved = path;
+    s = resolve_path(a, path, &resolved);
+    if (s != GTR_OK) return s;
     if (!device_ok()) return GTR_ERR_HIP;
-    GlaArgs a{q, k, v, log_g, z, rms_w, out, resid, B, H, gh, gw, dk, dv, direction, chunk,
-              dtype, static_cast<int64_t>(gh) * gw};
-    return run(a, path, stream, mk);
+    return run(a, resolved, stream, mk);
 }
 
 // Forward segment states shared by gtr_gla_fwd_states and gtr_gla_bwd_states: the
@@ -448,6 +515,8 @@ gtr_status gtr_gla_fwd_states(const void *q, const void *k, const void *v, const
                     "forward states need 16-bit I/O, dk = dv = 64 and chunk 64");
     if (states_bytes < need)
         return fail(GTR_ERR_ARG, "states buffer of %zu bytes, need %zu", states_bytes, need);
+    if (!vec16(a) || reinterpret_cast<uintptr_t>(states) % 16 != 0)
+        return fail(GTR_ERR_UNSUPPORTED, "forward states need 16-byte aligned tensors");
     const size_t rows = static_cast<size_t>(B) * grid_h * grid_w * H;
     const size_t eb = elem_bytes(dtype);
     const void *ins[] = {q, k, v, log_g, z, rms_w, out};
@@ -480,7 +549,22 @@ gtr_status gtr_gla_stack_fwd(const void *q, const void *k, const void *v, const 
                          v_b * n_blocks, static_cast<size_t>(dv) * 4 * n_blocks};
     s = check_aliasing(out, v_b * n_blocks, ins, nb, 6);
     if (s != GTR_OK) return s;
+    // Every block has the same shape; block i's pointers are block 0's plus whole
+    // tensors, so their alignment is block 0's (rows of 16-bit elements are 64 B or
+    // more).  The path and the workspace are settled here, so that an argument or
+    // workspace error leaves nothing enqueued.
+    GlaArgs a0{q, k, v, log_g, z, rms_w, out, n_blocks > 1 ? out : nullptr, B, H, grid_h, grid_w,
+               dk, dv, first_direction, chunk ? chunk : kDefaultChunk, dtype,
+               static_cast<int64_t>(grid_h) * grid_w};
+    int path = GTR_PATH_AUTO;
+    s = resolve_path(a0, GTR_PATH_AUTO, &path);
+    if (s != GTR_OK) return s;
     if (!device_ok()) return GTR_ERR_HIP;
+    {
+        void *ws = nullptr;
+        s = workspace(stream, run_workspace_bytes(a0, path), &ws);
+        if (s != GTR_OK) return s;
+    }
     for (int i = 0; i < n_blocks; ++i) {
         const char *qi = static_cast<const char *>(q) + qk_b * i;
         const char *ki = static_cast<const char *>(k) + qk_b * i;
@@ -494,8 +578,8 @@ gtr_status gtr_gla_stack_fwd(const void *q, const void *k, const void *v, const 
         GlaArgs a{qi, ki, vi, gi, zi, wi, oi, resid, B, H, grid_h, grid_w, dk, dv,
                   (first_direction + i) % 4, chunk, dtype, static_cast<int64_t>(grid_h) * grid_w};
         Marks mk;
-        s = run(a, GTR_PATH_AUTO, stream, mk);
-        if (s != GTR_OK) {
+        s = run(a, path, stream, mk);
+        if (s != GTR_OK) {  // a launch failure: blocks 0 .. i-1 are enqueued
             std::string msg = g_err;
             return fail(s, "block %d: %s", i, msg.c_str());
         }

@@ -30,6 +30,12 @@
  * reversed); TB visits the columns left to right, each top to bottom;
  * BT is TB reversed.  L = grid_h * grid_w.
  *
+ * Alignment: every tensor must be aligned to its element size (GTR_ERR_ARG
+ * otherwise).  The matrix-core and single-launch paths move rows in 16-byte
+ * pieces and need q, k, v, log_g, z and out (and a stack's residual) 16-byte
+ * aligned: an explicit request for them with a misaligned pointer returns
+ * GTR_ERR_UNSUPPORTED, and AUTO then takes the token-serial path.
+ *
  * Ownership: every tensor pointer is DEVICE memory owned by the caller; the
  * library never frees it.  out must not overlap any input.  The library keeps
  * a grow-only workspace per (device, stream), released by
@@ -39,9 +45,18 @@
  * returns without waiting for it.  The current HIP device must own the
  * pointers and the stream.
  *
- * Errors: on any error nothing is enqueued and a message is available from
- * gtr_last_error() (thread-local).  Data errors on the device (NaN, Inf,
- * log_g > 0) are not checked; they propagate.
+ * Graph capture: a call may be captured into a HIP graph once the same call
+ * (same shape and path) has run on that stream outside capture, so that the
+ * workspace already has its size; a call that would have to create or grow the
+ * workspace while its stream is capturing returns GTR_ERR_UNSUPPORTED and does
+ * not disturb the capture.  A captured graph holds the workspace's address:
+ * while it may still be replayed, make no larger call on that stream and do
+ * not call gtr_release_workspace().
+ *
+ * Errors: argument, path and workspace errors are found before anything is
+ * enqueued; a message is available from gtr_last_error() (thread-local).
+ * Data errors on the device (NaN, Inf, log_g > 0) are not checked; they
+ * propagate.
  */
 #ifndef GTRSCAN_H
 #define GTRSCAN_H
@@ -121,7 +136,10 @@ gtr_status gtr_gla_fwd_events(const void *q, const void *k, const void *v, const
  * (first_direction + i) mod 4 and uses the value input
  *     v_eff_i = round_io(v_i + out_{i-1})   (i > 0; float32 add),  v_eff_0 = v_0,
  * the previous block's output fed forward as a residual.  Blocks are ordered
- * on `stream`; there is no host synchronisation between them.
+ * on `stream`; there is no host synchronisation between them.  The path and the
+ * workspace are settled for all blocks before block 0 is enqueued, so argument
+ * and workspace errors leave nothing enqueued; a kernel launch that fails in
+ * block i (i > 0) leaves blocks 0 .. i-1 enqueued.
  */
 gtr_status gtr_gla_stack_fwd(const void *q, const void *k, const void *v, const float *log_g,
                              const void *z, const float *rms_w, void *out, int n_blocks,

@@ -75,6 +75,50 @@ def test_stack_rejects_bad_block_count():
     assert st == _lib.GTR_ERR_ARG
 
 
+def test_misaligned_element_is_rejected():
+    lib = _lib.load()
+    q = P[0] + 1  # an odd address for 16-bit elements
+    st = lib.gtr_gla_fwd(q, *P[1:], 1, 1, 8, 8, 64, 64, 0, 0, _lib.GTR_F16, None)
+    assert st == _lib.GTR_ERR_ARG and "aligned" in _lib.last_error()
+    lg = P[3] + 2  # log_g is float32
+    st = lib.gtr_gla_fwd(*P[:3], lg, *P[4:], 1, 1, 8, 8, 64, 64, 0, 0, _lib.GTR_F16, None)
+    assert st == _lib.GTR_ERR_ARG and "aligned" in _lib.last_error()
+
+
+@pytest.mark.parametrize("which", range(7))
+def test_matrix_paths_need_16_byte_rows(which):
+    # a row pointer off by 8 bytes (a contiguous view with a storage offset) is
+    # refused by the explicit matrix-core and single-launch paths before any
+    # device work; AUTO sends such a call to the token-serial path instead
+    lib = _lib.load()
+    ptrs = list(P)
+    ptrs[which] += 8
+    if which == 5:  # rms_w is read element by element: 8 bytes off is fine everywhere
+        return
+    for path in (_lib.PATH_MFMA, _lib.PATH_FAST):
+        st = lib.gtr_gla_fwd_path(*ptrs, 1, 2, 8, 8, 64, 64, 0, 64, _lib.GTR_F16, path, None)
+        assert st == _lib.GTR_ERR_UNSUPPORTED and "16-byte" in _lib.last_error(), (which, path)
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device error path")
+def test_misaligned_rows_still_reach_the_device_on_auto():
+    lib = _lib.load()
+    ptrs = list(P)
+    ptrs[0] += 8
+    st = lib.gtr_gla_fwd(*ptrs, 1, 2, 8, 8, 64, 64, 0, 64, _lib.GTR_F16, None)
+    assert st == _lib.GTR_ERR_HIP  # accepted; fails only for want of a device
+
+
+def test_stack_checks_paths_before_the_device():
+    lib = _lib.load()
+    ptrs = list(P)
+    ptrs[1] += 8
+    # AUTO inside a stack routes a misaligned stack to the token-serial path: the
+    # call gets as far as the device check
+    st = lib.gtr_gla_stack_fwd(*ptrs, 2, 1, 1, 8, 8, 64, 64, 0, 0, _lib.GTR_F16, None)
+    assert st in (_lib.GTR_ERR_HIP, _lib.GTR_OK) or torch.cuda.device_count() > 0
+
+
 def test_unknown_path_is_rejected():
     lib = _lib.load()
     st = lib.gtr_gla_fwd_path(*P, 1, 1, 8, 8, 32, 32, 0, 0, 0, 9, None)
