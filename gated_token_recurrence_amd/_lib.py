@@ -16,7 +16,7 @@ GTR_OK, GTR_ERR_ARG, GTR_ERR_UNSUPPORTED, GTR_ERR_HIP = 0, -1, -2, -3
 GTR_F32, GTR_F16, GTR_BF16 = 0, 1, 2
 PATH_AUTO, PATH_MFMA, PATH_FAST, PATH_SERIAL = 0, 1, 2, 3
 
-EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_path", "gtr_gla_fwd_events", "gtr_gla_stack_fwd",
+EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_noalloc", "gtr_gla_fwd_path", "gtr_gla_fwd_events", "gtr_gla_stack_fwd",
            "gtr_gla_lowrank_fwd", "gtr_gla_bwd", "gtr_gla_states_bytes", "gtr_gla_fwd_states",
            "gtr_gla_bwd_states", "gtr_sswiglu_mix", "gtr_gla_auto_path", "gtr_last_error",
            "gtr_version", "gtr_release_workspace", "gtr_set_segment_chunks")
@@ -42,6 +42,8 @@ def load():
     vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
     lib.gtr_gla_fwd.restype = i
     lib.gtr_gla_fwd.argtypes = [vp, vp, vp, fp, vp, fp, vp] + [i] * 9 + [vp]
+    lib.gtr_gla_fwd_noalloc.restype = i
+    lib.gtr_gla_fwd_noalloc.argtypes = [vp, vp, vp, fp, vp, fp, vp] + [i] * 9 + [vp]
     lib.gtr_gla_fwd_path.restype = i
     lib.gtr_gla_fwd_path.argtypes = [vp, vp, vp, fp, vp, fp, vp] + [i] * 10 + [vp]
     lib.gtr_gla_fwd_events.restype = i

@@ -191,19 +191,36 @@ struct Marks {
     hipError_t start(hipStream_t st) { return launches == 0 ? record(st, 0) : hipSuccess; }
 };
 
+// Where a run's workspace comes from: the library's grow-only buffer (ptr null) or
+// a fixed region that must already be large enough (the no-allocation entry point).
+struct WsSource {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+gtr_status take_workspace(hipStream_t st, size_t need, const WsSource *src, void **out) {
+    if (!src || !src->ptr) return workspace(st, need, out);
+    if (need > src->bytes)
+        return fail(GTR_ERR_UNSUPPORTED,
+                    "this call needs %zu bytes of scratch; the fixed scratch holds %zu", need,
+                    src->bytes);
+    *out = src->ptr;
+    return GTR_OK;
+}
+
 constexpr int kDefaultChunk = 64;
 constexpr int kFastMaxTokens = 2048;
 
 int g_chunks_per_wg = 0;  // 0: automatic (gtr_set_segment_chunks)
 
-gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk) {
+gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk, const WsSource *src = nullptr) {
     const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
     const int64_t n_seq = static_cast<int64_t>(a.B) * a.H;
     if (n_seq * n_chunks > 0x7fffffff) return fail(GTR_ERR_UNSUPPORTED, "too many chunks");
     const size_t ubytes = static_cast<size_t>(n_seq * n_chunks) * a.dk * a.dv * 4;
     const size_t gbytes = static_cast<size_t>(n_seq * n_chunks) * a.dk * 4;
     void *ws = nullptr;
-    gtr_status s = workspace(st, ubytes + gbytes, &ws);
+    gtr_status s = take_workspace(st, ubytes + gbytes, src, &ws);
     if (s != GTR_OK) return s;
     float *U = static_cast<float *>(ws);
     float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
@@ -222,7 +239,8 @@ gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk) {
 
 // states_out: where the segment states go (the caller's buffer of gtr_gla_fwd_states),
 // else the workspace
-gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk, float *states_out = nullptr) {
+gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk, float *states_out = nullptr,
+                    const WsSource *src = nullptr) {
     MfmaPlan pl, po;
     mfma_plans(a, g_chunks_per_wg, &pl, &po);
     const int64_t n_seq = static_cast<int64_t>(a.B) * a.H;
@@ -231,7 +249,7 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk, float *states_o
     const size_t ubytes = states_out ? 0 : static_cast<size_t>(pl.n_seg) * a.dk * a.dv * 4;
     const size_t gbytes = static_cast<size_t>(pl.n_seg) * a.dk * 4;
     void *ws = nullptr;
-    gtr_status s = workspace(st, ubytes + gbytes, &ws);
+    gtr_status s = take_workspace(st, ubytes + gbytes, src, &ws);
     if (s != GTR_OK) return s;
     float *U = states_out ? states_out : static_cast<float *>(ws);
     float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
@@ -453,6 +471,41 @@ GlaArgs shape_args(int B, int H, int gh, int gw, int dk, int dv, int direction, 
                    static_cast<int64_t>(gh) * gw};
 }
 
+// ------------------------------------------------------ fixed device scratch --
+// For callers that cannot allocate: the segment states (matrix-core path) or chunk
+// states (token-serial path) of gtr_gla_fwd_noalloc live in this array, one copy per
+// device, held from module load to process end.  Host code must never take the
+// array's name as a device address: it only names the symbol.  The address on a
+// device comes from hipGetSymbolAddress, made once per device with that device
+// current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_ptr;  // device -> address of its copy of `scratch`
+
+gtr_status scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(GTR_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+        it = g_scratch_ptr.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return GTR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -489,6 +542,40 @@ gtr_status gtr_gla_fwd_events(const void *q, const void *k, const void *v, const
                             dv, direction, chunk, dtype, path, stream, mk);
     if (n_launches) *n_launches = mk.launches;
     return s;
+}
+
+gtr_status gtr_gla_fwd_noalloc(const void *q, const void *k, const void *v, const float *log_g,
+                               const void *z, const float *rms_w, void *out, int B, int H,
+                               int grid_h, int grid_w, int dk, int dv, int direction, int chunk,
+                               gtr_dtype dtype, hipStream_t stream) {
+    g_err.clear();
+    gtr_status s = check(q, k, v, log_g, z, rms_w, out, B, H, grid_h, grid_w, dk, dv, direction,
+                         chunk, dtype, GTR_PATH_AUTO);
+    if (s != GTR_OK) return s;
+    const size_t rows = static_cast<size_t>(B) * grid_h * grid_w * H;
+    const size_t eb = elem_bytes(dtype);
+    const void *ins[] = {q, k, v, log_g, z, rms_w};
+    const size_t nb[] = {rows * dk * eb, rows * dk * eb, rows * dv * eb, rows * dk * 4,
+                         rows * dv * eb, static_cast<size_t>(dv) * 4};
+    s = check_aliasing(out, rows * dv * eb, ins, nb, 6);
+    if (s != GTR_OK) return s;
+    GlaArgs a{q, k, v, log_g, z, rms_w, out, nullptr, B, H, grid_h, grid_w, dk, dv, direction,
+              chunk ? chunk : kDefaultChunk, dtype, static_cast<int64_t>(grid_h) * grid_w};
+    const int path = auto_path(a);  // matrix-core or token-serial, as gtr_gla_fwd
+    const size_t need = run_workspace_bytes(a, path);
+    if (need > kScratchBytes)
+        return fail(GTR_ERR_UNSUPPORTED,
+                    "this call needs %zu bytes of scratch; the fixed scratch holds %zu (use "
+                    "gtr_gla_fwd)",
+                    need, kScratchBytes);
+    if (!device_ok()) return GTR_ERR_HIP;
+    WsSource src;
+    s = scratch_address(&src.ptr);
+    if (s != GTR_OK) return s;
+    src.bytes = kScratchBytes;
+    Marks mk;
+    return path == GTR_PATH_MFMA ? run_mfma(a, stream, mk, nullptr, &src)
+                                 : run_serial(a, stream, mk, &src);
 }
 
 size_t gtr_gla_states_bytes(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,

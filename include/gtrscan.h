@@ -128,6 +128,26 @@ gtr_status gtr_gla_fwd_events(const void *q, const void *k, const void *v, const
                               hipStream_t stream);
 
 /*
+ * gtr_gla_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that forbid allocation after start-up,
+ * harnesses without an allocator.  Same arguments, operation, path choice
+ * (AUTO) and results, bit for bit, as gtr_gla_fwd.  It calls no hipMalloc,
+ * hipFree or other allocating routine: the per-call segment (or chunk) states
+ * live in a fixed device array of the library, 32 MiB on each device, held from
+ * the library's load until the process ends.  A call whose states would not fit
+ * (more than 32 MiB: e.g. beyond about 2000 segments at dk = dv = 64) returns
+ * GTR_ERR_UNSUPPORTED before anything is enqueued.  Nothing in the array has to
+ * start at zero: every word a call reads was written earlier in the same call.
+ * All calls on one device share the array, so calls that may overlap in time on
+ * one device (different streams without ordering between them) race and must
+ * not be issued; calls ordered on one stream are safe.
+ */
+gtr_status gtr_gla_fwd_noalloc(const void *q, const void *k, const void *v, const float *log_g,
+                               const void *z, const float *rms_w, void *out,
+                               int B, int H, int grid_h, int grid_w, int dk, int dv,
+                               int direction, int chunk, gtr_dtype dtype, hipStream_t stream);
+
+/*
  * A stack of n_blocks mixer calls (Method §1: the scan direction cycles
  * LR, RL, TB, BT with depth and grid order is restored after every block).
  * Every tensor gains a leading [n_blocks] dimension: q, k, log_g, v, z as

@@ -119,6 +119,15 @@ def test_stack_checks_paths_before_the_device():
     assert st in (_lib.GTR_ERR_HIP, _lib.GTR_OK) or torch.cuda.device_count() > 0
 
 
+def test_noalloc_refuses_calls_beyond_the_scratch():
+    # 12 sequences of 16384 tokens on the token-serial path (float32 I/O): about
+    # 50 MB of chunk states, more than the 32 MiB fixed scratch; refused before
+    # any device work (the fake pointers are never touched)
+    lib = _lib.load()
+    st = lib.gtr_gla_fwd_noalloc(*P, 1, 12, 128, 128, 64, 64, 0, 64, _lib.GTR_F32, None)
+    assert st == _lib.GTR_ERR_UNSUPPORTED and "scratch" in _lib.last_error()
+
+
 def test_unknown_path_is_rejected():
     lib = _lib.load()
     st = lib.gtr_gla_fwd_path(*P, 1, 1, 8, 8, 32, 32, 0, 0, 0, 9, None)
