@@ -167,7 +167,9 @@ void mfma_plans(const GlaArgs &a, int64_t chunks_per_wg, MfmaPlan *ps, MfmaPlan 
     const int64_t T = static_cast<int64_t>(a.B) * a.H * N;
     int64_t q1 = chunks_per_wg, q2 = chunks_per_wg;
     if (chunks_per_wg <= 0) {
-        const int64_t t1 = kSummaryWorkgroups < T ? kSummaryWorkgroups : T;
+        // dv = 128 summary workgroups (eight waves at chunk 64) also take a whole CU
+        const int64_t most1 = (a.dv == 128 && a.chunk == 64) ? kSummaryWorkgroups / 2 : kSummaryWorkgroups;
+        const int64_t t1 = most1 < T ? most1 : T;
         q1 = (T + t1 - 1) / t1;
         // dv = 128 output workgroups take a whole CU (eight waves, or four at one wave
         // per SIMD): one per CU

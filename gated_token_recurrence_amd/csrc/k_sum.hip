@@ -23,6 +23,15 @@
 // sub-block gate totals (one barrier).  At a segment's end the four partials
 // are added through LDS.
 //
+// dv = 128 runs eight waves in two value halves: waves w and w + 4 take the same
+// 16 tokens, and wave w keeps the partial of value columns [64 (w / 4),
+// 64 (w / 4) + 64) (a full-width partial would need twice the accumulators).
+// The pair splits the key channels instead: wave w reads k and log_g of
+// channels [32 (w / 4), 32 (w / 4) + 32) only, forms their gates and K~, and
+// writes K~ into an LDS area the pair shares; a second barrier per chunk then
+// lets both read all 64 channels.  So k and log_g are read once, and each wave
+// stages only its half of V.
+//
 // Low-rank gate variant (LRG): the gates come from the tokens' rank-16
 // features (Method §1: a light low-rank projection with a temperature), four
 // 16x16x16 products against the head's projection held in registers, then
@@ -40,34 +49,39 @@ template <int DT, int DV, bool RES, bool LRG>
 struct SumTile {
     static constexpr bool F16 = DT == DT_F16;
     static constexpr int C = 64, NB = 4;
-    static constexpr int ND = DV / 16;  // value tiles
-    static constexpr int NE = DV / 32;  // 16-byte value pieces per lane
-    static constexpr int VP = DV / 64;  // 64-column planes of V
+    static constexpr int CS = DV / 64;   // value halves (dv = 128: two groups of four waves)
+    static constexpr int NW = 4 * CS;    // waves
+    static constexpr int NTH = 64 * NW;  // threads
+    static constexpr int ND = 4;         // value tiles of a wave's partial (its 64 columns)
+    static constexpr int NE = 2;         // 16-byte value pieces per lane
     static constexpr int SUB = 16 * 64;  // elements of one [16 tokens][64 columns] matrix
-    // LDS (bytes): per wave K~ hi, lo and V ([16][64] each, V per plane); gate
-    // totals (two chunk buffers); per-wave tables.  The segment-end reduction
-    // reuses the start of the area for the four [64][64] fp32 partials.
-    static constexpr int WAVE_BYTES = (2 + VP) * SUB * 2;
-    static constexpr int O_W = 0;
-    static constexpr int O_TOT = O_W + 4 * WAVE_BYTES;      // float [2][NB][DK]
-    static constexpr int O_TAB = O_TOT + 2 * NB * DK * 4;   // float [4 waves][2][DK]
-    static constexpr int BYTES_MAIN = O_TAB + 4 * 2 * DK * 4;
-    static constexpr int RED_BYTES = 4 * 64 * 68 * 4;       // one 64-column plane at a time
+    static constexpr int NK = 2 / CS;    // 32-channel key blocks a wave forms (dv = 128: one)
+    // LDS (bytes): per token group K~ hi, lo ([16][64] each, shared by the group's
+    // waves); per wave V ([16][64]); gate totals (two chunk buffers); per-wave
+    // tables.  The segment-end reduction reuses the start of the area for four
+    // [64][64] fp32 partials (one value half at a time).
+    static constexpr int O_K = 0;                            // [4 groups][hi, lo][SUB]
+    static constexpr int O_V = O_K + 4 * 2 * SUB * 2;        // [NW][SUB]
+    static constexpr int O_TOT = O_V + NW * SUB * 2;         // float [2][NB][DK]
+    static constexpr int O_TAB = O_TOT + 2 * NB * DK * 4;    // float [NW waves][2][DK]
+    static constexpr int BYTES_MAIN = O_TAB + NW * 2 * DK * 4;
+    static constexpr int RED_BYTES = 4 * 64 * 68 * 4;        // one 64-column half at a time
     static constexpr int BYTES = BYTES_MAIN > RED_BYTES ? BYTES_MAIN : RED_BYTES;
 
     GlaArgs a;
     char *smem;
     uint16_t *sKh, *sKl, *sV;
     float *sTab;
-    int w, l, lr, g;
+    int w, tw, hv, l, lr, g;  // wave, its token rows [16 tw, 16 tw + 16), its value half
     // inputs of the next two chunks (register sets alternate by chunk); pr: the
     // previous block's output, added to v where v is consumed
-    uint4 pk[2][2], pv[2][NE], pr[2][RES ? NE : 1];
-    float4 pg[2][LRG ? 1 : 4];  // log_g (LRG: the gate features pf instead)
+    uint4 pk[2][NK], pv[2][NE], pr[2][RES ? NE : 1];
+    float4 pg[2][LRG ? 1 : 2 * NK];  // log_g (LRG: the gate features pf instead)
     uint2 pf[2];
     LowRankGate<DT> lg;
-    float cs[16];
-    f32x4 U[4][ND];  // U[ct][dt][r] = partial U[16 ct + 4 g + r][16 dt + lr]
+    float cs[8 * NK];  // cumulative gates of the wave's channels: 32 kap + 8 g + s, kap of its blocks
+    int kap0;          // first 32-channel key block of the wave
+    f32x4 U[4][ND];  // U[ct][dt][r] = partial U[16 ct + 4 g + r][64 hv + 16 dt + lr]
     float R;         // summed log2-gate of the segment's chunks after this one, channel l
 
     __device__ __forceinline__ void init(const GlaArgs &args, char *sm) {
@@ -75,13 +89,15 @@ struct SumTile {
         smem = sm;
         const int tid = threadIdx.x;
         w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        tw = w & 3;
+        hv = w >> 2;
         l = tid & 63;
         lr = l & 15;
         g = l >> 4;
-        uint16_t *base = reinterpret_cast<uint16_t *>(sm + O_W + w * WAVE_BYTES);
-        sKh = base;
-        sKl = base + SUB;
-        sV = base + 2 * SUB;
+        kap0 = CS == 1 ? 0 : hv;
+        sKh = reinterpret_cast<uint16_t *>(sm + O_K) + tw * 2 * SUB;
+        sKl = sKh + SUB;
+        sV = reinterpret_cast<uint16_t *>(sm + O_V) + w * SUB;
         sTab = reinterpret_cast<float *>(sm + O_TAB) + w * 2 * DK;
     }
 
@@ -90,7 +106,7 @@ struct SumTile {
     // row (its values reach only the sequence's final state, which is never used)
     __device__ __forceinline__ int64_t row_of(uint32_t b, uint32_t h, int64_t ch, int64_t &tok) const {
         const uint32_t L32 = static_cast<uint32_t>(a.L);
-        const uint32_t t0 = static_cast<uint32_t>(ch) * C + 16 * w + lr;
+        const uint32_t t0 = static_cast<uint32_t>(ch) * C + 16 * tw + lr;
         uint32_t t = t0 < L32 ? t0 : L32 - 1;
         if (a.direction & 1) t = L32 - 1 - t;
         uint32_t pos = t;
@@ -110,10 +126,10 @@ struct SumTile {
                                                      tok * kFusedGateRank + 4 * g);
         } else {
 #pragma unroll
-            for (int kap = 0; kap < 2; ++kap) {
-                const int c0 = 32 * kap + 8 * g;
-                pg[S][2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
-                pg[S][2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
+            for (int j = 0; j < NK; ++j) {
+                const int c0 = 32 * (kap0 + j) + 8 * g;
+                pg[S][2 * j] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
+                pg[S][2 * j + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
             }
         }
     }
@@ -121,12 +137,12 @@ struct SumTile {
     template <int S>
     __device__ __forceinline__ void prefetch_kv(int64_t row) {
 #pragma unroll
-        for (int kap = 0; kap < 2; ++kap)
-            pk[S][kap] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + row * DK +
-                                                       32 * kap + 8 * g);
+        for (int j = 0; j < NK; ++j)
+            pk[S][j] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + row * DK +
+                                                     32 * (kap0 + j) + 8 * g);
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-            const int d0 = 32 * e + 8 * g;
+            const int d0 = 64 * hv + 32 * e + 8 * g;
             pv[S][e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + row * DV + d0);
             if constexpr (RES)
                 pr[S][e] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.resid) + row * DV + d0);
@@ -149,21 +165,21 @@ struct SumTile {
             lg.gates(pf[buf], cs);
         } else {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
+            for (int q4 = 0; q4 < 2 * NK; ++q4) {
                 cs[4 * q4] = pg[buf][q4].x; cs[4 * q4 + 1] = pg[buf][q4].y;
                 cs[4 * q4 + 2] = pg[buf][q4].z; cs[4 * q4 + 3] = pg[buf][q4].w;
             }
         }
         row_scan(cs);
         if (lr == 15) {
-            float *tot = reinterpret_cast<float *>(smem + O_TOT) + (buf * NB + w) * DK;
+            float *tot = reinterpret_cast<float *>(smem + O_TOT) + (buf * NB + tw) * DK;
 #pragma unroll
-            for (int kap = 0; kap < 2; ++kap) {
-                float *dst = tot + 32 * kap + 8 * g;
+            for (int j = 0; j < NK; ++j) {
+                float *dst = tot + 32 * (kap0 + j) + 8 * g;
                 *reinterpret_cast<float4 *>(dst) =
-                    make_float4(cs[8 * kap], cs[8 * kap + 1], cs[8 * kap + 2], cs[8 * kap + 3]);
+                    make_float4(cs[8 * j], cs[8 * j + 1], cs[8 * j + 2], cs[8 * j + 3]);
                 *reinterpret_cast<float4 *>(dst + 4) =
-                    make_float4(cs[8 * kap + 4], cs[8 * kap + 5], cs[8 * kap + 6], cs[8 * kap + 7]);
+                    make_float4(cs[8 * j + 4], cs[8 * j + 5], cs[8 * j + 6], cs[8 * j + 7]);
             }
         }
     }
@@ -176,7 +192,7 @@ struct SumTile {
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
             const float t = tot[J * DK + l];
-            if (J < w) r_l += t;
+            if (J < tw) r_l += t;
             tot_l += t;
         }
         tot_l *= kLog2e;
@@ -184,17 +200,17 @@ struct SumTile {
         R += tot_l;
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int kap = 0; kap < 2; ++kap) {
-            const int c0 = 32 * kap + 8 * g;
+        for (int j = 0; j < NK; ++j) {
+            const int c0 = 32 * (kap0 + j) + 8 * g;
             float gr[8], kt[8];
 #pragma unroll
             for (int h4 = 0; h4 < 2; ++h4) {
                 const float4 x = *reinterpret_cast<const float4 *>(sTab + c0 + 4 * h4);
                 gr[4 * h4] = x.x; gr[4 * h4 + 1] = x.y; gr[4 * h4 + 2] = x.z; gr[4 * h4 + 3] = x.w;
             }
-            unpack8<DT>(pk[buf][kap], kt);
+            unpack8<DT>(pk[buf][j], kt);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) kt[s] *= fexp2(fmaf(-cs[8 * kap + s], kLog2e, gr[s]));
+            for (int s = 0; s < 8; ++s) kt[s] *= fexp2(fmaf(-cs[8 * j + s], kLog2e, gr[s]));
             uint32_t hi[4], lo[4];
             split_pk<F16>(kt, hi, lo);
             const int off = swn(lr, c0);
@@ -203,10 +219,10 @@ struct SumTile {
         }
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-            const int d0 = 32 * e + 8 * g;
+            const int d0 = 32 * e + 8 * g;  // column within the wave's half
             uint4 x = pv[buf][e];
             if constexpr (RES) x = add_io<DT>(x, pr[buf][e]);  // stack residual
-            *reinterpret_cast<uint4 *>(sV + (d0 >> 6) * SUB + swn(lr, d0 & 63)) = x;
+            *reinterpret_cast<uint4 *>(sV + swn(lr, d0)) = x;
         }
     }
 
@@ -220,7 +236,7 @@ struct SumTile {
     __device__ __forceinline__ void accumulate() {
         s16x4 bv[ND];
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) bv[dt] = op16(sV + (dt >> 2) * SUB, 16 * (dt & 3));
+        for (int dt = 0; dt < ND; ++dt) bv[dt] = op16(sV, 16 * dt);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             const s16x4 ah = op16(sKh, 16 * ct);
@@ -233,29 +249,30 @@ struct SumTile {
         }
     }
 
-    // segment end: the four partials added through LDS, one 64-column plane at a
-    // time ([wave][column][channel], rows padded to 68 floats); wave w then sums
-    // channels [16 w, 16 w + 16) for every column (lane = column) and stores them
-    // as whole 256-byte rows
+    // segment end: the four token partials of each value half added through LDS,
+    // one half at a time ([token group][column][channel], rows padded to 68
+    // floats); every wave then sums 64 / NW channels for every column of that half
+    // (lane = column) and stores them as whole 256-byte rows
     __device__ __forceinline__ void finish(float *dst, float *gdst) {
         constexpr int RS = 68;
+        constexpr int CH = 64 / NW;  // channels summed per wave
         float *red = reinterpret_cast<float *>(smem);  // [4][64 columns][RS]
 #pragma unroll
-        for (int pl = 0; pl < VP; ++pl) {
-            __syncthreads();  // the LDS area is free (operands, previous plane)
-            {
-                float *m = red + w * 64 * RS + lr * RS + 4 * g;
+        for (int h = 0; h < CS; ++h) {
+            __syncthreads();  // the LDS area is free (operands, previous half)
+            if (hv == h) {
+                float *m = red + tw * 64 * RS + lr * RS + 4 * g;
 #pragma unroll
                 for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct)
-                        *reinterpret_cast<f32x4 *>(m + 16 * d4 * RS + 16 * ct) = U[ct][4 * pl + d4];
+                        *reinterpret_cast<f32x4 *>(m + 16 * d4 * RS + 16 * ct) = U[ct][d4];
             }
             __syncthreads();
-            const float *m = red + l * RS + 16 * w;
-            float sum[16];
+            const float *m = red + l * RS + CH * w;
+            float sum[CH];
 #pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
+            for (int j4 = 0; j4 < CH / 4; ++j4) {
                 f32x4 x = *reinterpret_cast<const f32x4 *>(m + 4 * j4);
 #pragma unroll
                 for (int q = 1; q < 4; ++q) {
@@ -265,9 +282,9 @@ struct SumTile {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sum[4 * j4 + r] = x[r];
             }
-            float *o = dst + (16 * w) * DV + 64 * pl + l;
+            float *o = dst + (CH * w) * DV + 64 * h + l;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[j * DV] = sum[j];
+            for (int j = 0; j < CH; ++j) o[j * DV] = sum[j];
         }
         if (w == 0) gdst[l] = R;
         __syncthreads();  // the LDS area is rewritten by the next chunk
@@ -275,9 +292,10 @@ struct SumTile {
 };
 
 template <int DT, int DV, bool RES, bool LRG>
-__global__ __launch_bounds__(NT, 2) void k_sum(GlaArgs a, float *__restrict__ Uo, float *__restrict__ Gs,
-                                              MfmaPlan pl) {
+__global__ __launch_bounds__(64 * 4 * (DV / 64), DV == 64 ? 2 : 1) void k_sum(GlaArgs a, float *__restrict__ Uo,
+                                                                             float *__restrict__ Gs, MfmaPlan pl) {
     using T = SumTile<DT, DV, RES, LRG>;
+    static_assert(T::NTH == 64 * 4 * (DV / 64), "launch bounds");
     __shared__ __attribute__((aligned(16))) char smem[T::BYTES];
     T t;
     t.init(a, smem);
@@ -340,6 +358,7 @@ __global__ __launch_bounds__(NT, 2) void k_sum(GlaArgs a, float *__restrict__ Uo
         __syncthreads();  // the chunk's sub-block totals
         t.template stage<S>();
         t.template prefetch_kv<S>(row);  // k and v are consumed
+        if constexpr (T::CS == 2) __syncthreads();  // the pair's two halves of K~
         t.accumulate();
         const bool seg_start = p == p0 || cur.ch == 0;
         if (seg_start) {  // the segment's first chunk: its summary is complete
@@ -366,13 +385,18 @@ __global__ __launch_bounds__(NT, 2) void k_sum(GlaArgs a, float *__restrict__ Uo
 template <int DT, int DV>
 hipError_t launch_sum(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(ps.n_wg));
-    if (a.feat) {  // gates from rank-16 features, no residual
-        if (a.resid || a.rank != kFusedGateRank) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k_sum<DT, DV, false, true>), grid, dim3(NT), 0, st, a, U, G, ps);
+    const dim3 block(64 * 4 * (DV / 64));
+    if (a.feat) {  // gates from rank-16 features, dv = 64, no residual
+        if constexpr (DV == 64) {
+            if (a.resid || a.rank != kFusedGateRank) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((k_sum<DT, DV, false, true>), grid, block, 0, st, a, U, G, ps);
+        } else {
+            return hipErrorInvalidValue;
+        }
     } else if (a.resid) {
-        hipLaunchKernelGGL((k_sum<DT, DV, true, false>), grid, dim3(NT), 0, st, a, U, G, ps);
+        hipLaunchKernelGGL((k_sum<DT, DV, true, false>), grid, block, 0, st, a, U, G, ps);
     } else {
-        hipLaunchKernelGGL((k_sum<DT, DV, false, false>), grid, dim3(NT), 0, st, a, U, G, ps);
+        hipLaunchKernelGGL((k_sum<DT, DV, false, false>), grid, block, 0, st, a, U, G, ps);
     }
     return hipGetLastError();
 }
@@ -380,14 +404,15 @@ hipError_t launch_sum(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, 
 }  // namespace
 
 bool sum_supported(const GlaArgs &a) {
-    // dv = 128 would need more registers than two workgroups per CU allow
-    return (a.dtype == DT_F16 || a.dtype == DT_BF16) && a.dk == DK && a.dv == 64 && a.chunk == 64;
+    return (a.dtype == DT_F16 || a.dtype == DT_BF16) && a.dk == DK && (a.dv == 64 || a.dv == 128) &&
+           a.chunk == 64;
 }
 
 hipError_t sum_launch(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t s) {
-    if (a.dv != 64) return hipErrorInvalidValue;
-    if (a.dtype == DT_F16) return launch_sum<DT_F16, 64>(a, ps, U, G, s);
-    if (a.dtype == DT_BF16) return launch_sum<DT_BF16, 64>(a, ps, U, G, s);
+    if (a.dtype == DT_F16) return a.dv == 64 ? launch_sum<DT_F16, 64>(a, ps, U, G, s)
+                                             : launch_sum<DT_F16, 128>(a, ps, U, G, s);
+    if (a.dtype == DT_BF16) return a.dv == 64 ? launch_sum<DT_BF16, 64>(a, ps, U, G, s)
+                                              : launch_sum<DT_BF16, 128>(a, ps, U, G, s);
     return hipErrorInvalidValue;
 }
 
