@@ -30,10 +30,13 @@
 // 16 tokens, wave w takes the value columns [64 (w / 4), 64 (w / 4) + 64) of
 // them and state tile w, so each wave holds what a dv = 64 wave holds (the
 // four-wave form would need about 450 registers per lane, one wave per SIMD).
-// Both halves form Q~ and the score tiles; each forms K^ for 32 of the 64 key
-// channels.  The RMSNorm sum over all 128 columns is completed through LDS:
-// each half puts its tokens' partial sums before the end-of-chunk barrier and
-// both add the two in the same order.
+// The pair splits the key channels: wave w reads q, k and log_g of channels
+// [32 (w / 4), 32 (w / 4) + 32) only and forms their gates, Q~ and K^; its half
+// of Q~ goes to an LDS area the pair shares, from which each wave takes the
+// other half after the second barrier.  Both halves form the score tiles.  The
+// RMSNorm sum over all 128 columns is completed through LDS: each half puts its
+// tokens' partial sums before the end-of-chunk barrier and both add the two in
+// the same order.
 //
 // Low-rank gate variant (LRG): instead of reading log_g, each wave forms its
 // tokens' gates from their rank-16 features (Method §1: a light low-rank
@@ -84,6 +87,7 @@ struct RowTile {
     static constexpr int VP = DV / 64;  // 64-column planes of V
     static constexpr int NV = (DT == DT_F16) ? 2 : 1;  // V as bf16 hi (+ lo for fp16)
     static constexpr int NE = 2;        // 16-byte value pieces per lane of its half (epilogue, V loads)
+    static constexpr int NK = 2 / CS;   // 32-channel key blocks whose q, k, gates a wave forms
     static constexpr int MAT = C * 64;
     // LDS carve-up (bytes).  Token-serial chunks reuse K (raw q, k) and S (fp32
     // gates, then the output exchange).
@@ -94,26 +98,37 @@ struct RowTile {
     static constexpr int O_TAB = O_TOT + NB * DK * 4;       // float [NW waves][2][DK]
     static constexpr int O_RW = O_TAB + NW * 2 * DK * 4;    // float [DV]
     static constexpr int O_SS = O_RW + DV * 4;              // float [CS][C]: halves' sums of squares
-    static constexpr int O_GATE = O_SS + CS * C * 4;        // low-rank gate weights (LRG)
+    static constexpr int O_QP = O_SS + CS * C * 4;          // Q~ hi, lo per token group (dv = 128)
+    static constexpr int O_GATE = O_QP + (CS == 2 ? 4 * 2 * 16 * 64 * 2 : 0);  // low-rank gate weights (LRG)
     static constexpr int BYTES = O_GATE + (LRG ? LowRankGate<DT>::LDS_BYTES : 0);
     static_assert(C * DK * 4 <= 2 * DV * 64 * 2, "fp32 gates must fit the state area");
     static_assert(ND * 4 * 64 * 16 <= 2 * DV * 64 * 2, "output exchange must fit the state area");
 
     GlaArgs a;
-    uint16_t *sK, *sV, *sS;
+    uint16_t *sK, *sV, *sS, *sQ;
     float *sTot, *sTab, *sRw, *sSS;
     char *sGate;
     int w, tw, hv, l, lr, g;  // wave, its token rows [16 tw, 16 tw + 16), its value half
+    int kap0;                 // first 32-channel key block of the wave (0 at dv = 64)
+
+    // register-array element i, i uniform across the wave but not a compile-time
+    // constant: selected by branches, so the array stays in registers
+    __device__ __forceinline__ static void put2(s16x8 (&x)[2], int i, s16x8 v) {
+        if (i == 0)
+            x[0] = v;
+        else
+            x[1] = v;
+    }
 
     // this lane's token: rows (negative = past the end, ~row of the last token) and
     // token indices b L + grid position (of the row read)
     int64_t rowC, rowN, tokC, tokN;
     // next chunk's inputs of this lane's token
-    uint4 pq[2], pk[2], pv[NE], pz[NE];
+    uint4 pq[NK], pk[NK], pv[NE], pz[NE];
     uint4 pr[RES ? NE : 1];  // previous block's output, added to v where v is consumed
-    float4 pg[LRG ? 1 : 4];  // log_g (LRG: the gate features pf instead)
+    float4 pg[LRG ? 1 : 2 * NK];  // log_g (LRG: the gate features pf instead)
     uint2 pf;
-    float cs[16];
+    float cs[8 * NK];  // cumulative gates of channels 32 kap + 8 g + s for the wave's blocks
     // state tiles (S[s][ct][r] = S[16 ct + 4 g + r][dcol(NS w + s, lr)]) and the
     // output tiles of this wave's tokens in its half (O[e][r] = O^T[dcol(NDW hv + e, 4 g + r)][token lr])
     f32x4 S[NS][4];
@@ -133,6 +148,8 @@ struct RowTile {
         w = __builtin_amdgcn_readfirstlane(tid >> 6);
         tw = CS == 1 ? w : w & 3;
         hv = CS == 1 ? 0 : w >> 2;
+        kap0 = CS == 1 ? 0 : hv;
+        sQ = reinterpret_cast<uint16_t *>(smem + O_QP) + tw * 2 * 16 * 64;
         l = tid & 63;
         lr = l & 15;
         g = l >> 4;
@@ -168,10 +185,10 @@ struct RowTile {
                                                   tok * kFusedGateRank + 4 * g);
         } else {
 #pragma unroll
-            for (int kap = 0; kap < 2; ++kap) {
-                const int c0 = 32 * kap + 8 * g;
-                pg[2 * kap] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
-                pg[2 * kap + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
+            for (int j = 0; j < NK; ++j) {
+                const int c0 = 32 * (kap0 + j) + 8 * g;
+                pg[2 * j] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0);
+                pg[2 * j + 1] = *reinterpret_cast<const float4 *>(a.log_g + row * DK + c0 + 4);
             }
         }
 #pragma unroll
@@ -186,10 +203,10 @@ struct RowTile {
     __device__ __forceinline__ void prefetch_qk(int64_t rw) {
         const int64_t row = live(rw);
 #pragma unroll
-        for (int kap = 0; kap < 2; ++kap) {
-            const int c0 = 32 * kap + 8 * g;
-            pq[kap] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + row * DK + c0);
-            pk[kap] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + row * DK + c0);
+        for (int j = 0; j < NK; ++j) {
+            const int c0 = 32 * (kap0 + j) + 8 * g;
+            pq[j] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + row * DK + c0);
+            pk[j] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + row * DK + c0);
         }
     }
 
@@ -244,20 +261,20 @@ struct RowTile {
             LowRankGate<DT>::gates_lds(sGate, l, g, a.inv_tau, pf, cs);
         } else {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
+            for (int q4 = 0; q4 < 2 * NK; ++q4) {
                 cs[4 * q4] = pg[q4].x; cs[4 * q4 + 1] = pg[q4].y;
                 cs[4 * q4 + 2] = pg[q4].z; cs[4 * q4 + 3] = pg[q4].w;
             }
         }
         row_scan(cs);
-        if (lr == 15 && hv == 0) {
+        if (lr == 15) {
 #pragma unroll
-            for (int kap = 0; kap < 2; ++kap) {
-                float *dst = sTot + tw * DK + 32 * kap + 8 * g;
+            for (int j = 0; j < NK; ++j) {
+                float *dst = sTot + tw * DK + 32 * (kap0 + j) + 8 * g;
                 *reinterpret_cast<float4 *>(dst) =
-                    make_float4(cs[8 * kap], cs[8 * kap + 1], cs[8 * kap + 2], cs[8 * kap + 3]);
+                    make_float4(cs[8 * j], cs[8 * j + 1], cs[8 * j + 2], cs[8 * j + 3]);
                 *reinterpret_cast<float4 *>(dst + 4) =
-                    make_float4(cs[8 * kap + 4], cs[8 * kap + 5], cs[8 * kap + 6], cs[8 * kap + 7]);
+                    make_float4(cs[8 * j + 4], cs[8 * j + 5], cs[8 * j + 6], cs[8 * j + 7]);
             }
         }
         const int i = 16 * tw + lr;
@@ -304,11 +321,12 @@ struct RowTile {
         __builtin_amdgcn_wave_barrier();
         const int i = 16 * tw + lr;
 #pragma unroll
-        for (int kap = 0; kap < 2; ++kap) {
+        for (int j = 0; j < NK; ++j) {
+            const int kap = CS == 1 ? j : kap0;
             const int c0 = 32 * kap + 8 * g;
-            // the two halves of a dv = 128 workgroup share K^ and the token-serial
+            // the two halves of a dv = 128 workgroup share Q~, K^ and the token-serial
             // operands: half hv forms those of the channels [32 hv, 32 hv + 32)
-            const bool mine = CS == 1 || kap == hv;
+            constexpr bool mine = true;
             if (!slow) {
                 float rI[8];
 #pragma unroll
@@ -317,19 +335,29 @@ struct RowTile {
                     rI[4 * h4] = x.x; rI[4 * h4 + 1] = x.y; rI[4 * h4 + 2] = x.z; rI[4 * h4 + 3] = x.w;
                 }
                 float qt[8], aa[8];
-                unpack8<DT>(pq[kap], qt);
+                unpack8<DT>(pq[j], qt);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    aa[s] = fmaf(cs[8 * kap + s], kLog2e, rI[s]);
+                    aa[s] = fmaf(cs[8 * j + s], kLog2e, rI[s]);
                     qt[s] *= fexp2(aa[s]);  // q 2^a
                 }
                 uint32_t qhi[4], qlo[4];
                 split_pk<false>(qt, qhi, qlo);
-                qh[kap] = __builtin_bit_cast(s16x8, u4(qhi));
-                ql[kap] = __builtin_bit_cast(s16x8, u4(qlo));
+                if constexpr (CS == 1) {
+                    qh[kap] = __builtin_bit_cast(s16x8, u4(qhi));
+                    ql[kap] = __builtin_bit_cast(s16x8, u4(qlo));
+                } else {
+                    put2(qh, kap, __builtin_bit_cast(s16x8, u4(qhi)));
+                    put2(ql, kap, __builtin_bit_cast(s16x8, u4(qlo)));
+                }
+                if constexpr (CS == 2) {  // the pair's other half reads it after the barrier
+                    const int off = lr * 64 + (((4 * kap + g) ^ (lr & 7)) << 3);
+                    *reinterpret_cast<uint4 *>(sQ + off) = u4(qhi);
+                    *reinterpret_cast<uint4 *>(sQ + 16 * 64 + off) = u4(qlo);
+                }
                 if (mine) {
                     float kh[8];
-                    unpack8<DT>(pk[kap], kh);
+                    unpack8<DT>(pk[j], kh);
 #pragma unroll
                     for (int s = 0; s < 8; ++s) kh[s] *= fexp2(-aa[s]);  // k 2^-a
                     uint32_t khi[4], klo[4];
@@ -341,21 +369,31 @@ struct RowTile {
             } else if (mine) {
                 // token-serial operands, [token][channel] without swizzle: q and k as
                 // stored (K area), g = 2^(a_i - a_{i-1}) in fp32 (state area)
-                *reinterpret_cast<uint4 *>(sK + i * DK + c0) = pq[kap];
-                *reinterpret_cast<uint4 *>(sK + MAT + i * DK + c0) = pk[kap];
+                *reinterpret_cast<uint4 *>(sK + i * DK + c0) = pq[j];
+                *reinterpret_cast<uint4 *>(sK + MAT + i * DK + c0) = pk[j];
                 float *fG = reinterpret_cast<float *>(sS);
                 float gg[8];
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    const float up = __shfl_up(cs[8 * kap + s], 1, 16);
+                    const float up = __shfl_up(cs[8 * j + s], 1, 16);
                     const float prev = (lr == 0) ? 0.f : up;
-                    gg[s] = fexp2((cs[8 * kap + s] - prev) * kLog2e);
+                    gg[s] = fexp2((cs[8 * j + s] - prev) * kLog2e);
                 }
                 *reinterpret_cast<float4 *>(fG + i * DK + c0) = make_float4(gg[0], gg[1], gg[2], gg[3]);
                 *reinterpret_cast<float4 *>(fG + i * DK + c0 + 4) = make_float4(gg[4], gg[5], gg[6], gg[7]);
             }
         }
         return slow;
+    }
+
+    // dv = 128 (after the second barrier): the other half of Q~ from the pair's area
+    __device__ __forceinline__ void partner_q() {
+        if constexpr (CS == 2) {
+            const int kap = 1 - hv;
+            const int off = lr * 64 + (((4 * kap + g) ^ (lr & 7)) << 3);
+            put2(qh, kap, *reinterpret_cast<const s16x8 *>(sQ + off));
+            put2(ql, kap, *reinterpret_cast<const s16x8 *>(sQ + 16 * 64 + off));
+        }
     }
 
     // V^T operand of value tile dd, V part p: lane row / column dcol(dd, lr), k
@@ -645,11 +683,13 @@ __global__ __launch_bounds__(64 * 4 * (DV / 64), DV == 64 ? 2 : 1) void k_rows(G
             t.prefetch_gv(t.rowN, t.tokN);  // phase 1 consumed the gates and v
             const bool slow = t.phase2();
             t.prefetch_qk(t.rowN);  // phase 2 consumed q and k
-            __syncthreads();  // B2: K^
-            if (!slow)
+            __syncthreads();  // B2: K^ (and the pair's halves of Q~)
+            if (!slow) {
+                t.partner_q();
                 t.compute();
-            else
+            } else {
                 t.serial();
+            }
             if constexpr (R::CS == 1) {
                 t.epilogue();
                 t.prefetch_z(t.rowN);
