@@ -490,6 +490,7 @@ def cpu_baseline(w: W.Workload, x: dict, target_s: float = 12.0, single_s: float
         oracle.set_threads(all_threads)
     return {"value": w.tokens / per_call, "unit": "tokens/s", "cores": all_threads,
             "kind": "oracle", "sample": sample, "us_per_call": per_call * 1e6,
+            "cpu_model": cpu_model(),
             "single_thread": {"value": w.tokens / per_one, "unit": "tokens/s", "cores": 1,
                               "sample": sample_one, "us_per_call": per_one * 1e6}}
 
@@ -507,17 +508,6 @@ def kernel_sources_hash():
         h.update(os.path.basename(p).encode())
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
-
-
-def traffic_record(path_name, workload):
-    p = os.path.join(ROOT, "profiles", f"traffic_{path_name}_{workload}.json")
-    if not os.path.exists(p):
-        return None
-    with open(p) as f:
-        rec = json.load(f)
-    if rec.get("sources_hash") != kernel_sources_hash():
-        return None  # the kernels changed since the counters were taken
-    return rec
 
 
 PATH_NAMES = {g.PATH_AUTO: "auto", g.PATH_MFMA: "mfma", g.PATH_FAST: "fast",
@@ -568,6 +558,13 @@ KERNEL_KEYS = {  # launch name -> test on the kernel symbol
     "fast_single_launch": lambda n: "k_fast" in n,
 }
 
+# SQ and GRBM counters taken in one pass (the hardware collects at most 8 SQ
+# counters at once): instruction mix, matrix-core and VALU activity, GPU busy
+# cycles for the utilisation fractions.
+SQ_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS "
+               "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+CU_COUNT, SIMDS_PER_CU, XCD_COUNT = 256, 4, 8
+
 
 def _counter_values(csv_path):
     """Per (kernel, counter) list of per-dispatch values from a rocprofv3
@@ -593,29 +590,76 @@ def _mean(v):
     return sum(v) / len(v)
 
 
-def ingest_counters(fetch_csv, write_csv, workload, path_name, kernel):
-    """Writes profiles/traffic_<path>_<workload>.json from two counter runs of
-    ``bench.py --profile-run`` (FETCH_SIZE, then WRITE_SIZE).  Each counter is
-    scaled by the ratio of the calibration copy's known bytes to what the same
-    counter read for it."""
+def ingest_counters(fetch_csv, write_csv, sq_csv, workload, path_name, launches):
+    """Writes profiles/counters_<path>_<workload>.json from three counter runs of
+    ``bench.py --profile-run`` (FETCH_SIZE; WRITE_SIZE; the SQ/GRBM set above).
+    FETCH_SIZE and WRITE_SIZE are scaled by the ratio of the calibration copy's
+    known bytes to what the same counter read for it; per launch of the call and
+    summed over the call.  Utilisation: matrix-core busy cycles over the GPU's busy
+    cycles times its SIMDs (rocprofv3's MfmaUtil); VALU: the VALU-active count over
+    the busy cycles times the CUs (rocprofv3's VALUBusy)."""
     fetch, write = _counter_values(fetch_csv), _counter_values(write_csv)
-    # the calibration copy is the largest copy dispatch (uploads of inputs are smaller)
+    sq = _counter_values(sq_csv) if sq_csv else {}
     copy_f = _find(fetch, "FETCH_SIZE", "copyBuffer", max) * 1024
     copy_w = _find(write, "WRITE_SIZE", "copyBuffer", max) * 1024
     f_scale, w_scale = COPY_BYTES / copy_f, COPY_BYTES / copy_w
-    kf = _find(fetch, "FETCH_SIZE", KERNEL_KEYS[kernel], _mean) * 1024 * f_scale
-    kw = _find(write, "WRITE_SIZE", KERNEL_KEYS[kernel], _mean) * 1024 * w_scale
-    rec = {"workload": workload, "path": path_name, "kernel": kernel,
-           "fetch_bytes_per_launch": round(kf), "write_bytes_per_launch": round(kw),
-           "bytes_per_launch": round(kf + kw),
+    per = {}
+    for name in launches:
+        key = KERNEL_KEYS[name]
+        kf = _find(fetch, "FETCH_SIZE", key, _mean) * 1024 * f_scale
+        kw = _find(write, "WRITE_SIZE", key, _mean) * 1024 * w_scale
+        rec = {"fetch_bytes": round(kf), "write_bytes": round(kw), "bytes": round(kf + kw)}
+        if sq:
+            c = {cn: _find(sq, cn, key, _mean) for cn in SQ_COUNTERS.split()}
+            waves = c["SQ_WAVES"]
+            # GRBM_GUI_ACTIVE comes summed over the XCDs: per XCD it is the kernel's
+            # busy clock count (rocprofv3's MfmaUtil and VALUBusy take its maximum)
+            gui = c["GRBM_GUI_ACTIVE"] / XCD_COUNT
+            rec.update({
+                "valu_insts_per_wave": round(c["SQ_INSTS_VALU"] / waves, 1),
+                "trans_insts_per_wave": round(c["SQ_INSTS_VALU_TRANS_F32"] / waves, 1),
+                "mfma_insts_per_wave": round(c["SQ_INSTS_MFMA"] / waves, 1),
+                "lds_insts_per_wave": round(c["SQ_INSTS_LDS"] / waves, 1),
+                "busy_us_at_2400mhz": round(gui / 2400.0, 2),
+                # rocprofv3's MfmaUtil and VALUBusy, as fractions
+                "mfma_busy_frac": round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * CU_COUNT * SIMDS_PER_CU), 4),
+                "valu_busy_frac": round(c["SQ_ACTIVE_INST_VALU"] / (gui * CU_COUNT), 4),
+                "raw": {cn: round(v, 1) for cn, v in c.items()}})
+        per[name] = rec
+    out = {"workload": workload, "path": path_name, "launches": per,
+           "call_fetch_bytes": sum(r["fetch_bytes"] for r in per.values()),
+           "call_write_bytes": sum(r["write_bytes"] for r in per.values()),
+           "call_bytes": sum(r["bytes"] for r in per.values()),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "calibration_copy_bytes": COPY_BYTES, "sources_hash": kernel_sources_hash(),
-           "fetch_csv": os.path.relpath(fetch_csv, ROOT), "write_csv": os.path.relpath(write_csv, ROOT)}
-    out = os.path.join(ROOT, "profiles", f"traffic_{path_name}_{workload}.json")
-    with open(out, "w") as f:
-        json.dump(rec, f, indent=1)
+           "csv": [os.path.relpath(p, ROOT) for p in (fetch_csv, write_csv, sq_csv) if p]}
+    path = os.path.join(ROOT, "profiles", f"counters_{path_name}_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
         f.write("\n")
-    print(json.dumps(rec))
+    print(json.dumps(out))
+
+
+def counters_record(path_name, workload):
+    p = os.path.join(ROOT, "profiles", f"counters_{path_name}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("sources_hash") != kernel_sources_hash():
+        return None  # the kernels changed since the counters were taken
+    return rec
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -631,16 +675,19 @@ def main():
     ap.add_argument("--profile-run", action="store_true",
                     help="for rocprofv3 counter passes: a plain 256 MiB device copy (the "
                          "calibration kernel), then --steps calls of the workload; no timing")
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the traffic record for --workload from two rocprofv3 counter "
-                         "CSVs of --profile-run (FETCH_SIZE, WRITE_SIZE); no GPU needed")
-    ap.add_argument("--kernel", default="chunk_output",
-                    help="launch whose traffic --ingest-counters records")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="CSV",
+                    help="write the counter record for --workload from the rocprofv3 counter "
+                         "CSVs of --profile-run: FETCH_SIZE, WRITE_SIZE and optionally the SQ "
+                         "set (bench.SQ_COUNTERS); no GPU needed")
     args = ap.parse_args()
     if args.ingest_counters:
+        if len(args.ingest_counters) not in (2, 3):
+            raise SystemExit("--ingest-counters takes FETCH_CSV WRITE_CSV [SQ_CSV]")
         wi = W.WORKLOADS[args.workload]
         pn = PATH_NAMES[resolve_path(wi, args.path, args.chunk or wi.chunk)]
-        ingest_counters(*args.ingest_counters, args.workload, pn, args.kernel)
+        f_csv, w_csv = args.ingest_counters[:2]
+        sq_csv = args.ingest_counters[2] if len(args.ingest_counters) == 3 else None
+        ingest_counters(f_csv, w_csv, sq_csv, args.workload, pn, LAUNCH_NAMES[pn])
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -670,26 +717,46 @@ def main():
     us = res["us_per_call"]
     value = w.tokens / (us * 1e-6)
     names = LAUNCH_NAMES[pname]
-    dom = int(np.argmax(res["launch_us_mean"]))
-    dom_us = res["launch_us_mean"][dom]
+    launch_us = res["launch_us_mean"]
+    dom = int(np.argmax(launch_us))
+    dom_us = launch_us[dom]
+    # The dominant kernel (chunk outputs) reads every input and writes the output: its
+    # algorithmic bytes per launch are the call's.  The call as a whole is the bar the
+    # method is judged on: both are reported, the call under "whole_call".
     achieved = comp / (dom_us * 1e-6) / 1e9
-    tr = traffic_record(pname, w.name)
-    traffic = None
-    if tr is not None and tr.get("kernel") == names[dom]:
-        traffic = tr.get("bytes_per_launch")
+    call_achieved = comp / (us * 1e-6) / 1e9
+    cr = counters_record(pname, w.name)
+    traffic = call_traffic = None
+    mfma_meas = valu_meas = mfma_call = None
+    if cr is not None:
+        lr = cr["launches"]
+        if names[dom] in lr:
+            traffic = lr[names[dom]]["bytes"]
+            mfma_meas = lr[names[dom]].get("mfma_busy_frac")
+            valu_meas = lr[names[dom]].get("valu_busy_frac")
+        call_traffic = cr["call_bytes"]
+        if all("mfma_busy_frac" in lr.get(n, {}) for n in names):
+            mfma_call = sum(lr[n]["mfma_busy_frac"] * t for n, t in zip(names, launch_us)) / sum(launch_us)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": names[dom], "kernel_us": round(dom_us, 3),
                 "algorithmic_bytes": comp,
-                "whole_call_frac": round(comp / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "mfma_frac_algorithmic": round(w.algorithmic_flops(chunk) / (us * 1e-6) / 1e12
-                                               / MFMA_BF16_PEAK_TFLOPS, 5)}
+                "whole_call": {"us": round(us, 3), "achieved": round(call_achieved, 1),
+                               "frac": round(call_achieved / HBM_PEAK_GBS, 4),
+                               "traffic": call_traffic},
+                "whole_call_frac": round(call_achieved / HBM_PEAK_GBS, 4),
+                "mfma_util": {"measured_kernel": mfma_meas,
+                              "measured_call": round(mfma_call, 4) if mfma_call is not None else None,
+                              "algorithmic_call": round(w.algorithmic_flops(chunk) / (us * 1e-6)
+                                                        / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                              "peak_tflops": MFMA_BF16_PEAK_TFLOPS},
+                "valu_busy_kernel": valu_meas}
     extra = {}
     if not args.no_extra:
         for name in ("mixer_640", "mixer_640_wide"):
             we = W.WORKLOADS[name]
             pa = resolve_path(we, args.path, we.chunk)
-            for pe in dict.fromkeys([pa, g.PATH_FAST]):
+            for pe in dict.fromkeys([pa, g.PATH_MFMA, g.PATH_FAST]):
                 key = name if pe == pa else f"{name}@{PATH_NAMES[pe]}"
                 try:
                     _, r = time_workload(we, dev, hip, sp, args.steps, args.warmup, pe, we.chunk,

@@ -296,11 +296,18 @@ bool fast_ok(const GlaArgs &a) {
     return a.B == 1 && a.L <= kFastMaxTokens;
 }
 
-// AUTO takes the matrix-core path for 16-bit I/O at its shapes with 16-byte
-// aligned rows and the token-serial path otherwise.  The single-launch path is
-// taken only when asked for: on MI355X the three-launch path is measured faster
-// at 1.6K tokens too, because per-chunk latency, not launch overhead, bounds both.
-int auto_path(const GlaArgs &a) { return mfma_ok(a) ? GTR_PATH_MFMA : GTR_PATH_SERIAL; }
+// AUTO takes the single-launch path for batch-one calls of at most kFastAutoChunks
+// chunks per sequence (measured on MI355X: it wins there, by 7 us at one chunk,
+// and loses from about 20 chunks on, where each chunk's fold of every earlier
+// chunk's summary dominates), the matrix-core path for the other 16-bit calls at
+// its shapes with 16-byte aligned rows, and the token-serial path otherwise.
+constexpr int64_t kFastAutoChunks = 16;
+
+int auto_path(const GlaArgs &a) {
+    const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
+    if (!a.feat && !a.resid && fast_ok(a) && n_chunks <= kFastAutoChunks) return GTR_PATH_FAST;
+    return mfma_ok(a) ? GTR_PATH_MFMA : GTR_PATH_SERIAL;
+}
 
 // Resolves AUTO and checks that an explicit path can take the arguments (before
 // anything touches the device).
@@ -561,7 +568,8 @@ gtr_status gtr_gla_fwd_noalloc(const void *q, const void *k, const void *v, cons
     if (s != GTR_OK) return s;
     GlaArgs a{q, k, v, log_g, z, rms_w, out, nullptr, B, H, grid_h, grid_w, dk, dv, direction,
               chunk ? chunk : kDefaultChunk, dtype, static_cast<int64_t>(grid_h) * grid_w};
-    const int path = auto_path(a);  // matrix-core or token-serial, as gtr_gla_fwd
+    // matrix-core or token-serial (the single-launch path needs the library's counters)
+    const int path = mfma_ok(a) ? GTR_PATH_MFMA : GTR_PATH_SERIAL;
     const size_t need = run_workspace_bytes(a, path);
     if (need > kScratchBytes)
         return fail(GTR_ERR_UNSUPPORTED,

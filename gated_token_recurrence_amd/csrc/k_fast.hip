@@ -19,7 +19,9 @@
 // whatever else runs on the device (the waits are also bounded).  The last
 // workgroup of a sequence to finish clears that sequence's flags, and the last
 // workgroup of the launch clears the ticket counters, so the next launch (or
-// graph replay) starts from zero.
+// graph replay) starts from zero.  A wait that gives up (after far longer than
+// any real wait) makes the chunk's incoming state NaN, so its outputs show it
+// instead of being silently wrong.
 #include "mfma_common.hpp"
 
 namespace gtr {
@@ -44,6 +46,7 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
     unsigned *ticket = cnt, *finished = cnt + 1, *seq_done = cnt + 2, *ready = cnt + 2 + n_seq;
     // the ticket is passed through the first LDS word (Q~ tile, first written in phase 2)
     int *s_ticket = reinterpret_cast<int *>(smem);
+    __shared__ int s_gave_up;
     if (t.tid == 0)
         *s_ticket = static_cast<int>(
             __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -68,19 +71,21 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
             t.s_update();
         else
             t.serial();  // token by token from zero: the final state is the summary
-        t.store_state(U + p * dd);
-        if (t.w == 0) Gs[static_cast<int64_t>(p) * DK + t.l] = fexp2(gam);
-        __syncthreads();  // every thread's summary stores are issued
-        if (t.tid == 0) {
-            // agent-scope release: this XCD's L2 is written back once, then the flag
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // agent-coherent stores (no cache write-back needed), each thread waits for
+        // its own to complete, then one flag for the workgroup
+        t.store_state_coherent(U + p * dd);
+        if (t.w == 0)
+            __hip_atomic_store(Gs + static_cast<int64_t>(p) * DK + t.l, fexp2(gam), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t.tid == 0)
             __hip_atomic_store(ready + p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
     }
     t.zero_state();
 
     // ---- 2. wait for the chunks before this one (lane m of wave 0 polls chunk m's
-    // flag with cache-bypassing loads), then one acquire for the workgroup
+    // flag with cache-bypassing loads); the summaries are then read the same way
     if (ch > 0) {
         if (t.w == 0) {
             const unsigned *fl = ready + static_cast<int64_t>(bh) * N;
@@ -89,10 +94,11 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
             while (true) {
                 if (!mine)
                     mine = __hip_atomic_load(fl + t.l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-                if (__builtin_amdgcn_read_exec() == __ballot(mine) || ++spins >= kSpinLimit) break;
+                if (__builtin_amdgcn_read_exec() == __ballot(mine)) break;
+                if (++spins >= kSpinLimit) break;
                 __builtin_amdgcn_s_sleep(2);
             }
-            if (t.l == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (t.l == 0) s_gave_up = spins >= kSpinLimit;
         }
         __syncthreads();
 
@@ -110,6 +116,7 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
             for (int i = 0; i < MB; ++i)
                 if (m0 + i < ch) t.state_in_apply(in[i]);
         }
+        if (s_gave_up) t.poison_state();
     }
 
     // ---- 3. outputs from the incoming state and the staged operands

@@ -470,6 +470,16 @@ struct Tile {
         for (int e = 0; e < CPL / 8; ++e) pz[e] = *reinterpret_cast<const uint4 *>(zp + 8 * e);
     }
 
+    // the incoming state could not be formed (a bounded wait gave up): NaN, so the
+    // chunk's outputs show it
+    __device__ __forceinline__ void poison_state() {
+#pragma unroll
+        for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) S[dd][ct] = f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                          __builtin_nanf(""), __builtin_nanf("")};
+    }
+
     __device__ __forceinline__ void zero_state() {
 #pragma unroll
         for (int dd = 0; dd < DPW; ++dd)
@@ -498,25 +508,42 @@ struct Tile {
                     dst[(16 * ct + 4 * g + r) * DV + 16 * (w * DPW + dd) + lr] = S[dd][ct][r];
     }
 
-    // One step of a scan over chunk summaries, in the state's register layout:
-    // S <- Diag(e) S + u, with u a [DK][DV] summary and e the per-channel decay.
-    struct StateIn {
-        f32x4 e[4];
-        float u[DPW][4][4];
-    };
-    __device__ __forceinline__ void state_in_load(StateIn &x, const float *u, const float *e) const {
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const float4 d = *reinterpret_cast<const float4 *>(e + 16 * ct + 4 * g);
-            x.e[ct] = f32x4{d.x, d.y, d.z, d.w};
-        }
+    // store_state with agent-coherent stores: visible to other workgroups (any XCD)
+    // that read it with agent-coherent loads, with no cache write-back
+    __device__ __forceinline__ void store_state_coherent(float *dst) const {
 #pragma unroll
         for (int dd = 0; dd < DPW; ++dd)
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    x.u[dd][ct][r] = u[(16 * ct + 4 * g + r) * DV + 16 * (w * DPW + dd) + lr];
+                    __hip_atomic_store(dst + (16 * ct + 4 * g + r) * DV + 16 * (w * DPW + dd) + lr,
+                                       S[dd][ct][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // One step of a scan over chunk summaries, in the state's register layout:
+    // S <- Diag(e) S + u, with u a [DK][DV] summary and e the per-channel decay.
+    struct StateIn {
+        f32x4 e[4];
+        float u[DPW][4][4];
+    };
+    // (agent-coherent loads: the summaries come from other workgroups of this launch)
+    __device__ __forceinline__ void state_in_load(StateIn &x, const float *u, const float *e) const {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                x.e[ct][r] = __hip_atomic_load(e + 16 * ct + 4 * g + r, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x.u[dd][ct][r] = __hip_atomic_load(
+                        u + (16 * ct + 4 * g + r) * DV + 16 * (w * DPW + dd) + lr, __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
     }
     __device__ __forceinline__ void state_in_apply(const StateIn &x) {
 #pragma unroll

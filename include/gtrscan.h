@@ -81,10 +81,12 @@ typedef enum { GTR_F32 = 0, GTR_F16 = 1, GTR_BF16 = 2 } gtr_dtype;
 
 typedef enum { GTR_LR = 0, GTR_RL = 1, GTR_TB = 2, GTR_BT = 3 } gtr_direction;
 
-/* Kernel path.  AUTO picks the MFMA chunk path for 16-bit I/O with dk = 64,
- * dv in {64, 128}, chunk in {32, 64}, and the fp32 token-serial chunk path
- * otherwise (float32 I/O, other dk/dv or chunk).  The single-launch path runs
- * only when asked for. */
+/* Kernel path.  AUTO picks, for 16-bit I/O with dk = 64, dv in {64, 128},
+ * chunk in {32, 64} and 16-byte aligned tensors: the single-launch path for
+ * B == 1 with at most 16 chunks per sequence and no residual or gate
+ * projection, the MFMA chunk path otherwise; and the fp32 token-serial chunk
+ * path for everything else (float32 I/O, other dk/dv or chunk, unaligned
+ * views).  gtr_gla_auto_path reports the choice. */
 typedef enum {
     GTR_PATH_AUTO = 0,
     GTR_PATH_MFMA = 1,    /* three launches: segment summaries, state scan, chunk outputs */
@@ -130,8 +132,10 @@ gtr_status gtr_gla_fwd_events(const void *q, const void *k, const void *v, const
 /*
  * gtr_gla_fwd for callers that cannot allocate device memory: code under HIP
  * graph capture, serving loops that forbid allocation after start-up,
- * harnesses without an allocator.  Same arguments, operation, path choice
- * (AUTO) and results, bit for bit, as gtr_gla_fwd.  It calls no hipMalloc,
+ * harnesses without an allocator.  Same arguments and operation as
+ * gtr_gla_fwd; it takes the MFMA path where gtr_gla_fwd's AUTO takes the MFMA
+ * or the single-launch path, and the token-serial path otherwise, with results
+ * equal bit for bit to gtr_gla_fwd_path on that path.  It calls no hipMalloc,
  * hipFree or other allocating routine: the per-call segment (or chunk) states
  * live in a fixed device array of the library, 32 MiB on each device, held from
  * the library's load until the process ends.  A call whose states would not fit

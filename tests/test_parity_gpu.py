@@ -430,14 +430,18 @@ def _stack_case(oracle_mod, nb, B, gh, gw, H, dk, dv, dtype, chunk, first, bh=No
     out = g.gla_stack_fwd(t["q"], t["k"], t["v"], t["log_g"], t["z"], t["rms_w"], first,
                           chunk=chunk)
     torch.cuda.synchronize()
-    # (1) chain of single calls
+    # (1) chain of single calls, on the path the stack takes for every block: with
+    # more than one block the residual rules out the single-launch path
+    auto = _lib.load().gtr_gla_auto_path(B, H, gh, gw, dk, dv, chunk, W.DTYPE_CODE[dtype])
+    assert auto >= 0, _lib.last_error()
+    path = auto if nb == 1 or auto != g.PATH_FAST else g.PATH_MFMA
     prev = None
     for i in range(nb):
         v = t["v"][i]
         if prev is not None:
             v = (v.float() + prev.float()).to(v.dtype)   # float32 add, round to nearest even
         o = g.gla_fwd(t["q"][i], t["k"][i], v.contiguous(), t["log_g"][i], t["z"][i],
-                      t["rms_w"][i], (first + i) % 4, chunk=chunk)
+                      t["rms_w"][i], (first + i) % 4, chunk=chunk, path=path)
         torch.cuda.synchronize()
         assert torch.equal(o, out[i]), f"stack block {i} differs from the single-call chain"
         prev = o
