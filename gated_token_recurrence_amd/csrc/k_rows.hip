@@ -579,7 +579,7 @@ struct RowTile {
 
     // ---- epilogue: y = o / sqrt(mean_j o_j^2 + eps) * rms_w * z * sigmoid(z) for the
     // wave's tokens, stored at the token's grid position (pairs rounded to nearest
-    // even by the packed conversion)
+    // even by the packed conversion; streaming stores)
     __device__ __forceinline__ float half_ss() const {
         float ss = 0.f;
 #pragma unroll
@@ -627,7 +627,7 @@ struct RowTile {
             const uint4 yb = make_uint4(pk2<DT == DT_F16>(y[0], y[1]), pk2<DT == DT_F16>(y[2], y[3]),
                                         pk2<DT == DT_F16>(y[4], y[5]), pk2<DT == DT_F16>(y[6], y[7]));
             if (rowC >= 0)
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + rowC * DV + d0) = yb;
+                store_stream16(static_cast<uint16_t *>(a.out) + rowC * DV + d0, yb);
         }
     }
 };

@@ -102,6 +102,15 @@ __device__ __forceinline__ void split_pk(const float (&x)[N], uint32_t (&hi)[N /
 
 __device__ __forceinline__ uint4 u4(const uint32_t (&x)[4]) { return make_uint4(x[0], x[1], x[2], x[3]); }
 
+// 16-byte store with the streaming (non-temporal) hint: for outputs nothing in the
+// same call reads again.  Measured on MI355X, it keeps them from lingering dirty in
+// the caches, whose later write-back otherwise slows the next call's first reads.
+__device__ __forceinline__ void store_stream16(void *p, const uint4 &v) {
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t *>(p));
+}
+
 // the eight 16-bit values of u as floats (I/O type DT)
 template <int DT>
 __device__ __forceinline__ void unpack8(const uint4 &u, float (&x)[8]) {
