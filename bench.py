@@ -590,7 +590,7 @@ def _mean(v):
     return sum(v) / len(v)
 
 
-def ingest_counters(fetch_csv, write_csv, sq_csv, workload, path_name, launches):
+def ingest_counters(fetch_csv, write_csv, sq_csv, workload, path_name, launches, out_dir=None):
     """Writes profiles/counters_<path>_<workload>.json from three counter runs of
     ``bench.py --profile-run`` (FETCH_SIZE; WRITE_SIZE; the SQ/GRBM set above).
     FETCH_SIZE and WRITE_SIZE are scaled by the ratio of the calibration copy's
@@ -633,15 +633,16 @@ def ingest_counters(fetch_csv, write_csv, sq_csv, workload, path_name, launches)
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "calibration_copy_bytes": COPY_BYTES, "sources_hash": kernel_sources_hash(),
            "csv": [os.path.relpath(p, ROOT) for p in (fetch_csv, write_csv, sq_csv) if p]}
-    path = os.path.join(ROOT, "profiles", f"counters_{path_name}_{workload}.json")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"counters_{path_name}_{workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
+    return out
 
 
-def counters_record(path_name, workload):
-    p = os.path.join(ROOT, "profiles", f"counters_{path_name}_{workload}.json")
+def counters_record(path_name, workload, out_dir=None):
+    p = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"counters_{path_name}_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -660,6 +661,45 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+def roofline_record(comp, us, launch_us, names, cr, flops):
+    """The JSON line's roofline object.  comp: the call's algorithmic bytes; us: the
+    call's mean duration; launch_us: mean duration of each launch (names); cr: the
+    counter record of this path and workload (or None); flops: the call's algorithmic
+    flops.  The dominant kernel (chunk outputs) reads every input and writes the
+    output, so its algorithmic bytes per launch are the call's; "frac" is that
+    kernel's fraction of the HBM peak, and the call as a whole (the bar the method is
+    judged on) is reported under "whole_call"."""
+    dom = int(np.argmax(launch_us))
+    dom_us = launch_us[dom]
+    achieved = comp / (dom_us * 1e-6) / 1e9
+    call_achieved = comp / (us * 1e-6) / 1e9
+    traffic = call_traffic = None
+    mfma_meas = valu_meas = mfma_call = None
+    if cr is not None:
+        lr = cr["launches"]
+        if names[dom] in lr:
+            traffic = lr[names[dom]]["bytes"]
+            mfma_meas = lr[names[dom]].get("mfma_busy_frac")
+            valu_meas = lr[names[dom]].get("valu_busy_frac")
+        call_traffic = cr["call_bytes"]
+        if all("mfma_busy_frac" in lr.get(n, {}) for n in names):
+            mfma_call = sum(lr[n]["mfma_busy_frac"] * t for n, t in zip(names, launch_us)) / sum(launch_us)
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": names[dom], "kernel_us": round(dom_us, 3),
+            "frac_of": f"the dominant kernel ({names[dom]}); the whole call: whole_call_frac",
+            "algorithmic_bytes": comp,
+            "whole_call": {"us": round(us, 3), "achieved": round(call_achieved, 1),
+                           "frac": round(call_achieved / HBM_PEAK_GBS, 4),
+                           "traffic": call_traffic},
+            "whole_call_frac": round(call_achieved / HBM_PEAK_GBS, 4),
+            "mfma_util": {"measured_kernel": mfma_meas,
+                          "measured_call": round(mfma_call, 4) if mfma_call is not None else None,
+                          "algorithmic_call": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                          "peak_tflops": MFMA_BF16_PEAK_TFLOPS},
+            "valu_busy_kernel": valu_meas}
 
 
 def main():
@@ -718,39 +758,8 @@ def main():
     value = w.tokens / (us * 1e-6)
     names = LAUNCH_NAMES[pname]
     launch_us = res["launch_us_mean"]
-    dom = int(np.argmax(launch_us))
-    dom_us = launch_us[dom]
-    # The dominant kernel (chunk outputs) reads every input and writes the output: its
-    # algorithmic bytes per launch are the call's.  The call as a whole is the bar the
-    # method is judged on: both are reported, the call under "whole_call".
-    achieved = comp / (dom_us * 1e-6) / 1e9
-    call_achieved = comp / (us * 1e-6) / 1e9
-    cr = counters_record(pname, w.name)
-    traffic = call_traffic = None
-    mfma_meas = valu_meas = mfma_call = None
-    if cr is not None:
-        lr = cr["launches"]
-        if names[dom] in lr:
-            traffic = lr[names[dom]]["bytes"]
-            mfma_meas = lr[names[dom]].get("mfma_busy_frac")
-            valu_meas = lr[names[dom]].get("valu_busy_frac")
-        call_traffic = cr["call_bytes"]
-        if all("mfma_busy_frac" in lr.get(n, {}) for n in names):
-            mfma_call = sum(lr[n]["mfma_busy_frac"] * t for n, t in zip(names, launch_us)) / sum(launch_us)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": names[dom], "kernel_us": round(dom_us, 3),
-                "algorithmic_bytes": comp,
-                "whole_call": {"us": round(us, 3), "achieved": round(call_achieved, 1),
-                               "frac": round(call_achieved / HBM_PEAK_GBS, 4),
-                               "traffic": call_traffic},
-                "whole_call_frac": round(call_achieved / HBM_PEAK_GBS, 4),
-                "mfma_util": {"measured_kernel": mfma_meas,
-                              "measured_call": round(mfma_call, 4) if mfma_call is not None else None,
-                              "algorithmic_call": round(w.algorithmic_flops(chunk) / (us * 1e-6)
-                                                        / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
-                              "peak_tflops": MFMA_BF16_PEAK_TFLOPS},
-                "valu_busy_kernel": valu_meas}
+    roofline = roofline_record(comp, us, launch_us, names, counters_record(pname, w.name),
+                               w.algorithmic_flops(chunk))
     extra = {}
     if not args.no_extra:
         for name in ("mixer_640", "mixer_640_wide"):
