@@ -293,8 +293,11 @@ gtr_status gtr_sswiglu_mix(const void *u, const float *w_conv, const float *b_co
                            int B, int grid_h, int grid_w, int F, int k, gtr_dtype dtype,
                            hipStream_t stream);
 
-/* The gtr_path that GTR_PATH_AUTO selects for these arguments, or a negative
- * gtr_status if the arguments are invalid (no device access). */
+/* The gtr_path that GTR_PATH_AUTO selects for a gtr_gla_fwd call with these
+ * arguments and 16-byte aligned tensors, or a negative gtr_status if the
+ * arguments are invalid (no device access).  (Unaligned views take the
+ * token-serial path; the stack's blocks after the first, which add a residual,
+ * and the low-rank gate calls never take the single-launch path.) */
 int gtr_gla_auto_path(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
                       gtr_dtype dtype);
 
