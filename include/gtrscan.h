@@ -296,8 +296,9 @@ gtr_status gtr_sswiglu_mix(const void *u, const float *w_conv, const float *b_co
 /* The gtr_path that GTR_PATH_AUTO selects for a gtr_gla_fwd call with these
  * arguments and 16-byte aligned tensors, or a negative gtr_status if the
  * arguments are invalid (no device access).  (Unaligned views take the
- * token-serial path; the stack's blocks after the first, which add a residual,
- * and the low-rank gate calls never take the single-launch path.) */
+ * token-serial path; a stack of more than one block, whose blocks all take one
+ * path and add a residual after the first, and the low-rank gate calls never
+ * take the single-launch path.) */
 int gtr_gla_auto_path(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
                       gtr_dtype dtype);
 
