@@ -166,8 +166,9 @@ template <> __device__ __forceinline__ uint32_t f2h<DT_F16>(float x) {
 }
 template <> __device__ __forceinline__ uint32_t f2h<DT_BF16>(float x) { return f32_to_bf16(x); }
 
-// x + y element-wise on eight 16-bit values of the I/O type, each sum rounded to
-// the I/O type (the stack residual v + out_prev)
+// x + y element-wise on eight 16-bit values of the I/O type, each sum formed in
+// float32 and rounded to nearest even to the I/O type (the stack residual
+// v + out_prev), two values per packed conversion
 template <int DT>
 __device__ __forceinline__ uint4 add_io(const uint4 &x, const uint4 &y) {
     const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
@@ -175,9 +176,10 @@ __device__ __forceinline__ uint4 add_io(const uint4 &x, const uint4 &y) {
     uint32_t o[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const uint32_t lo = f2h<DT>(h2f<DT>(xs[u] & 0xffffu) + h2f<DT>(ys[u] & 0xffffu));
-        const uint32_t hi = f2h<DT>(h2f<DT>(xs[u] >> 16) + h2f<DT>(ys[u] >> 16));
-        o[u] = lo | (hi << 16);
+        float x0, x1, y0, y1;
+        unpk2<DT == DT_F16>(xs[u], x0, x1);
+        unpk2<DT == DT_F16>(ys[u], y0, y1);
+        o[u] = pk2<DT == DT_F16>(x0 + y0, x1 + y1);
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -437,15 +439,7 @@ struct Tile {
             if (a.resid) {  // stack residual: v + out_prev, rounded to the I/O type
                 const uint4 y = *reinterpret_cast<const uint4 *>(
                     static_cast<const uint16_t *>(a.resid) + row * DV + d0);
-                uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-                const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = f2h<DT>(h2f<DT>(xs[e] & 0xffffu) + h2f<DT>(ys[e] & 0xffffu));
-                    const uint32_t hi = f2h<DT>(h2f<DT>(xs[e] >> 16) + h2f<DT>(ys[e] >> 16));
-                    xs[e] = lo | (hi << 16);
-                }
-                x = make_uint4(xs[0], xs[1], xs[2], xs[3]);
+                x = add_io<DT>(x, y);
             }
             pv[vm] = x;
         }
