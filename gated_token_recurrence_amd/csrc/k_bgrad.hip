@@ -139,7 +139,7 @@ template <int DT>
 __device__ __forceinline__ uint4 pack8(const float *x) {
     uint32_t u[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = f2h<DT>(x[2 * e]) | (f2h<DT>(x[2 * e + 1]) << 16);
+    for (int e = 0; e < 4; ++e) u[e] = pk2<DT == DT_F16>(x[2 * e], x[2 * e + 1]);
     return u4(u);
 }
 

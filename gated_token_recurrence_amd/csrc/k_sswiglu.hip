@@ -70,15 +70,16 @@ __device__ __forceinline__ P pack(const float (&y)[CPL]) {
     } else {
 #pragma unroll
         for (int c = 0; c < CPL; c += 2) {
-            uint32_t lo, hi;
+            // a pair per packed round-to-nearest-even conversion
+            typedef float f2_t __attribute__((ext_vector_type(2)));
+            const f2_t v = {y[c], y[c + 1]};
             if constexpr (DT == DT_F16) {
-                lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(y[c]));  // RNE
-                hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(y[c + 1]));
+                typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+                w[c / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2_t));
             } else {
-                lo = f32_to_bf16(y[c]);
-                hi = f32_to_bf16(y[c + 1]);
+                typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+                w[c / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2_t));
             }
-            w[c / 2] = lo | (hi << 16);
         }
     }
     return p;
