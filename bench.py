@@ -517,6 +517,19 @@ LAUNCH_NAMES = {
     "serial": ["chunk_summary", "state_scan", "chunk_output"],
     "fast": ["fast_single_launch"],
 }
+# launches a call may leave out: the matrix-core path has no scan launch when its output
+# kernel folds the incoming states itself (few segments per sequence)
+OPTIONAL_LAUNCHES = {"mfma": ("state_scan",)}
+
+
+def launch_names(pname, n):
+    """Names of the n launches of a call on path pname."""
+    names = LAUNCH_NAMES[pname]
+    if n < len(names):
+        names = [x for x in names if x not in OPTIONAL_LAUNCHES.get(pname, ())]
+    if len(names) != n:
+        raise SystemExit(f"{n} launches on the {pname} path: expected {len(LAUNCH_NAMES[pname])}")
+    return names
 
 
 def resolve_path(w, requested, chunk=0):
@@ -588,6 +601,15 @@ def _find(vals, counter, key, reduce):
 
 def _mean(v):
     return sum(v) / len(v)
+
+
+def present_launches(csv_path, path_name):
+    """The path's launches whose kernel appears in a counter CSV (an optional launch
+    the call left out is dropped; a missing required one stays, for ingest to report)."""
+    kernels = {kn for kn, _ in _counter_values(csv_path)}
+    return [n for n in LAUNCH_NAMES[path_name]
+            if n not in OPTIONAL_LAUNCHES.get(path_name, ()) or
+            any(KERNEL_KEYS[n](kn) for kn in kernels)]
 
 
 def ingest_counters(fetch_csv, write_csv, sq_csv, workload, path_name, launches, out_dir=None):
@@ -727,7 +749,7 @@ def main():
         pn = PATH_NAMES[resolve_path(wi, args.path, args.chunk or wi.chunk)]
         f_csv, w_csv = args.ingest_counters[:2]
         sq_csv = args.ingest_counters[2] if len(args.ingest_counters) == 3 else None
-        ingest_counters(f_csv, w_csv, sq_csv, args.workload, pn, LAUNCH_NAMES[pn])
+        ingest_counters(f_csv, w_csv, sq_csv, args.workload, pn, present_launches(f_csv, pn))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -756,8 +778,8 @@ def main():
     comp = w.compulsory_bytes()
     us = res["us_per_call"]
     value = w.tokens / (us * 1e-6)
-    names = LAUNCH_NAMES[pname]
     launch_us = res["launch_us_mean"]
+    names = launch_names(pname, len(launch_us))
     roofline = roofline_record(comp, us, launch_us, names, counters_record(pname, w.name),
                                w.algorithmic_flops(chunk))
     extra = {}
@@ -805,8 +827,10 @@ def main():
         try:
             r = time_lowrank(w, dev, hip, sp, args.steps, args.warmup, chunk)
             lb = w.compulsory_bytes_lowrank(16)
-            lnames = (LAUNCH_NAMES[pname] if r["launches"] == 3
-                      else ("gate_projection",) + tuple(LAUNCH_NAMES[pname]))
+            # the gate formed in the kernels: the plain call's launches; written out
+            # first: one more
+            lnames = (names if r["launches"] == len(names)
+                      else ("gate_projection",) + tuple(names))
             lowrank = {"workload": f"{w.name} shapes, log_g formed from rank-16 fp16 gate "
                                    f"features (tau 16) in the kernels",
                        "us_per_call": round(r["us_per_call"], 3),

@@ -210,6 +210,10 @@ gtr_status take_workspace(hipStream_t st, size_t need, const WsSource *src, void
 
 constexpr int kDefaultChunk = 64;
 constexpr int kFastMaxTokens = 2048;
+// Sequences of at most this many segments skip the scan launch: their output kernel
+// folds the incoming states itself (the scan then costs a launch and its drain, ~11 us
+// on MI355X for the 12-block stack's blocks, against a few loads per workgroup).
+constexpr int64_t kFoldSegments = 8;
 
 int g_chunks_per_wg = 0;  // 0: automatic (gtr_set_segment_chunks)
 
@@ -257,10 +261,19 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk, float *states_o
     if (e == hipSuccess) e = sum_supported(a) ? sum_launch(a, pl, U, G, st) : mfma_summary(a, pl, U, G, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "segment summary launch");
-    e = state_scan_plan(U, G, pl, static_cast<int>(n_seq), a.dk, a.dv, st);
-    if (e == hipSuccess) e = mk.after_launch(st);
-    if (e != hipSuccess) return hip_fail(e, "state scan launch");
-    e = rows_supported(a) ? rows_output(a, po, pl, U, st) : mfma_output(a, po, pl, U, st);
+    // With few segments per sequence the output kernel folds each segment's incoming
+    // state from the summaries itself (at most kFoldSegments - 1 of them, the same
+    // arithmetic in the same order as the scan) and the scan launch is left out; the
+    // caller's states buffer always gets the scanned states.
+    const int64_t most = (pl.N + pl.Q - 1) / pl.Q + 1;  // segments of one sequence, at most
+    const bool fold = !states_out && rows_supported(a) && most <= kFoldSegments;
+    if (!fold) {
+        e = state_scan_plan(U, G, pl, static_cast<int>(n_seq), a.dk, a.dv, st);
+        if (e == hipSuccess) e = mk.after_launch(st);
+        if (e != hipSuccess) return hip_fail(e, "state scan launch");
+    }
+    e = rows_supported(a) ? rows_output(a, po, pl, U, fold ? G : nullptr, st)
+                          : mfma_output(a, po, pl, U, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "chunk output launch");
     return GTR_OK;

@@ -135,6 +135,8 @@ struct RowTile {
     f32x4 O[NDW];
     s16x8 qh[2], ql[2];  // Q~ of this wave's tokens, B-operand layout
 
+    __device__ __forceinline__ static int hv_of(int wave) { return CS == 1 ? 0 : wave >> 2; }
+
     __device__ __forceinline__ void init(const GlaArgs &args, char *smem) {
         a = args;
         sK = reinterpret_cast<uint16_t *>(smem + O_K);
@@ -146,8 +148,12 @@ struct RowTile {
         sGate = smem + O_GATE;
         const int tid = threadIdx.x;
         w = __builtin_amdgcn_readfirstlane(tid >> 6);
-        tw = CS == 1 ? w : w & 3;
-        hv = CS == 1 ? 0 : w >> 2;
+        // Wave w's token group.  A group's causal share of the score and intra-chunk
+        // products grows with its index, and waves w and w + 4 (and the same wave of the
+        // two workgroups that share a CU, launched 256 apart) run on one SIMD: the groups
+        // are spread so that no SIMD takes the last group twice.
+        tw = CS == 1 ? ((w + 2 * ((blockIdx.x >> 8) & 1)) & 3) : ((w + 2 * hv_of(w)) & 3);
+        hv = hv_of(w);
         kap0 = CS == 1 ? 0 : hv;
         sQ = reinterpret_cast<uint16_t *>(smem + O_QP) + tw * 2 * 16 * 64;
         l = tid & 63;
@@ -227,6 +233,41 @@ struct RowTile {
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[s][ct][r] = src[(16 * ct + 4 * g + r) * DV + d];
+        }
+    }
+
+    __device__ __forceinline__ void zero_state() {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) S[s][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Incoming state of the owned tiles folded from the segment summaries U (fp32
+    // [segment][DK][DV]) and summed log2-gates Gs ([segment][DK]) of the sequence's
+    // segments s0 .. sj - 1, in order: the boundary recurrence
+    // S <- Diag(2^(G_m)) S + U_m, the same arithmetic as the scan kernels.
+    __device__ __forceinline__ void fold_state(const float *U, const float *Gs, int64_t s0,
+                                               int64_t sj) {
+        zero_state();
+        for (int64_t m = s0; m < sj; ++m) {
+            const float *src = U + m * DK * DV;
+            float4 gm[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                gm[ct] = *reinterpret_cast<const float4 *>(Gs + m * DK + 16 * ct + 4 * g);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int d = dcol(NS * w + s, lr);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const float e[4] = {fexp2(gm[ct].x), fexp2(gm[ct].y), fexp2(gm[ct].z),
+                                        fexp2(gm[ct].w)};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        S[s][ct][r] = e[r] * S[s][ct][r] + src[(16 * ct + 4 * g + r) * DV + d];
+                }
+            }
         }
     }
 
@@ -312,10 +353,7 @@ struct RowTile {
         }
         r_l *= kLog2e;
         tot_l *= kLog2e;
-        float sp2 = -tot_l;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) sp2 = fmaxf(sp2, __shfl_xor(sp2, off));
-        const bool slow = sp2 > kSpanMax;
+        const bool slow = __ballot(-tot_l > kSpanMax) != 0;  // any channel's span
         sTab[l] = r_l;
         sTab[DK + l] = fexp2(tot_l);
         __builtin_amdgcn_wave_barrier();
@@ -436,43 +474,44 @@ struct RowTile {
             }
         }
         __builtin_amdgcn_sched_barrier(0);  // keeps the operand loads of each step near it
-        // causal score tiles P^T_J[j][i] = K^_J Q~_w^T, J <= w, kept as hi + lo
-        uint32_t ph[NB][2], pl[NB][2];
-#pragma unroll
-        for (int J = 0; J < NB; ++J) {
-            ph[J][0] = ph[J][1] = pl[J][0] = pl[J][1] = 0u;
-            if (J <= tw) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kap = 0; kap < 2; ++kap) {
-                    const int off = swn(16 * J + lr, 32 * kap + 8 * g);
-                    const s16x8 kh = *reinterpret_cast<const s16x8 *>(sK + off);
-                    const s16x8 kl = *reinterpret_cast<const s16x8 *>(sK + MAT + off);
-                    acc = mma<false>(kh, qh[kap], acc);
-                    acc = mma<false>(kh, ql[kap], acc);
-                    acc = mma<false>(kl, qh[kap], acc);
-                }
-                float x[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = (J == tw && 4 * g + r > lr) ? 0.f : acc[r];  // j <= i
-                split_pk<false>(x, ph[J], pl[J]);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // intra-chunk readout O^T += V^T P^T, 32 tokens per step
+        // causal score tiles P^T_J[j][i] = K^_J Q~_w^T (hi + lo), two at a time, each
+        // pair feeding the intra-chunk readout O^T += V^T P^T (32 tokens per step) at
+        // once.  A wave takes the pairs that reach its own tokens; a tile past them
+        // (J > w) is formed and zeroed by the mask like the causal part of J = w.
 #pragma unroll
         for (int kt = 0; kt < NB / 2; ++kt) {
             if (2 * kt <= tw) {
-                const s16x8 bh = __builtin_bit_cast(
-                    s16x8, make_uint4(ph[2 * kt][0], ph[2 * kt][1], ph[2 * kt + 1][0], ph[2 * kt + 1][1]));
-                const s16x8 bl = __builtin_bit_cast(
-                    s16x8, make_uint4(pl[2 * kt][0], pl[2 * kt][1], pl[2 * kt + 1][0], pl[2 * kt + 1][1]));
+                uint32_t bh[4], bl[4];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int J = 2 * kt + u;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kap = 0; kap < 2; ++kap) {
+                        const int off = swn(16 * J + lr, 32 * kap + 8 * g);
+                        const s16x8 kh = *reinterpret_cast<const s16x8 *>(sK + off);
+                        const s16x8 kl = *reinterpret_cast<const s16x8 *>(sK + MAT + off);
+                        acc = mma<false>(kh, qh[kap], acc);
+                        acc = mma<false>(kh, ql[kap], acc);
+                        acc = mma<false>(kl, qh[kap], acc);
+                    }
+                    float x[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        x[r] = (J > tw || (J == tw && 4 * g + r > lr)) ? 0.f : acc[r];  // j <= i
+                    uint32_t h2[2], l2[2];
+                    split_pk<false>(x, h2, l2);
+                    bh[2 * u] = h2[0]; bh[2 * u + 1] = h2[1];
+                    bl[2 * u] = l2[0]; bl[2 * u + 1] = l2[1];
+                }
+                const s16x8 ph = __builtin_bit_cast(s16x8, make_uint4(bh[0], bh[1], bh[2], bh[3]));
+                const s16x8 pl = __builtin_bit_cast(s16x8, make_uint4(bl[0], bl[1], bl[2], bl[3]));
 #pragma unroll
                 for (int e = 0; e < NDW; ++e) {
                     const s16x8 av = op_v(0, NDW * hv + e, 32 * kt);
-                    O[e] = mma<false>(av, bh, O[e]);
-                    O[e] = mma<false>(av, bl, O[e]);
-                    if (NV == 2) O[e] = mma<false>(op_v(NV - 1, NDW * hv + e, 32 * kt), bh, O[e]);
+                    O[e] = mma<false>(av, ph, O[e]);
+                    O[e] = mma<false>(av, pl, O[e]);
+                    if (NV == 2) O[e] = mma<false>(op_v(NV - 1, NDW * hv + e, 32 * kt), ph, O[e]);
                 }
             }
         }
@@ -634,6 +673,7 @@ struct RowTile {
 
 template <int DT, int DV, bool RES, bool LRG>
 __global__ __launch_bounds__(64 * 4 * (DV / 64), DV == 64 ? 2 : 1) void k_rows(GlaArgs a, const float *__restrict__ Sx,
+                                                               const float *__restrict__ Gf,
                                                                MfmaPlan pl, MfmaPlan ps) {
     using R = RowTile<DT, DV, RES, LRG>;
     static_assert(R::NTH == 64 * 4 * (DV / 64), "launch bounds");
@@ -658,9 +698,16 @@ __global__ __launch_bounds__(64 * 4 * (DV / 64), DV == 64 ? 2 : 1) void k_rows(G
     // the incoming state is loaded outside the chunk loop: the chunk loop then
     // issues the same loads every time and the wait-count bookkeeping never has to
     // drain the load queue.
+    // With Gf, Sx holds the segment summaries and the state entering the range is
+    // folded from those of its sequence's earlier segments (every later piece of the
+    // range starts a sequence, from zero); without, Sx holds each segment's state.
+    if (Gf) t.fold_state(Sx, Gf, seg_id(p0 - ch, ps), seg_id(p0, ps));
     for (int64_t p = p0; p < p1;) {
         const int64_t pe = (p - ch + pl.N < p1) ? p - ch + pl.N : p1;  // segment end
-        t.load_state(Sx + seg_id(p, ps) * DK * DV);
+        if (!Gf)
+            t.load_state(Sx + seg_id(p, ps) * DK * DV);
+        else if (p != p0)
+            t.zero_state();
         LowRankGate<DT> lg;
         if constexpr (LRG) lg.load(a, h, t.lr, t.g);  // the segment's head
         t.state_ready();
@@ -710,20 +757,20 @@ __global__ __launch_bounds__(64 * 4 * (DV / 64), DV == 64 ? 2 : 1) void k_rows(G
 }
 
 template <int DT, int DV>
-hipError_t launch_rows(const GlaArgs &a, const float *Sx, const MfmaPlan &po, const MfmaPlan &ps,
-                       hipStream_t st) {
+hipError_t launch_rows(const GlaArgs &a, const float *Sx, const float *Gf, const MfmaPlan &po,
+                       const MfmaPlan &ps, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(po.n_wg));
     if (a.feat) {  // gates from rank-16 features: dv = 64, no residual
         if constexpr (DV == 64) {
             if (a.resid || a.rank != kFusedGateRank) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((k_rows<DT, DV, false, true>), grid, dim3(RowTile<DT, DV, false, true>::NTH), 0, st, a, Sx, po, ps);
+            hipLaunchKernelGGL((k_rows<DT, DV, false, true>), grid, dim3(RowTile<DT, DV, false, true>::NTH), 0, st, a, Sx, Gf, po, ps);
         } else {
             return hipErrorInvalidValue;
         }
     } else if (a.resid) {
-        hipLaunchKernelGGL((k_rows<DT, DV, true, false>), grid, dim3(RowTile<DT, DV, true, false>::NTH), 0, st, a, Sx, po, ps);
+        hipLaunchKernelGGL((k_rows<DT, DV, true, false>), grid, dim3(RowTile<DT, DV, true, false>::NTH), 0, st, a, Sx, Gf, po, ps);
     } else {
-        hipLaunchKernelGGL((k_rows<DT, DV, false, false>), grid, dim3(RowTile<DT, DV, false, false>::NTH), 0, st, a, Sx, po, ps);
+        hipLaunchKernelGGL((k_rows<DT, DV, false, false>), grid, dim3(RowTile<DT, DV, false, false>::NTH), 0, st, a, Sx, Gf, po, ps);
     }
     return hipGetLastError();
 }
@@ -736,13 +783,13 @@ bool rows_supported(const GlaArgs &a) {
 }
 
 hipError_t rows_output(const GlaArgs &a, const MfmaPlan &po, const MfmaPlan &ps, const float *Sx,
-                       hipStream_t s) {
+                       const float *Gf, hipStream_t s) {
     if (a.dtype == DT_F16) {
-        if (a.dv == 64) return launch_rows<DT_F16, 64>(a, Sx, po, ps, s);
-        if (a.dv == 128) return launch_rows<DT_F16, 128>(a, Sx, po, ps, s);
+        if (a.dv == 64) return launch_rows<DT_F16, 64>(a, Sx, Gf, po, ps, s);
+        if (a.dv == 128) return launch_rows<DT_F16, 128>(a, Sx, Gf, po, ps, s);
     } else if (a.dtype == DT_BF16) {
-        if (a.dv == 64) return launch_rows<DT_BF16, 64>(a, Sx, po, ps, s);
-        if (a.dv == 128) return launch_rows<DT_BF16, 128>(a, Sx, po, ps, s);
+        if (a.dv == 64) return launch_rows<DT_BF16, 64>(a, Sx, Gf, po, ps, s);
+        if (a.dv == 128) return launch_rows<DT_BF16, 128>(a, Sx, Gf, po, ps, s);
     }
     return hipErrorInvalidValue;
 }

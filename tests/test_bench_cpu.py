@@ -126,3 +126,32 @@ def test_bench_runs_on_one_gpu_only():
                        capture_output=True, text=True, timeout=300)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_launch_names_follow_the_launch_count():
+    assert bench.launch_names("mfma", 3) == ["segment_summary", "state_scan", "chunk_output"]
+    # the output kernel folds the incoming states itself: no scan launch
+    assert bench.launch_names("mfma", 2) == ["segment_summary", "chunk_output"]
+    assert bench.launch_names("fast", 1) == ["fast_single_launch"]
+    with pytest.raises(SystemExit, match="launches"):
+        bench.launch_names("mfma", 1)
+    with pytest.raises(SystemExit, match="launches"):
+        bench.launch_names("serial", 2)  # the token-serial path always scans
+
+
+def test_ingest_without_the_scan_launch(tmp_path):
+    paths, true_bytes = _fixture(tmp_path)
+    for p in paths:  # the same record with the scan kernel's rows taken out
+        rows = [r for r in csv.DictReader(open(p)) if "scan" not in r["Kernel_Name"]]
+        _csv(p, [(r["Kernel_Name"], r["Counter_Name"], r["Counter_Value"]) for r in rows])
+    names = bench.present_launches(paths[0], "mfma")
+    assert names == ["segment_summary", "chunk_output"]
+    out = bench.ingest_counters(*paths, "mixer_2048", "mfma", names, out_dir=str(tmp_path))
+    assert set(out["launches"]) == {"segment_summary", "chunk_output"}
+    assert out["call_fetch_bytes"] == pytest.approx(
+        true_bytes["segment_summary"][0] + true_bytes["chunk_output"][0], rel=1e-6)
+    # a required launch that is missing is still an error
+    assert bench.present_launches(paths[0], "fast") == ["fast_single_launch"]
+    with pytest.raises(SystemExit, match="expected one kernel"):
+        bench.ingest_counters(*paths, "mixer_2048", "fast", ["fast_single_launch"],
+                              out_dir=str(tmp_path))

@@ -3,9 +3,12 @@ fp64 oracle: log g = logsigmoid(feat . gate_w + gate_b) / tau, then the mixer.
 
 Bar as for gtr_gla_fwd: 16-bit I/O within rel-L2 1e-3 and max-abs 2e-2 of the
 oracle rounded to the I/O type; float32 I/O within rel-L2 1e-5.  The launch
-count tells which way the call went: 3 launches = the gate formed inside the
-summary and output kernels, 4 = log_g written out first.
+count tells which way the call went: the gate formed inside the summary and
+output kernels launches what a plain call on the matrix-core path launches;
+log_g written out first adds the projection launch to the plain call's.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -44,16 +47,42 @@ def _oracle(oracle_mod, x, dtype, direction, bh=None):
                                   x["rms_w"].astype(np.float64), direction, bh=bh)
 
 
-def _case(oracle_mod, shape, direction=0, chunk=0, path=g.PATH_AUTO, rank=16, launches=None,
+def _plain_launches(x, shape, direction, chunk, path):
+    """Launches of a plain mixer call of the same shape on the path the low-rank call
+    resolves to (under AUTO the matrix-core path where the shape has one, never the
+    single launch)."""
+    B, gh, gw, H, dk, dv, dtype = shape
+    lib = _lib.load()
+    if path == g.PATH_AUTO:
+        auto = lib.gtr_gla_auto_path(B, H, gh, gw, dk, dv, chunk, W.DTYPE_CODE[dtype])
+        path = g.PATH_SERIAL if auto == g.PATH_SERIAL else g.PATH_MFMA
+    t = _dev(x, dtype)
+    log_g = torch.full((B, gh, gw, H, dk), -0.1, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(t["v"])
+    n = ctypes.c_int(0)
+    _lib.check(lib.gtr_gla_fwd_events(
+        t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), log_g.data_ptr(),
+        t["z"].data_ptr(), t["rms_w"].data_ptr(), out.data_ptr(), B, H, gh, gw, dk, dv,
+        direction, chunk, W.DTYPE_CODE[dtype], path, None, 0, ctypes.byref(n),
+        torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    return n.value
+
+
+def _case(oracle_mod, shape, direction=0, chunk=0, path=g.PATH_AUTO, rank=16, gate=None,
           seed=7, **kw):
+    """gate: "fused" (formed in the kernels) or "written" (log_g written out first)."""
     B, gh, gw, H, dk, dv, dtype = shape
     x = W.make_lowrank(B, gh, gw, H, dk, dv, dtype, seed=seed, rank=rank, **kw)
     _note(f"lowrank {shape} dir={direction} chunk={chunk} path={path} rank={rank}")
     got, n = _run(x, dtype, direction, chunk=chunk, path=path)
     ref = _oracle(oracle_mod, x, dtype, direction)
     rel, mx = assert_parity(got, ref, dtype, oracle_mod, f"lowrank {shape}")
-    if launches is not None:
-        assert n == launches, f"{n} launches, expected {launches}"
+    if gate is not None:
+        plain = _plain_launches(x, shape, direction, chunk,
+                                g.PATH_MFMA if gate == "fused" else path)
+        want = plain if gate == "fused" else plain + 1
+        assert n == want, f"{n} launches, expected {want} (gate {gate})"
     return rel, mx
 
 
@@ -71,12 +100,12 @@ FUSED_SHAPES = [
 
 @pytest.mark.parametrize("shape", FUSED_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_fused_gate_shapes(oracle_mod, shape):
-    _case(oracle_mod, shape, launches=3)
+    _case(oracle_mod, shape, gate="fused")
 
 
 @pytest.mark.parametrize("direction", [0, 1, 2, 3])
 def test_fused_gate_directions(oracle_mod, direction):
-    _case(oracle_mod, (2, 19, 23, 2, 64, 64, "f16"), direction=direction, launches=3)
+    _case(oracle_mod, (2, 19, 23, 2, 64, 64, "f16"), direction=direction, gate="fused")
 
 
 @pytest.mark.parametrize("sc", [1, 3, 7])
@@ -86,8 +115,8 @@ def test_fused_gate_ranges_across_heads(oracle_mod, sc):
     lib = _lib.load()
     lib.gtr_set_segment_chunks(sc)
     try:
-        _case(oracle_mod, (2, 16, 12, 3, 64, 64, "bf16"), direction=1, launches=3)
-        _case(oracle_mod, (1, 10, 10, 5, 64, 64, "f16"), direction=2, launches=3)
+        _case(oracle_mod, (2, 16, 12, 3, 64, 64, "bf16"), direction=1, gate="fused")
+        _case(oracle_mod, (1, 10, 10, 5, 64, 64, "f16"), direction=2, gate="fused")
     finally:
         lib.gtr_set_segment_chunks(0)
 
@@ -99,25 +128,25 @@ def test_fused_gate_saturated_and_fast_decaying_channels(oracle_mod):
     shift = np.zeros(H * dk)
     shift[::7] = 12.0
     shift[3::11] = -14.0
-    _case(oracle_mod, (1, 20, 16, H, 64, 64, "f16"), direction=0, launches=3, bias_shift=shift)
-    _case(oracle_mod, (1, 20, 16, H, 64, 64, "bf16"), direction=3, launches=3, bias_shift=shift)
+    _case(oracle_mod, (1, 20, 16, H, 64, 64, "f16"), direction=0, gate="fused", bias_shift=shift)
+    _case(oracle_mod, (1, 20, 16, H, 64, 64, "bf16"), direction=3, gate="fused", bias_shift=shift)
 
 
 @pytest.mark.parametrize("case", [
-    # shape, chunk, path, rank, launches
-    ((1, 17, 15, 2, 64, 64, "f16"), 0, g.PATH_AUTO, 8, 4),      # another rank
-    ((1, 17, 15, 2, 64, 64, "bf16"), 0, g.PATH_AUTO, 1, 4),
-    ((1, 11, 13, 2, 64, 64, "f16"), 0, g.PATH_AUTO, 48, 4),
-    ((2, 12, 12, 2, 64, 128, "bf16"), 0, g.PATH_AUTO, 16, 4),   # dv = 128
-    ((1, 9, 10, 3, 64, 64, "f16"), 32, g.PATH_AUTO, 16, 4),     # chunk 32
-    ((1, 9, 7, 2, 32, 32, "f32"), 16, g.PATH_AUTO, 16, 4),      # float32 I/O
-    ((1, 6, 11, 2, 128, 64, "f32"), 64, g.PATH_AUTO, 5, 4),
-    ((1, 17, 15, 2, 64, 64, "f16"), 0, g.PATH_SERIAL, 16, 4),
-    ((1, 17, 15, 2, 64, 64, "bf16"), 0, g.PATH_FAST, 16, 2),
+    # shape, chunk, path, rank
+    ((1, 17, 15, 2, 64, 64, "f16"), 0, g.PATH_AUTO, 8),      # another rank
+    ((1, 17, 15, 2, 64, 64, "bf16"), 0, g.PATH_AUTO, 1),
+    ((1, 11, 13, 2, 64, 64, "f16"), 0, g.PATH_AUTO, 48),
+    ((2, 12, 12, 2, 64, 128, "bf16"), 0, g.PATH_AUTO, 16),   # dv = 128
+    ((1, 9, 10, 3, 64, 64, "f16"), 32, g.PATH_AUTO, 16),     # chunk 32
+    ((1, 9, 7, 2, 32, 32, "f32"), 16, g.PATH_AUTO, 16),      # float32 I/O
+    ((1, 6, 11, 2, 128, 64, "f32"), 64, g.PATH_AUTO, 5),
+    ((1, 17, 15, 2, 64, 64, "f16"), 0, g.PATH_SERIAL, 16),
+    ((1, 17, 15, 2, 64, 64, "bf16"), 0, g.PATH_FAST, 16),
 ], ids=lambda c: f"{'x'.join(map(str, c[0]))}-c{c[1]}-p{c[2]}-r{c[3]}")
 def test_written_out_gate_paths(oracle_mod, case):
-    shape, chunk, path, rank, launches = case
-    _case(oracle_mod, shape, chunk=chunk, path=path, rank=rank, launches=launches)
+    shape, chunk, path, rank = case
+    _case(oracle_mod, shape, chunk=chunk, path=path, rank=rank, gate="written")
 
 
 def test_fused_gate_back_to_back_is_bitwise_stable(oracle_mod):
