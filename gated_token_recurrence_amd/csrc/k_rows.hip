@@ -457,21 +457,25 @@ struct RowTile {
 
     // ---- products of a chunk (after phase 2 everywhere)
     __device__ __forceinline__ void compute() {
-        // inter-chunk readout O^T = S^T Q~_w^T
+        // inter-chunk readout O^T = S^T Q~_w^T, the value tiles' products interleaved
         const uint16_t *sh = sS, *sl = sS + DV * 64;
 #pragma unroll
-        for (int e = 0; e < NDW; ++e) {
-            O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int d = dcol(NDW * hv + e, lr);
+        for (int e = 0; e < NDW; ++e) O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kap = 0; kap < 2; ++kap) {
-                const int off = sws(d, 32 * kap + 8 * g);
-                const s16x8 ah = *reinterpret_cast<const s16x8 *>(sh + off);
-                const s16x8 al = *reinterpret_cast<const s16x8 *>(sl + off);
-                O[e] = mma<false>(ah, qh[kap], O[e]);
-                O[e] = mma<false>(ah, ql[kap], O[e]);
-                O[e] = mma<false>(al, qh[kap], O[e]);
+        for (int kap = 0; kap < 2; ++kap) {
+            s16x8 ah[NDW], al[NDW];
+#pragma unroll
+            for (int e = 0; e < NDW; ++e) {
+                const int off = sws(dcol(NDW * hv + e, lr), 32 * kap + 8 * g);
+                ah[e] = *reinterpret_cast<const s16x8 *>(sh + off);
+                al[e] = *reinterpret_cast<const s16x8 *>(sl + off);
             }
+#pragma unroll
+            for (int e = 0; e < NDW; ++e) O[e] = mma<false>(ah[e], qh[kap], O[e]);
+#pragma unroll
+            for (int e = 0; e < NDW; ++e) O[e] = mma<false>(ah[e], ql[kap], O[e]);
+#pragma unroll
+            for (int e = 0; e < NDW; ++e) O[e] = mma<false>(al[e], qh[kap], O[e]);
         }
         __builtin_amdgcn_sched_barrier(0);  // keeps the operand loads of each step near it
         // causal score tiles P^T_J[j][i] = K^_J Q~_w^T (hi + lo), two at a time, each
