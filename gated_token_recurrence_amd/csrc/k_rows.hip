@@ -12,12 +12,13 @@
 // fp32 instead (S_t = Diag(g_t) S + k_t v_t^T, o_t = S_t^T q_t).
 //
 // Work split inside a workgroup of four waves: wave w owns the chunk's tokens
-// [16 w, 16 w + 16) -- it loads them, forms their operands, computes all of their
-// output columns and runs their epilogue -- and the state columns of value
-// tiles NS w .. NS w + NS - 1.  So:
+// [16 u, 16 u + 16) of its token group u (a rotation of the wave index, see
+// init) -- it loads them, forms their operands, computes all of their output
+// columns and runs their epilogue -- and the state columns of value tiles
+// NS w .. NS w + NS - 1.  So:
 //   * Q~ = q 2^a of a wave's own tokens is already in the MFMA operand layout
 //     where it is formed and never goes through LDS;
-//   * a wave's score tiles P^T_J = K^_J Q~_w^T (J <= w) stay in registers and
+//   * a wave's score tiles P^T_J = K^_J Q~_u^T (J <= u) stay in registers and
 //     feed the intra-chunk product directly (their register order is the k-slot
 //     order of the V^T operand);
 //   * every output column of a token is in one wave, so RMSNorm needs only
@@ -26,8 +27,12 @@
 // update, V for the intra product and the state update, and the state S^T
 // (hi, lo) that every wave reads for Q~ S.  Three barriers per chunk.
 //
-// dv = 128 runs eight waves in two value halves: waves w and w + 4 own the same
-// 16 tokens, wave w takes the value columns [64 (w / 4), 64 (w / 4) + 64) of
+// Incoming state of a range: the scanned state of its segment, or, for
+// sequences of few segments, the boundary recurrence folded in the prologue
+// from the segment summaries (the scan launch is then left out).
+//
+// dv = 128 runs eight waves in two value halves: two waves, one per half, own
+// the same 16 tokens, wave w takes the value columns [64 (w / 4), 64 (w / 4) + 64) of
 // them and state tile w, so each wave holds what a dv = 64 wave holds (the
 // four-wave form would need about 450 registers per lane, one wave per SIMD).
 // The pair splits the key channels: wave w reads q, k and log_g of channels

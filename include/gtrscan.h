@@ -89,7 +89,9 @@ typedef enum { GTR_LR = 0, GTR_RL = 1, GTR_TB = 2, GTR_BT = 3 } gtr_direction;
  * views).  gtr_gla_auto_path reports the choice. */
 typedef enum {
     GTR_PATH_AUTO = 0,
-    GTR_PATH_MFMA = 1,    /* three launches: segment summaries, state scan, chunk outputs */
+    GTR_PATH_MFMA = 1,    /* segment summaries, state scan, chunk outputs (the scan left out
+                             at chunk 64 when every sequence has at most 8 segments: the
+                             output kernel then folds the incoming states itself) */
     GTR_PATH_FAST = 2,    /* one launch; B == 1, L <= 2048, 16-bit I/O, MFMA shapes */
     GTR_PATH_SERIAL = 3   /* fp32 arithmetic, token-serial inside each chunk */
 } gtr_path;
@@ -118,9 +120,10 @@ gtr_status gtr_gla_fwd_path(const void *q, const void *k, const void *v, const f
 /* gtr_gla_fwd_path that also records `events` (hipEvent_t handles created by
  * the caller) on `stream`: events[0] before the first kernel launch and
  * events[i] after launch i, for as many as n_events allows.  The launches of a
- * call are, in order: MFMA path -- segment summaries, state scan, chunk
- * outputs; serial path -- chunk summaries, state scan, chunk outputs; fast
- * path -- one kernel.  For timing single kernels.  *n_launches (nullable)
+ * call are, in order: MFMA path -- segment summaries, state scan (absent where
+ * the output kernel folds the states, see GTR_PATH_MFMA), chunk outputs;
+ * serial path -- chunk summaries, state scan, chunk outputs; fast path -- one
+ * kernel.  For timing single kernels.  *n_launches (nullable)
  * receives the number of launches of the call. */
 gtr_status gtr_gla_fwd_events(const void *q, const void *k, const void *v, const float *log_g,
                               const void *z, const float *rms_w, void *out,
