@@ -111,6 +111,65 @@ def test_mfma_workgroup_ranges(oracle_mod, segment_chunks, sc):
         assert_parity(got, ref, "f16", oracle_mod, f"segments of {sc}")
 
 
+def _launches(t, shape, direction, chunk=64, path=g.PATH_MFMA):
+    """Launch count of one gtr_gla_fwd_events call on these device tensors."""
+    import ctypes
+    B, gh, gw, H, dk, dv, dtype = shape
+    out = torch.empty_like(t["v"])
+    n = ctypes.c_int(0)
+    lib = _lib.load()
+    _lib.check(lib.gtr_gla_fwd_events(
+        t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["log_g"].data_ptr(),
+        t["z"].data_ptr(), t["rms_w"].data_ptr(), out.data_ptr(), B, H, gh, gw, dk, dv,
+        direction, chunk, W.DTYPE_CODE[dtype], path, None, 0, ctypes.byref(n),
+        torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    return n.value
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("sc,launches", [(1, 2), (2, 2), (3, 2), (0, 2)])
+def test_output_kernel_fold_equals_scan(oracle_mod, segment_chunks, dtype, sc, launches):
+    """Sequences of at most 8 segments (7 chunks each here: segments of 1, 2 or 3 chunks
+    forced, and the automatic plan, one chunk per segment at this size):
+    the output kernel folds each range's incoming state from the segment summaries
+    itself, with the scan's arithmetic in the scan's order, and the scan launch is left
+    out; gla_fwd_states always scans.  The two outputs are equal bit for bit (ranges
+    that cross into the next sequence start it from zero), and both meet the oracle."""
+    shape = (2, 16, 28, 3, 64, 64, dtype)  # 448 tokens: 7 chunks per sequence
+    x = W.make_custom(*shape, seed=31 + sc)
+    segment_chunks(sc)
+    t = inputs_to_dev(x, dtype)
+    args = (t["q"], t["k"], t["v"], t["log_g"], t["z"], t["rms_w"])
+    for direction in (0, 3):
+        _note(f"fold vs scan {shape} sc {sc} direction {direction}")
+        assert _launches(t, shape, direction) == launches
+        folded = g.gla_fwd(*args, direction, chunk=64, path=g.PATH_MFMA)
+        scanned, _ = g.gla_fwd_states(*args, direction, chunk=64)
+        torch.cuda.synchronize()
+        assert torch.equal(folded, scanned), f"fold and scan differ (sc {sc}, direction {direction})"
+        ref = _oracle(oracle_mod, x, dtype, direction)
+        assert_parity(to_f64(folded), ref, dtype, oracle_mod, f"fold sc {sc}")
+
+
+def test_output_kernel_fold_limit(oracle_mod, segment_chunks):
+    """One chunk per segment: 7 chunks per sequence fold (2 launches), 8 and more
+    scan (3 launches: the bound counts a range's possible extra piece); both
+    meet the oracle, and at dv = 128 too."""
+    for shape, launches in (((1, 8, 56, 2, 64, 64, "f16"), 2),     # 7 chunks
+                            ((1, 8, 64, 2, 64, 64, "f16"), 3),     # 8 chunks
+                            ((1, 8, 72, 2, 64, 64, "bf16"), 3),    # 9 chunks
+                            ((2, 8, 56, 2, 64, 128, "bf16"), 2)):  # dv = 128
+        x = W.make_custom(*shape, seed=41)
+        segment_chunks(1)
+        t = inputs_to_dev(x, shape[-1])
+        _note(f"fold limit {shape}")
+        assert _launches(t, shape, 1) == launches
+        got = _run(x, shape[-1], 1, chunk=64, path=g.PATH_MFMA)
+        ref = _oracle(oracle_mod, x, shape[-1], 1)
+        assert_parity(got, ref, shape[-1], oracle_mod, f"fold limit {shape}")
+
+
 @pytest.mark.parametrize("chunk,sc", [(64, 1), (32, 1), (64, 3), (32, 5)])
 def test_mfma_long_segment_chains(oracle_mod, segment_chunks, chunk, sc):
     """One long sequence cut into many segments: 257 and 513 segments (the
