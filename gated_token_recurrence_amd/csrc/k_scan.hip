@@ -160,6 +160,73 @@ __global__ __launch_bounds__(64 * P) void k_scan_rows(float *__restrict__ U,
     }
 }
 
+// k_scan_rows with four consecutive elements per lane (one 16-byte load per
+// segment instead of four 4-byte ones): workgroup = (sequence, 256-element
+// slice), four times fewer workgroups.  The four elements of a lane share one key
+// channel (dv >= 64), and each element's fold is k_scan_rows' (the same results).
+template <int M, int P>
+__global__ __launch_bounds__(64 * P) void k_scan_rows4(float *__restrict__ U,
+                                                       const float *__restrict__ G, MfmaPlan pl,
+                                                       int dk, int dv) {
+    __shared__ float sA[P][64];
+    __shared__ float4 sB[P][64];
+    const int64_t dd = static_cast<int64_t>(dk) * dv;
+    const uint32_t slices = static_cast<uint32_t>(dk * dv / 256);
+    const uint32_t seq32 = blockIdx.x / slices;
+    const int64_t seq = seq32;
+    const int lane = threadIdx.x & 63;
+    const int part = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const uint32_t el0 = (blockIdx.x - seq32 * slices) * 256;
+    const int64_t el = el0 + 4 * lane;
+    const int c = static_cast<int>(static_cast<uint32_t>(el) / static_cast<uint32_t>(dv));
+    const int64_t s0 = seg_id(seq * pl.N, pl), s1 = seg_id((seq + 1) * pl.N, pl);
+    const int64_t len = (s1 - s0 + P - 1) / P;  // <= M (checked by the host)
+    const int64_t kb = s0 + part * len;
+    const int n = static_cast<int>(kb < s1 ? (kb + len < s1 ? len : s1 - kb) : 0);
+    float4 x[M];
+    float e[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int64_t k = (i < n) ? kb + i : s1 - 1;  // in bounds; unused past n
+        const float4 xv = *reinterpret_cast<const float4 *>(U + k * dd + el);
+        const float gv = G[k * dk + c];
+        x[i] = (i < n) ? xv : make_float4(0.f, 0.f, 0.f, 0.f);
+        e[i] = (i < n) ? __builtin_amdgcn_exp2f(gv) : 1.f;
+    }
+    float A = 1.f;
+    float4 B = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        B.x = e[i] * B.x + x[i].x;
+        B.y = e[i] * B.y + x[i].y;
+        B.z = e[i] * B.z + x[i].z;
+        B.w = e[i] * B.w + x[i].w;
+        A *= e[i];
+    }
+    sA[part][lane] = A;
+    sB[part][lane] = B;
+    __syncthreads();
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);  // state before this part's first segment
+    for (int q = 0; q < part; ++q) {
+        const float a = sA[q][lane];
+        const float4 b = sB[q][lane];
+        s.x = a * s.x + b.x;
+        s.y = a * s.y + b.y;
+        s.z = a * s.z + b.z;
+        s.w = a * s.w + b.w;
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        if (i < n) {
+            *reinterpret_cast<float4 *>(U + (kb + i) * dd + el) = s;
+            s.x = e[i] * s.x + x[i].x;
+            s.y = e[i] * s.y + x[i].y;
+            s.z = e[i] * s.z + x[i].z;
+            s.w = e[i] * s.w + x[i].w;
+        }
+    }
+}
+
 // Few segments per sequence (at most M): one wave per (sequence, 64-element
 // slice), W of them per workgroup, each lane loading its element of every
 // segment at once and folding them in order.  With several slices per workgroup
@@ -261,8 +328,12 @@ hipError_t state_scan_plan(float *U, const float *G, const MfmaPlan &pl, int n_s
     if (most <= 8 && n_slices % 16 == 0 && n_slices / 16 <= 0x7fffffff) {
         hipLaunchKernelGGL((k_scan_slices<8, 16>), dim3(static_cast<unsigned>(n_slices / 16)),
                            dim3(64 * 16), 0, s, U, G, pl, dk, dv);
+    } else if (most <= 4 * 16 && (dk * dv) % 256 == 0) {
+        // four parts (more parts measured no faster at 16.4K tokens: 44 segments per
+        // sequence), four elements per lane (10.3 -> 8.4 us there)
+        hipLaunchKernelGGL((k_scan_rows4<16, 4>), dim3(static_cast<unsigned>(n_el / 256)), dim3(NT),
+                           0, s, U, G, pl, dk, dv);
     } else if (most <= 4 * 16) {
-        // four parts (more parts measured no faster at 16.4K tokens: 44 segments per sequence)
         hipLaunchKernelGGL((k_scan_rows<16, 4>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);
     } else if (most <= 4 * 32) {
         hipLaunchKernelGGL((k_scan_rows<32, 4>), rows_grid, dim3(NT), 0, s, U, G, pl, dk, dv);
