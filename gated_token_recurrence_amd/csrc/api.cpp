@@ -310,12 +310,12 @@ bool fast_ok(const GlaArgs &a) {
 }
 
 // AUTO takes the single-launch path for batch-one calls of at most kFastAutoChunks
-// chunks per sequence (measured on MI355X with warmed-up calls: it wins there, by
-// 5-7 us at one chunk and by about 1 us at 13, and loses from 14 chunks on, where
-// each chunk's fold of every earlier chunk's summary dominates), the matrix-core
-// path for the other 16-bit calls at its shapes with 16-byte aligned rows, and the
-// token-serial path otherwise.
-constexpr int64_t kFastAutoChunks = 13;
+// chunks per sequence (measured on MI355X with warmed-up calls, 6 and 16 heads: it
+// wins there, by 5-7 us at one chunk and by 1-3 us at 13 to 16, ties at 20 with 6
+// heads and loses from about 17 chunks with 16, where each chunk's fold of every
+// earlier chunk's summary dominates), the matrix-core path for the other 16-bit
+// calls at its shapes with 16-byte aligned rows, and the token-serial path otherwise.
+constexpr int64_t kFastAutoChunks = 16;
 
 int auto_path(const GlaArgs &a) {
     const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;

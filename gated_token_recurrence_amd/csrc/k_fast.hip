@@ -9,10 +9,15 @@
 //      (operands stay in LDS), computes the chunk summary
 //      U_n = sum_t (k_t 2^(G - a_t)) v_t^T from a zero state, writes U_n and the
 //      chunk's decay 2^(G_n) per key channel, and raises the chunk's ready flag;
-//   2. it waits for the ready flags of the chunks before it in its sequence and
+//   2. it forms the chunk's intra-chunk products (scores and P V), which need no
+//      incoming state, while the chunks before it finish their summaries;
+//   3. it waits for the ready flags of the chunks before it in its sequence and
 //      builds its incoming state S_n = sum_{m < n} Diag(2^(G_{m+1} + ... +
-//      G_{n-1})) U_m directly in the registers that hold the state;
-//   3. it produces its outputs from that state and the operands still in LDS.
+//      G_{n-1})) U_m directly in the registers that hold the state, in order,
+//      S <- Diag(2^G_m) S + U_m; the decays come from an LDS table that the whole
+//      workgroup fills first, so the registers in flight hold only summaries
+//      (eight predecessors' at dv = 64);
+//   4. it adds the readout of that state, Q~ S, and finishes the outputs.
 // Chunks are handed out in ticket order, so a workgroup only waits for
 // workgroups that took their tickets earlier and are running; those wait only
 // for earlier ones in turn, so every wait ends whatever the grid size and
@@ -84,7 +89,16 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
     }
     t.zero_state();
 
-    // ---- 2. wait for the chunks before this one (lane m of wave 0 polls chunk m's
+    // ---- 2. the intra-chunk products, which do not need the incoming state, while
+    // the chunks before this one finish theirs
+    if (!slow) {
+        t.zero_out();
+        t.scores();
+        __syncthreads();  // score tiles
+        t.intra();
+    }
+
+    // ---- 3. wait for the chunks before this one (lane m of wave 0 polls chunk m's
     // flag with cache-bypassing loads); the summaries are then read the same way
     if (ch > 0) {
         if (t.w == 0) {
@@ -100,31 +114,55 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
             }
             if (t.l == 0) s_gave_up = spins >= kSpinLimit;
         }
-        __syncthreads();
+        __syncthreads();  // (also: every wave is past its intra-chunk products)
 
         // S <- Diag(2^G_m) S + U_m over the chunks m before this one, in order
         const float *ub = U + static_cast<int64_t>(bh) * N * dd, *eb = Gs + static_cast<int64_t>(bh) * N * DK;
-        constexpr int MB = DV == 64 ? 4 : 2;  // chunks whose loads are in flight together
-        for (int m0 = 0; m0 < ch; m0 += MB) {
-            typename T::StateIn in[MB];
+        if (!slow && ch * DK * 4 <= T::K::KN) {
+            // the predecessors' decays into an LDS table first (the K^ area: scores
+            // and the state update are done with it), every thread loading a few
+            float *etab = reinterpret_cast<float *>(smem + T::K::O_KN);
+            constexpr int PER = 64 * DK / NT;  // table entries per thread, 64 predecessors at most
 #pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                const int m = (m0 + i < ch) ? m0 + i : ch - 1;  // clamped, then skipped
-                t.state_in_load(in[i], ub + m * dd, eb + static_cast<int64_t>(m) * DK);
+            for (int i = 0; i < PER; ++i) {
+                const int x = t.tid + NT * i;  // entry: predecessor x / DK, channel x % DK
+                if (x < ch * DK)
+                    etab[x] = __hip_atomic_load(eb + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            __syncthreads();
+            constexpr int MB = DV == 64 ? 8 : 4;  // summaries in flight together
+            for (int m0 = 0; m0 < ch; m0 += MB) {
+                typename T::UIn in[MB];
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
-                if (m0 + i < ch) t.state_in_apply(in[i]);
+                for (int i = 0; i < MB; ++i) {
+                    const int m = (m0 + i < ch) ? m0 + i : ch - 1;  // clamped, then skipped
+                    t.state_u_load(in[i], ub + m * dd);
+                }
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    if (m0 + i < ch) t.state_u_apply(in[i], etab + (m0 + i) * DK);
+            }
+        } else {
+            constexpr int MB = DV == 64 ? 4 : 2;  // chunks whose loads are in flight together
+            for (int m0 = 0; m0 < ch; m0 += MB) {
+                typename T::StateIn in[MB];
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const int m = (m0 + i < ch) ? m0 + i : ch - 1;  // clamped, then skipped
+                    t.state_in_load(in[i], ub + m * dd, eb + static_cast<int64_t>(m) * DK);
+                }
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    if (m0 + i < ch) t.state_in_apply(in[i]);
+            }
         }
         if (s_gave_up) t.poison_state();
     }
 
-    // ---- 3. outputs from the incoming state and the staged operands
+    // ---- 4. outputs: the readout of the incoming state added to the intra-chunk
+    // products (token by token instead for a chunk past the matrix path's span)
     if (!slow) {
-        t.inter();
-        t.scores();
-        __syncthreads();  // score tiles
-        t.intra();
+        t.template inter<true>();
     } else {
         __syncthreads();
         t.serial();

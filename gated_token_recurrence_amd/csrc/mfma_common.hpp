@@ -558,6 +558,41 @@ struct Tile {
                     S[dd][ct][r] = fmaf(S[dd][ct][r], x.e[ct][r], x.u[dd][ct][r]);
     }
 
+    // The same step with the decay read from an LDS table ([predecessor][DK] fp32,
+    // filled once per workgroup), so that only the summaries are loaded per
+    // predecessor and twice as many of them can be in flight.
+    struct UIn {
+        float u[DPW][4][4];
+    };
+    __device__ __forceinline__ void state_u_load(UIn &x, const float *u) const {
+#pragma unroll
+        for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x.u[dd][ct][r] = __hip_atomic_load(
+                        u + (16 * ct + 4 * g + r) * DV + 16 * (w * DPW + dd) + lr, __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ __forceinline__ void state_u_apply(const UIn &x, const float *etab) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const f32x4 e = *reinterpret_cast<const f32x4 *>(etab + 16 * ct + 4 * g);
+#pragma unroll
+            for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[dd][ct][r] = fmaf(S[dd][ct][r], e[r], x.u[dd][ct][r]);
+        }
+    }
+
+    __device__ __forceinline__ void zero_out() {
+#pragma unroll
+        for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) O[dd][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     // ---- phase 1: cumulative gates within the sub-block (registers, natural-log
     // units), block totals, V into LDS.  Consumes the prefetched inputs except q, k.
     __device__ __forceinline__ void phase1() {
@@ -685,7 +720,9 @@ struct Tile {
         return slow;
     }
 
-    // ---- inter-chunk readout O^T[d][i] = S^T (Q~)^T (the state before the chunk)
+    // ---- inter-chunk readout O^T[d][i] = S^T (Q~)^T (the state before the chunk);
+    // ACC: added to what O holds (the intra-chunk products formed first)
+    template <bool ACC = false>
     __device__ __forceinline__ void inter() {
 #pragma unroll
         for (int dd = 0; dd < DPW; ++dd) {
@@ -700,8 +737,10 @@ struct Tile {
                 ah[kap] = __builtin_bit_cast(s16x8, u4(hi));
                 al[kap] = __builtin_bit_cast(s16x8, u4(lo));
             }
+            if (!ACC) {
 #pragma unroll
-            for (int tb = 0; tb < NB; ++tb) O[dd][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int tb = 0; tb < NB; ++tb) O[dd][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int kap = 0; kap < 2; ++kap) {
 #pragma unroll

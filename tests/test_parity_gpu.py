@@ -299,9 +299,10 @@ def test_fast_path_shapes(oracle_mod, shape):
 
 
 @pytest.mark.parametrize("shape", [(8, 8, 6, "f16"), (16, 16, 16, "bf16"), (28, 28, 6, "f16"),
-                                   (13, 17, 4, "bf16")], ids=lambda s: "x".join(map(str, s)))
+                                   (13, 17, 4, "bf16"), (32, 32, 16, "f16")],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_auto_takes_the_single_launch_for_short_calls(oracle_mod, shape):
-    """Batch-one calls of at most 13 chunks per sequence go to the single-launch path
+    """Batch-one calls of at most 16 chunks per sequence go to the single-launch path
     under AUTO (checked through gtr_gla_auto_path), and meet the bar in every direction."""
     gh, gw, H, dtype = shape
     assert _lib.load().gtr_gla_auto_path(1, H, gh, gw, 64, 64, 64, W.DTYPE_CODE[dtype]) == g.PATH_FAST
