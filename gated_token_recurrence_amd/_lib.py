@@ -19,7 +19,7 @@ PATH_AUTO, PATH_MFMA, PATH_FAST, PATH_SERIAL = 0, 1, 2, 3
 EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_noalloc", "gtr_gla_fwd_path", "gtr_gla_fwd_events", "gtr_gla_stack_fwd",
            "gtr_gla_lowrank_fwd", "gtr_gla_bwd", "gtr_gla_states_bytes", "gtr_gla_fwd_states",
            "gtr_gla_bwd_states", "gtr_sswiglu_mix", "gtr_gla_auto_path", "gtr_last_error",
-           "gtr_version", "gtr_release_workspace", "gtr_set_segment_chunks")
+           "gtr_version", "gtr_release_workspace", "gtr_set_segment_chunks", "gtr_set_wait_limit")
 
 _lib = None
 
@@ -80,6 +80,8 @@ def load():
     lib.gtr_version.argtypes = []
     lib.gtr_set_segment_chunks.restype = None
     lib.gtr_set_segment_chunks.argtypes = [i]
+    lib.gtr_set_wait_limit.restype = None
+    lib.gtr_set_wait_limit.argtypes = [ctypes.c_uint]
     lib.gtr_release_workspace.restype = None
     lib.gtr_release_workspace.argtypes = []
     _lib = lib

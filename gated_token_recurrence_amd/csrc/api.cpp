@@ -216,6 +216,7 @@ constexpr int kFastMaxTokens = 2048;
 constexpr int64_t kFoldSegments = 8;
 
 int g_chunks_per_wg = 0;  // 0: automatic (gtr_set_segment_chunks)
+unsigned g_fast_spin_limit = kFastSpinLimit;  // gtr_set_wait_limit
 
 gtr_status run_serial(const GlaArgs &a, hipStream_t st, Marks &mk, const WsSource *src = nullptr) {
     const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
@@ -349,7 +350,7 @@ gtr_status run_fast(const GlaArgs &a, hipStream_t st, Marks &mk) {
     float *U = static_cast<float *>(ws);
     float *G = U + T * a.dk * a.dv;
     hipError_t e = mk.start(st);
-    if (e == hipSuccess) e = fast_launch(a, U, G, static_cast<unsigned *>(ctr), st);
+    if (e == hipSuccess) e = fast_launch(a, U, G, static_cast<unsigned *>(ctr), g_fast_spin_limit, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "single-launch kernel");
     return GTR_OK;
@@ -850,6 +851,8 @@ const char *gtr_last_error(void) { return g_err.c_str(); }
 int gtr_version(void) { return GTR_VERSION; }
 
 void gtr_set_segment_chunks(int chunks) { g_chunks_per_wg = chunks > 0 ? chunks : 0; }
+
+void gtr_set_wait_limit(unsigned polls) { g_fast_spin_limit = polls > 0 ? polls : kFastSpinLimit; }
 
 void gtr_release_workspace(void) {
     std::lock_guard<std::mutex> lock(g_ws_mu);

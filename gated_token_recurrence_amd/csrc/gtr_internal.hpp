@@ -174,7 +174,11 @@ int64_t fast_counters(const GlaArgs &a);  // 32-bit counters the launch needs
 bool fast_supported(const GlaArgs &a);    // shape has a kernel and <= 64 chunks per sequence
 // U: [chunks][dk][dv] fp32; G: [chunks][dk]; cnt: fast_counters() words, zero before
 // the first launch (each launch leaves them zero).
-hipError_t fast_launch(const GlaArgs &a, float *U, float *G, unsigned *cnt, hipStream_t s);
+// spin_limit: polls of a wait for earlier chunks before it gives up (the chunk's
+// incoming state is then NaN).
+constexpr unsigned kFastSpinLimit = 1u << 24;  // far beyond any real wait
+hipError_t fast_launch(const GlaArgs &a, float *U, float *G, unsigned *cnt, unsigned spin_limit,
+                       hipStream_t s);
 // Low-rank gate written out: log_g [B L][H dk] (float32) from a.feat, a.gate_w,
 // a.gate_b, a.inv_tau, a.rank (k_gate.hip).
 hipError_t gate_materialize(const GlaArgs &a, float *log_g, hipStream_t s);

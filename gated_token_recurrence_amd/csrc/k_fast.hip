@@ -34,15 +34,13 @@ namespace {
 
 using namespace mf;
 
-constexpr unsigned kSpinLimit = 1u << 24;  // bounded wait (far beyond any real wait)
-
 // Counter block: [0] ticket, [1] finished workgroups, then per sequence one
 // finished-workgroup count, then one ready flag per chunk.
 template <int DT, int DV, int NB>
 __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float *__restrict__ U,
                                                                  float *__restrict__ Gs,
                                                                  unsigned *__restrict__ cnt,
-                                                                 int N) {
+                                                                 int N, unsigned spin_limit) {
     using T = Tile<DT, DV, NB, false>;
     __shared__ __attribute__((aligned(16))) char smem[T::K::BYTES];
     T t;
@@ -109,10 +107,10 @@ __global__ __launch_bounds__(NT, DV == 128 ? 1 : 2) void k_fast(GlaArgs a, float
                 if (!mine)
                     mine = __hip_atomic_load(fl + t.l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
                 if (__builtin_amdgcn_read_exec() == __ballot(mine)) break;
-                if (++spins >= kSpinLimit) break;
+                if (++spins >= spin_limit) break;
                 __builtin_amdgcn_s_sleep(2);
             }
-            if (t.l == 0) s_gave_up = spins >= kSpinLimit;
+            if (t.l == 0) s_gave_up = spins >= spin_limit;
         }
         __syncthreads();  // (also: every wave is past its intra-chunk products)
 
@@ -218,14 +216,15 @@ bool fast_supported(const GlaArgs &a) {
     return mfma_supported(a) && pick(a) != nullptr && (a.L + a.chunk - 1) / a.chunk <= 64;
 }
 
-hipError_t fast_launch(const GlaArgs &a, float *U, float *G, unsigned *cnt, hipStream_t s) {
+hipError_t fast_launch(const GlaArgs &a, float *U, float *G, unsigned *cnt, unsigned spin_limit,
+                       hipStream_t s) {
     const void *k = pick(a);
     const int64_t N = (a.L + a.chunk - 1) / a.chunk;
     if (!k || N > 64) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(reinterpret_cast<void (*)(GlaArgs, float *, float *, unsigned *, int)>(
+    hipLaunchKernelGGL(reinterpret_cast<void (*)(GlaArgs, float *, float *, unsigned *, int, unsigned)>(
                            const_cast<void *>(k)),
                        dim3(static_cast<unsigned>(fast_chunks(a))), dim3(NT), 0, s, a, U, G, cnt,
-                       static_cast<int>(N));
+                       static_cast<int>(N), spin_limit);
     return hipGetLastError();
 }
 

@@ -317,6 +317,15 @@ int gtr_version(void);
  * rounding. */
 void gtr_set_segment_chunks(int chunks);
 
+/* Test hook: how many times a single-launch (GTR_PATH_FAST) workgroup polls the
+ * ready flags of its sequence's earlier chunks before its bounded wait gives up;
+ * 0 restores the default (2^24 polls, far beyond any real wait).  A wait that
+ * gives up makes that chunk's incoming state NaN, so every output of the chunk
+ * is NaN instead of silently wrong; the launch still finishes and leaves its
+ * counters ready for the next call.  A small limit lets a test force give-ups
+ * from the host.  Process-wide; read when a call is enqueued. */
+void gtr_set_wait_limit(unsigned polls);
+
 /* Frees every cached workspace after synchronising the device that owns it. */
 void gtr_release_workspace(void);
 

@@ -357,6 +357,43 @@ def test_fast_path_back_to_back(oracle_mod):
         assert_parity(to_f64(out), ref, dtype, oracle_mod, "fast back-to-back")
 
 
+def test_fast_path_wait_give_up_poisons(oracle_mod):
+    """With the bounded wait cut to one poll (gtr_set_wait_limit, forced from the host),
+    a single-launch chunk whose earlier chunks have not all published gives up: every
+    output of that chunk is NaN, never a wrong value.  So each token row is either all
+    NaN or within the per-row bound of the oracle, and no row of a sequence's first
+    chunk (which never waits) is NaN.  The next calls with the default limit are correct
+    everywhere: a give-up leaves the launch's counters ready for the next launch."""
+    w = W.WORKLOADS["mixer_640"]  # 25 chunks per sequence, 6 heads
+    x = W.make_inputs(w)
+    ref = _oracle(oracle_mod, x, w.dtype, 0)
+    lib = _lib.load()
+    gave_up = 0
+    try:
+        lib.gtr_set_wait_limit(1)
+        for i in range(3):
+            _note(f"single launch, wait limit 1, call {i}")
+            got = _run(x, w.dtype, 0, chunk=64, path=g.PATH_FAST)
+            nan = np.isnan(got)
+            row_nan = nan.any(axis=-1)
+            assert (nan.all(axis=-1) == row_nan).all(), "a row is partly NaN"
+            tok = np.arange(w.L).reshape(w.grid_h, w.grid_w)  # LR: scan step = grid position
+            first = (tok < 64)[None, :, :, None]
+            assert not (row_nan & first).any(), "a first chunk's row is NaN"
+            rows = _row_rel_errors(np.where(nan, 0.0, got), ref, w.dtype, oracle_mod)
+            ok = ~row_nan
+            assert rows[ok].max() <= 1e-2, f"a finite row is off by {rows[ok].max():.2e}"
+            gave_up += int(row_nan.sum())
+        _note(f"  {gave_up} token rows poisoned over three calls")
+    finally:
+        lib.gtr_set_wait_limit(0)
+    for direction in (0, 2):
+        _note(f"single launch after give-ups, direction {direction}")
+        got = _run(x, w.dtype, direction, chunk=64, path=g.PATH_FAST)
+        assert_parity(got, _oracle(oracle_mod, x, w.dtype, direction), w.dtype, oracle_mod,
+                      f"after give-ups dir {direction}")
+
+
 def test_fast_path_rejects_batches(oracle_mod):
     x = W.make_custom(2, 8, 8, 1, 64, 64, "f16", seed=9)
     with pytest.raises(g.GtrError):
