@@ -353,12 +353,16 @@ __global__ __launch_bounds__(64 * 4 * (DV / 64), DV == 64 ? 2 : 1) void k_sum(Gl
         const bool ahead = p - 2 >= p0;
         int64_t tok;
         const int64_t row = ahead ? t.row_of(far.b, far.h, far.ch, tok) : t.row_of(cur.b, cur.h, cur.ch, tok);
+        // the gates and the K~ staging (vector work the next barrier and the products
+        // wait on) at raised wave priority, the products at the normal one
+        __builtin_amdgcn_s_setprio(1);
         t.template gates<S>();
         t.template prefetch_g<S>(row, tok);  // the gates are consumed
         __syncthreads();  // the chunk's sub-block totals
         t.template stage<S>();
         t.template prefetch_kv<S>(row);  // k and v are consumed
         if constexpr (T::CS == 2) __syncthreads();  // the pair's two halves of K~
+        __builtin_amdgcn_s_setprio(0);
         t.accumulate();
         const bool seg_start = p == p0 || cur.ch == 0;
         if (seg_start) {  // the segment's first chunk: its summary is complete
