@@ -311,16 +311,19 @@ bool fast_ok(const GlaArgs &a) {
 }
 
 // AUTO takes the single-launch path for batch-one calls of at most kFastAutoChunks
-// chunks per sequence (measured on MI355X with warmed-up calls, 6 and 16 heads: it
-// wins there, by 5-7 us at one chunk and by 1-3 us at 13 to 16, ties at 20 with 6
-// heads and loses from about 17 chunks with 16, where each chunk's fold of every
-// earlier chunk's summary dominates), the matrix-core path for the other 16-bit
-// calls at its shapes with 16-byte aligned rows, and the token-serial path otherwise.
-constexpr int64_t kFastAutoChunks = 16;
+// chunks per sequence (measured on MI355X with warmed-up calls, 6 and 16 heads: at
+// chunk 64 it wins by 5-7 us at one chunk and by 1-3 us at 13 to 16, ties at 20 with
+// 6 heads and loses from about 17 chunks with 16; at chunk 32 it wins by 1.5-3 us up
+// to 8 chunks, about ties at 12 and loses at 16: each chunk's fold of every earlier
+// chunk's summary dominates), the matrix-core path for the other 16-bit calls at its
+// shapes with 16-byte aligned rows, and the token-serial path otherwise.
+constexpr int64_t kFastAutoChunks = 16;    // chunk 64
+constexpr int64_t kFastAutoChunks32 = 12;  // chunk 32
 
 int auto_path(const GlaArgs &a) {
     const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
-    if (!a.feat && !a.resid && fast_ok(a) && n_chunks <= kFastAutoChunks) return GTR_PATH_FAST;
+    const int64_t most = a.chunk == 32 ? kFastAutoChunks32 : kFastAutoChunks;
+    if (!a.feat && !a.resid && fast_ok(a) && n_chunks <= most) return GTR_PATH_FAST;
     return mfma_ok(a) ? GTR_PATH_MFMA : GTR_PATH_SERIAL;
 }
 

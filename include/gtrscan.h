@@ -83,7 +83,7 @@ typedef enum { GTR_LR = 0, GTR_RL = 1, GTR_TB = 2, GTR_BT = 3 } gtr_direction;
 
 /* Kernel path.  AUTO picks, for 16-bit I/O with dk = 64, dv in {64, 128},
  * chunk in {32, 64} and 16-byte aligned tensors: the single-launch path for
- * B == 1 with at most 16 chunks per sequence and no residual or gate
+ * B == 1 with at most 16 chunks per sequence (12 at chunk 32) and no residual or gate
  * projection, the MFMA chunk path otherwise; and the fp32 token-serial chunk
  * path for everything else (float32 I/O, other dk/dv or chunk, unaligned
  * views).  gtr_gla_auto_path reports the choice. */

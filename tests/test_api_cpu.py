@@ -135,12 +135,14 @@ def test_noalloc_refuses_calls_beyond_the_scratch():
     ((1, 12, 32, 32, 64, 64, 64, _lib.GTR_BF16), _lib.PATH_FAST),
     ((1, 12, 32, 34, 64, 64, 64, _lib.GTR_BF16), _lib.PATH_MFMA),
     ((1, 12, 8, 8, 64, 128, 32, _lib.GTR_F16), _lib.PATH_FAST),
+    ((1, 12, 12, 32, 64, 64, 32, _lib.GTR_F16), _lib.PATH_FAST),
+    ((1, 12, 13, 32, 64, 64, 32, _lib.GTR_F16), _lib.PATH_MFMA),
     ((1, 12, 24, 24, 64, 64, 32, _lib.GTR_BF16), _lib.PATH_MFMA),
     ((1, 12, 40, 40, 64, 64, 64, _lib.GTR_BF16), _lib.PATH_MFMA),
     ((2, 12, 16, 16, 64, 64, 64, _lib.GTR_BF16), _lib.PATH_MFMA),
     ((1, 12, 16, 16, 64, 64, 64, _lib.GTR_F32), _lib.PATH_SERIAL),
     ((1, 12, 16, 16, 32, 32, 64, _lib.GTR_BF16), _lib.PATH_SERIAL),
-], ids=["fast-13-chunks", "fast-16-chunks", "mfma-17-chunks", "fast-64-dv128", "mfma-18-chunks", "mfma-25-chunks", "mfma-batch",
+], ids=["fast-13-chunks", "fast-16-chunks", "mfma-17-chunks", "fast-64-dv128", "fast-12-chunks-of-32", "mfma-13-chunks-of-32", "mfma-18-chunks", "mfma-25-chunks", "mfma-batch",
         "serial-f32", "serial-dk32"])
 def test_auto_path_choice(args, path):
     assert _lib.load().gtr_gla_auto_path(*args) == path, _lib.last_error()
