@@ -259,7 +259,7 @@ gtr_status run_mfma(const GlaArgs &a, hipStream_t st, Marks &mk, float *states_o
     float *U = states_out ? states_out : static_cast<float *>(ws);
     float *G = reinterpret_cast<float *>(static_cast<char *>(ws) + ubytes);
     hipError_t e = mk.start(st);
-    if (e == hipSuccess) e = sum_supported(a) ? sum_launch(a, pl, U, G, st) : mfma_summary(a, pl, U, G, st);
+    if (e == hipSuccess) e = segment_summaries(a, pl, U, G, st);
     if (e == hipSuccess) e = mk.after_launch(st);
     if (e != hipSuccess) return hip_fail(e, "segment summary launch");
     // With few segments per sequence the output kernel folds each segment's incoming

@@ -816,7 +816,7 @@ hipError_t bwd_launch(const GlaArgs &a, const void *dy, void *dq, void *dk, void
             // the forward's segment states, given (gtr_gla_fwd_states): two launches fewer
             Useg = const_cast<float *>(fwd_states);
         } else {
-            e = msum ? sum_launch(a, ps, Useg, Gseg, st) : serial_summary(a, Useg, Gseg, n_chunks, st);
+            e = msum ? segment_summaries(a, ps, Useg, Gseg, st) : serial_summary(a, Useg, Gseg, n_chunks, st);
             if (e != hipSuccess || (e = hooks.after(st)) != hipSuccess) return e;
             e = msum ? state_scan_plan(Useg, Gseg, ps, static_cast<int>(a.B * a.H), a.dk, a.dv, st)
                      : state_scan(Useg, Gseg, static_cast<int>(a.B * a.H), n_chunks, a.dk, a.dv, st);

@@ -420,4 +420,15 @@ hipError_t sum_launch(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, 
     return hipErrorInvalidValue;
 }
 
+// The segment summaries of plan ps.  One-chunk segments (short calls: at most about
+// 512 chunks in all) go to the shared-tile summary kernel of k_mfma.hip, which has no
+// reduction of four per-wave partials at the segment's end (measured on MI355X:
+// 1.6K tokens 20.2 -> 19.0 us with 6 heads, 24.6 -> 24.3 us with 16); longer segments,
+// and calls whose gate is formed from features (the shared-tile kernel reads log_g),
+// to the per-wave-partial kernel above.
+hipError_t segment_summaries(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t s) {
+    if (sum_supported(a) && (ps.Q > 1 || a.feat)) return sum_launch(a, ps, U, G, s);
+    return mfma_summary(a, ps, U, G, s);
+}
+
 }  // namespace gtr
