@@ -460,8 +460,10 @@ struct RowTile {
         return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 
-    // ---- products of a chunk (after phase 2 everywhere)
-    __device__ __forceinline__ void compute() {
+    // ---- products of a chunk (after phase 2 everywhere).  upd: the state after the
+    // chunk is used (the chunk is not the last of its piece of a sequence); otherwise
+    // the state update is left out (a one-chunk range's whole third of the products).
+    __device__ __forceinline__ void compute(bool upd) {
         // inter-chunk readout O^T = S^T Q~_w^T, the value tiles' products interleaved
         const uint16_t *sh = sS, *sl = sS + DV * 64;
 #pragma unroll
@@ -525,6 +527,7 @@ struct RowTile {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (!upd) return;
         // state update of the owned tiles: S = Diag(2^G) (S + K^^T V)
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -749,7 +752,7 @@ __global__ __launch_bounds__(64 * 4 * (DV / 64), DV == 64 ? 2 : 1) void k_rows(G
             __syncthreads();  // B2: K^ (and the pair's halves of Q~)
             if (!slow) {
                 t.partner_q();
-                t.compute();
+                t.compute(p + 1 < pe);
             } else {
                 t.serial();
             }
