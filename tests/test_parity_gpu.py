@@ -578,11 +578,20 @@ def _stack_case(oracle_mod, nb, B, gh, gw, H, dk, dv, dtype, chunk, first, bh=No
         o = g.gla_fwd(t["q"][i], t["k"][i], vt, t["log_g"][i], t["z"][i], t["rms_w"][i],
                       (first + i) % 4, chunk=chunk)
         torch.cuda.synchronize()
-        rel, mx = assert_parity(pick(to_f64(o)), pick(refs[i]), dtype, oracle_mod,
-                                f"oracle-fed block {i}")
+        oi = pick(to_f64(o))
+        rel, mx = assert_parity(oi, pick(refs[i]), dtype, oracle_mod, f"oracle-fed block {i}")
+        worst = ""
+        if bh is None:  # every token-head row, as for the single-call full-size case
+            # one bf16 unit in the last place is 2^-8 of a value: a row whose few largest
+            # outputs round the other way reaches ~5e-3 (measured); a misplaced row is O(1)
+            rows = _row_rel_errors(oi, refs[i], dtype, oracle_mod)
+            worst = f"; worst row {rows.max():.2e}"
+            row_tol = 2e-2 if dtype == "bf16" else 1e-2
+            assert rows.max() <= row_tol, \
+                f"block {i} row {np.unravel_index(rows.argmax(), rows.shape)}: {rows.max():.2e}"
         drel, dmx = errors(pick(got[i]), pick(refs[i]), dtype, oracle_mod)
         _note(f"  block {i} (direction {(first + i) % 4}): oracle-fed rel-L2 {rel:.2e} "
-              f"max-abs {mx:.2e}; free-running rel-L2 {drel:.2e} max-abs {dmx:.2e}")
+              f"max-abs {mx:.2e}{worst}; free-running rel-L2 {drel:.2e} max-abs {dmx:.2e}")
         assert drel <= drift_tol and dmx <= 2e-2, f"free-running drift at block {i}: {drel:.2e}"
 
 
@@ -609,7 +618,8 @@ def test_small_stack_fp16_mfma(oracle_mod):
 @pytest.mark.timeout(900)
 def test_stack_1024_full_size(oracle_mod):
     """The 12-block stack at full size (B=8, 64x64, H=12, dk=64, dv=128, bf16), every
-    (batch, head) sequence of every block against the oracle."""
+    (batch, head) sequence of every block against the oracle, and every token row of the
+    oracle-fed blocks within 2e-2 (bf16) of its reference row."""
     w = W.WORKLOADS["stack_1024"]
     _note("stack_1024: generating 12 blocks of inputs")
     blocks = [W.make_inputs(w, block=i) for i in range(w.n_blocks)]
