@@ -162,7 +162,7 @@ hipError_t mfma_output(const GlaArgs &a, const MfmaPlan &po, const MfmaPlan &ps,
 bool sum_supported(const GlaArgs &a);
 hipError_t sum_launch(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t s);
 // The segment summaries of plan ps on the matrix-core path (mfma_supported): the
-// kernel above, or mfma_summary for one-chunk segments (same outputs).
+// kernel above, or mfma_summary for short segments (same outputs).
 hipError_t segment_summaries(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t s);
 // Chunk outputs with token-row ownership per wave (k_rows.hip): 16-bit I/O,
 // dk = 64, dv in {64, 128}, chunk 64.  Same plans and incoming states as mfma_output;

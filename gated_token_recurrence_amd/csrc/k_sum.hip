@@ -420,14 +420,19 @@ hipError_t sum_launch(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, 
     return hipErrorInvalidValue;
 }
 
-// The segment summaries of plan ps.  One-chunk segments (short calls: at most about
-// 512 chunks in all) go to the shared-tile summary kernel of k_mfma.hip, which has no
-// reduction of four per-wave partials at the segment's end (measured on MI355X:
-// 1.6K tokens 20.2 -> 19.0 us with 6 heads, 24.6 -> 24.3 us with 16); longer segments,
+// The segment summaries of plan ps.  Short segments go to the shared-tile summary
+// kernel of k_mfma.hip, which has no reduction of four per-wave partials at a segment's
+// end: up to 5 chunks at dv = 64, one chunk at dv = 128 (measured on MI355X, fp16:
+// 1.6K tokens 20.2 -> 19.0 us with 6 heads, 24.6 -> 24.3 us with 16; 64x64 grid, 12
+// heads (2 chunks) 32.9 -> 31.4 us; 3 to 5 chunks 0.4-0.7 us faster; 6 chunks, the
+// 16.4K-token workload, alike; dv = 128 with 6 heads 25.4 -> 23.5 us).  Longer segments,
 // and calls whose gate is formed from features (the shared-tile kernel reads log_g),
-// to the per-wave-partial kernel above.
+// go to the per-wave-partial kernel above.
+constexpr int64_t kSharedTileChunks64 = 5, kSharedTileChunks128 = 1;
+
 hipError_t segment_summaries(const GlaArgs &a, const MfmaPlan &ps, float *U, float *G, hipStream_t s) {
-    if (sum_supported(a) && (ps.Q > 1 || a.feat)) return sum_launch(a, ps, U, G, s);
+    const int64_t most = a.dv == 64 ? kSharedTileChunks64 : kSharedTileChunks128;
+    if (sum_supported(a) && (ps.Q > most || a.feat)) return sum_launch(a, ps, U, G, s);
     return mfma_summary(a, ps, U, G, s);
 }
 

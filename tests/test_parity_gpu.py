@@ -314,6 +314,20 @@ def test_auto_takes_the_single_launch_for_short_calls(oracle_mod, shape):
         assert_parity(got, ref, dtype, oracle_mod, f"auto {shape} dir {direction}")
 
 
+def test_auto_single_launch_at_chunk_32(oracle_mod):
+    """At chunk 32, batch-one calls of at most 12 chunks per sequence go to the single
+    launch under AUTO (13 to the three launches), and meet the bar in every direction."""
+    lib = _lib.load()
+    assert lib.gtr_gla_auto_path(1, 6, 12, 32, 64, 64, 32, W.DTYPE_CODE["f16"]) == g.PATH_FAST
+    assert lib.gtr_gla_auto_path(1, 6, 13, 32, 64, 64, 32, W.DTYPE_CODE["f16"]) == g.PATH_MFMA
+    x = W.make_custom(1, 12, 32, 6, 64, 64, "f16", seed=333)
+    for direction in range(4):
+        _note(f"AUTO (single launch) chunk 32, 12 chunks, direction {direction}")
+        got = _run(x, "f16", direction, chunk=32)
+        assert_parity(got, _oracle(oracle_mod, x, "f16", direction), "f16", oracle_mod,
+                      f"chunk 32 auto dir {direction}")
+
+
 @pytest.mark.parametrize("name", ["mixer_640", "mixer_640_wide"])
 def test_fast_path_workloads(oracle_mod, name):
     """The 1.6K-token workloads on the single-launch path, every direction."""
